@@ -1,0 +1,80 @@
+"""Pins for the oracle's LSE combine and decode-step cost model (no GPU)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _parts(rng, n, D, R, cuts):
+    k = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D))
+    q = rng.standard_normal((R, D))
+    bounds = [0] + list(cuts) + [n]
+    os_, ls_ = [], []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        o, l = O.softmax_attention(q, k[a:b], v[a:b], 0.3)
+        os_.append(o)
+        ls_.append(l)
+    return np.stack(os_), np.stack(ls_), O.softmax_attention(q, k, v, 0.3)
+
+
+@pytest.mark.parametrize("cuts", [[], [1], [5, 6, 40], [10, 20, 30, 40, 50]])
+def test_combine_of_disjoint_parts_equals_whole(cuts):
+    rng = np.random.default_rng(len(cuts))
+    op, lp, (o, lse) = _parts(rng, 64, 8, 3, cuts)
+    oc, lc = O.lse_combine(op, lp)
+    assert np.max(np.abs(oc - o)) < 1e-12 and np.max(np.abs(lc - lse)) < 1e-12
+
+
+def test_combine_is_permutation_invariant_and_ignores_empty_parts():
+    rng = np.random.default_rng(9)
+    op, lp, (o, lse) = _parts(rng, 50, 8, 2, [7, 30])
+    perm = [2, 0, 1]
+    a = O.lse_combine(op[perm], lp[perm])
+    empty_o = np.full((1, 2, 8), 123.0)       # garbage values must not leak in
+    empty_l = np.full((1, 2), -np.inf)
+    b = O.lse_combine(np.concatenate([op, empty_o]), np.concatenate([lp, empty_l]))
+    for oc, lc in (a, b):
+        assert np.max(np.abs(oc - o)) < 1e-12 and np.max(np.abs(lc - lse)) < 1e-12
+    one = O.lse_combine(op[:1], lp[:1])
+    assert np.allclose(one[0], op[0], atol=1e-15, rtol=0) and np.allclose(one[1], lp[0], atol=1e-15, rtol=0)
+    none = O.lse_combine(empty_o, empty_l)
+    assert np.all(none[0] == 0) and np.all(np.isneginf(none[1]))
+
+
+def _pages():
+    return json.load(open(os.path.join(GOLDEN, "pages_numbers.json")))
+
+
+def test_window_drops_roughly_99_percent_at_1m():
+    g = _pages()["dropped_fraction_at_1m"]
+    n = 1 << 20
+    frac = 1 - O.draft_entries_read(n, O.SINK_WINDOW, 4, 4096) / O.draft_entries_read(n, O.FULL)
+    assert frac >= g["min"]
+
+
+def test_step_bytes_ratio_sits_in_the_reported_speedup_range():
+    g = _pages()["speedup_range_at_1m"]
+    n0, gamma = 1 << 20, _pages()["draft_steps_per_cycle"]["value"]
+    nat = O.step_kv_bytes(n0, gamma, 10, 2, 256, 2, O.FULL)
+    win = O.step_kv_bytes(n0, gamma, 10, 2, 256, 2, O.SINK_WINDOW, 4, 4096)
+    assert g["lo"] <= nat / win <= g["hi"]
+    # hand count: 10 layers x (n0+4) tokens + 3 draft steps at n0+1..n0+3, 2048 B per token
+    assert nat == 2048 * (10 * (n0 + 4) + (n0 + 1) + (n0 + 2) + (n0 + 3))
+    assert win == 2048 * (10 * (n0 + 4) + 3 * 4100)
+
+
+def test_one_draft_step_costs_a_tenth_of_the_target_read():
+    g = _pages()["draft_to_target_tax"]
+    n0 = 131072
+    per_draft_step = O.step_kv_bytes(n0, 1, 0, 2, 256, 2, O.FULL)
+    target = O.step_kv_bytes(n0, 0, g["layers_target"], 2, 256, 2, O.FULL)
+    ratio = per_draft_step / target
+    assert abs(ratio - g["layers_draft"] / g["layers_target"]) < 1e-3
+    assert abs(ratio - g["measured"]) < 0.015     # the case study measured 8.8%

@@ -1,0 +1,145 @@
+"""Pins for the oracle's visible sets, ring buffer and paged addressing (no GPU)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _list_model_visible(n, S, W):
+    """First S plus last W of the list [0..n-1], duplicates removed (list slicing, no arithmetic)."""
+    xs = list(range(n))
+    keep = xs[:S] + (xs[-W:] if W > 0 else [])
+    return sorted(set(keep))
+
+
+@settings(max_examples=300, deadline=None)
+@given(n=st.integers(0, 400), S=st.integers(0, 16), W=st.integers(1, 128))
+def test_visible_set_is_first_sinks_plus_last_window(n, S, W):
+    got = O.visible_positions(n, O.SINK_WINDOW, S, W)
+    assert list(got) == _list_model_visible(n, S, W)
+    assert len(got) == min(n, S + W)
+    assert O.draft_entries_read(n, O.SINK_WINDOW, S, W) == min(n, S + W)
+
+
+@settings(max_examples=100, deadline=None)
+@given(n=st.integers(1, 200), S=st.integers(0, 8), W=st.integers(1, 64))
+def test_window_covering_context_is_full_attention(n, S, W):
+    if S + W < n:
+        W = n  # force the covering case
+    assert np.array_equal(O.visible_positions(n, O.SINK_WINDOW, S, W), O.visible_positions(n, O.FULL))
+    rng = np.random.default_rng(n)
+    k = rng.standard_normal((n, 2, 8)).astype(np.float32)
+    v = rng.standard_normal((n, 2, 8)).astype(np.float32)
+    q = rng.standard_normal((4, 8))
+    a = O.draft_attention(q, O.LogicalKV(k, "f32"), O.LogicalKV(v, "f32"), n, O.SINK_WINDOW, S, W, 0.35)
+    b = O.draft_attention(q, O.LogicalKV(k, "f32"), O.LogicalKV(v, "f32"), n, O.FULL, 0, 0, 0.35)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])   # bitwise
+
+
+def test_window_read_is_constant_in_context():
+    S, W = 4, 4096
+    reads = [O.draft_entries_read(n, O.SINK_WINDOW, S, W) for n in (4100, 131072, 524288, 1048576, 1048579)]
+    assert reads == [S + W] * len(reads)
+    full = [O.draft_entries_read(n, O.FULL) for n in (131072, 1048576)]
+    assert full == [131072, 1048576]
+
+
+def test_window_attention_matches_attention_over_the_kept_tokens():
+    """sink_window = plain attention over the explicitly sliced sinks + tail of the sequence."""
+    rng = np.random.default_rng(8)
+    n, S, W, D = 300, 3, 40, 8
+    k = rng.standard_normal((n, 1, D)).astype(np.float32)
+    v = rng.standard_normal((n, 1, D)).astype(np.float32)
+    q = rng.standard_normal((2, D))
+    o, lse = O.draft_attention(q, O.LogicalKV(k, "f32"), O.LogicalKV(v, "f32"), n, O.SINK_WINDOW, S, W, 0.2)
+    ks = np.concatenate([k[:S, 0], k[n - W:, 0]]).astype(np.float64)
+    vs = np.concatenate([v[:S, 0], v[n - W:, 0]]).astype(np.float64)
+    s = (q @ ks.T) * 0.2
+    w = np.exp(s)
+    assert np.max(np.abs(o - (w @ vs) / w.sum(1, keepdims=True))) < 1e-12
+    assert np.max(np.abs(lse - np.log(w.sum(1)))) < 1e-12
+
+
+def test_ring_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "ring_s2_w3.json")))
+    S, W = g["sink"], g["window"]
+    assert [O.ring_slot(p, S, W) for p in range(len(g["slot_of_position"]))] == g["slot_of_position"]
+    for n, tags in g["tags_after_n"].items():
+        assert list(O.ring_expected_tags(int(n), S, W)) == tags
+    for n, vis in g["visible_after_n"].items():
+        assert list(O.visible_positions(int(n), O.SINK_WINDOW, S, W)) == vis
+
+
+@pytest.mark.parametrize("S,W,N", [(4, 16, 3), (4, 16, 10), (4, 16, 20), (4, 16, 500), (0, 7, 50), (1, 1, 9), (3, 5, 8)])
+def test_ring_after_n_appends_holds_sinks_and_last_window(S, W, N):
+    """Append one token at a time; the ring must hold exactly the list model's positions."""
+    tags = np.full(S + W, -1, dtype=np.int64)
+    kept = []
+    for p in range(N):
+        O.ring_append(tags, p, 1, S, W)
+        kept.append(p)
+        kept = kept[:S] + kept[S:][-W:]           # list model: first S, last W
+        assert sorted(t for t in tags if t >= 0) == sorted(kept)
+    assert len(set(int(t) for t in tags if t >= 0)) == min(N, S + W)
+    # every held position is visible, and every visible position is held
+    assert sorted(t for t in tags if t >= 0) == list(O.visible_positions(N, O.SINK_WINDOW, S, W))
+    assert np.array_equal(tags, O.window_slot_positions(N, S, W))
+
+
+@pytest.mark.parametrize("S,W,pos,T", [(4, 16, 0, 100), (4, 16, 7, 3), (2, 8, 30, 17), (4, 16, 0, 4), (0, 5, 3, 12)])
+def test_bulk_append_equals_sequential_appends(S, W, pos, T):
+    a = np.full(S + W, -1, dtype=np.int64)
+    b = np.full(S + W, -1, dtype=np.int64)
+    O.ring_append(a, 0, pos, S, W) if pos else None
+    O.ring_append(b, 0, pos, S, W) if pos else None
+    writes = O.ring_append(a, pos, T, S, W)
+    for i in range(T):
+        O.ring_append(b, pos + i, 1, S, W)
+    assert np.array_equal(a, b)
+    slots = [s for _, s in writes]
+    assert len(slots) == len(set(slots))                # no slot written twice
+
+
+def _place_paged(logical, bt_row, bs, num_blocks):
+    """Build a paged pool from a logical [n][H][D] array by block-level slicing."""
+    n, H, D = logical.shape
+    pool = np.zeros((num_blocks, H, bs, D), dtype=logical.dtype)
+    for j in range(-(-n // bs)):
+        seg = logical[j * bs:(j + 1) * bs]               # [<=bs][H][D]
+        pool[bt_row[j], :, :seg.shape[0], :] = seg.transpose(1, 0, 2)
+    return pool
+
+
+@pytest.mark.parametrize("n,bs", [(1, 16), (16, 16), (17, 16), (300, 16), (100, 8)])
+def test_paged_gather_equals_contiguous(n, bs):
+    rng = np.random.default_rng(n)
+    H, D = 2, 8
+    nb = -(-n // bs) + 3
+    bt = rng.permutation(nb).astype(np.int32)
+    logical = rng.standard_normal((n, H, D)).astype(np.float32)
+    pool = _place_paged(logical, bt, bs, nb)
+    src = O.PagedKV(pool, bt, bs, "f32", n)
+    pos = rng.permutation(n)
+    for h in range(H):
+        assert np.array_equal(src.rows(pos, h), logical[pos, h].astype(np.float64))
+    q = rng.standard_normal((4, D))
+    a = O.draft_attention(q, src, src, n, O.FULL, 0, 0, 0.3)
+    b = O.draft_attention(q, O.LogicalKV(logical, "f32"), O.LogicalKV(logical, "f32"), n, O.FULL, 0, 0, 0.3)
+    assert np.array_equal(a[0], b[0])
+
+
+def test_paged_offsets_hand_worked_and_past_2_pow_31():
+    # pool [block][kv_head][16][D]: block 5, head 1, offset 3, D 256, 2 heads
+    assert O.paged_element_offset([9, 5], 16 + 3, 1, 2, 16, 256) == ((5 * 2 + 1) * 16 + 3) * 256
+    # a block id of 300,000 (a 4.8M-token pool) puts the element offset past 2**31
+    big = 300000
+    off = O.paged_element_offset([big] * 2, 15, 1, 2, 16, 256)
+    assert off == big * 2 * 16 * 256 + 1 * 16 * 256 + 15 * 256
+    assert off > 2 ** 31
