@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Decode-step attention benchmark for Windowed-MTP on one MI355X.
+
+One step is the attention of one speculative decode step at 1,048,576 tokens
+of context (the per-decode-step cost model): gamma = 3 draft steps of one MTP
+draft layer (append one entry, draft attention, LSE combine) followed by the
+verify attention of 10 full-attention target layers (append gamma+1 entries,
+verify over all keys with 4 causal queries, LSE combine).  16 query heads,
+2 KV heads, head_dim 256, bf16 KV, fp32 accumulation, paged pools of 16-token
+blocks with a random-permutation block table.
+
+The draft runs in both modes: native (full context from the paged pool) and
+Windowed-MTP (4 sinks + 4,096-token window from the compact ring).  `value` is
+the Windowed-MTP step time in microseconds; the native step and the ratio are
+reported beside it.  Inputs are synthetic and resident in HBM before timing.
+
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from long_context_decode_gqa_amd import wmtp as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M context"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Step:
+    """Device state of one decode step: draft layer (pool + ring) and target layers."""
+
+    def __init__(self, wl, n0, target_layers, chunk_full, chunk_win, split, dev):
+        self.wl, self.n0, self.dev = wl, n0, dev
+        Hq, Hk, D, g = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma
+        self.sh = W.make_shape(Hq, Hk, D, torch.bfloat16, wl.scale)
+        self.chunk_full, self.chunk_win, self.split = chunk_full, chunk_win, split
+        blocks = synth.blocks_for(n0 + g + 1, 16)
+        bt, total = synth.block_table(wl.seed, [blocks], permuted=True)
+        self.bt = torch.from_numpy(bt).to(dev)
+        self.total_blocks = total
+        self.layers = []                      # (k, v, desc): index 0 is the draft layer's native pool
+        for layer in range(target_layers + 1):
+            k = synth.normal((total, Hk, 16, D), wl.seed, ("pool_k", layer), wl.kv_scale, "bf16", dev)
+            v = synth.normal((total, Hk, 16, D), wl.seed, ("pool_v", layer), wl.kv_scale, "bf16", dev)
+            self.layers.append((k, v, W.make_paged(k, v, self.bt)))
+            log(f"  pool {layer} ready")
+        S, Wn = wl.sink, wl.window
+        self.rk = torch.zeros((1, Hk, S + Wn, D), dtype=torch.bfloat16, device=dev)
+        self.rv = torch.zeros_like(self.rk)
+        self.tags = torch.full((1, S + Wn), -1, dtype=torch.int32, device=dev)
+        self.ring = W.make_ring(self.rk, self.rv, self.tags, S, Wn)
+        # ring holds the sinks and the last W context tokens of the draft layer's sequence
+        sink_k = synth.normal((1, S, Hk, D), wl.seed, "ring_sink_k", wl.kv_scale, "bf16", dev)
+        sink_v = synth.normal((1, S, Hk, D), wl.seed, "ring_sink_v", wl.kv_scale, "bf16", dev)
+        tail_k = synth.normal((1, Wn, Hk, D), wl.seed, "ring_tail_k", wl.kv_scale, "bf16", dev)
+        tail_v = synth.normal((1, Wn, Hk, D), wl.seed, "ring_tail_v", wl.kv_scale, "bf16", dev)
+        W.ring_append(self.sh, self.ring, sink_k, sink_v, [0])
+        W.ring_append(self.sh, self.ring, tail_k, tail_v, [n0 - Wn])
+        # per-step inputs
+        self.q_draft = synth.normal((g, 1, Hq, D), wl.seed, "q_draft", 1.0, "bf16", dev)
+        self.k_draft = synth.normal((g, 1, 1, Hk, D), wl.seed, "k_new", wl.kv_scale, "bf16", dev)
+        self.v_draft = synth.normal((g, 1, 1, Hk, D), wl.seed, "v_new", wl.kv_scale, "bf16", dev)
+        self.q_ver = [synth.normal((1, g + 1, Hq, D), wl.seed, ("q_verify", l), 1.0, "bf16", dev)
+                      for l in range(target_layers)]
+        self.k_ver = synth.normal((1, g + 1, Hk, D), wl.seed, "k_new_layer", wl.kv_scale, "bf16", dev)
+        self.v_ver = synth.normal((1, g + 1, Hk, D), wl.seed, "v_new_layer", wl.kv_scale, "bf16", dev)
+        # workspaces and outputs
+        lens_d = [n0 + g]
+        self.ws_full = W.workspace(W.draft_workspace_bytes(W.FULL, self.sh, lens_d, chunk_full), dev)
+        self.ws_win = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, self.sh, lens_d, chunk_win, S, Wn), dev)
+        self.ws_ver = W.workspace(W.verify_workspace_bytes(self.sh, g + 1, [n0 + g + 1], split), dev)
+        self.out_d = torch.empty((1, Hq, D), dtype=torch.float32, device=dev)
+        self.lse_d = torch.empty((1, Hq), dtype=torch.float32, device=dev)
+        self.out_v = torch.empty((1, (g + 1) * Hq, D), dtype=torch.float32, device=dev)
+        self.lse_v = torch.empty((1, (g + 1) * Hq), dtype=torch.float32, device=dev)
+
+    def draft(self, mode, flag, ev=None):
+        g, n0 = self.wl.gamma, self.n0
+        for j in range(g):
+            pos, n = n0 + j, n0 + j + 1
+            if mode == W.FULL:
+                W.paged_append(self.sh, self.layers[0][2], self.k_draft[j], self.v_draft[j], [pos])
+                if ev is not None:
+                    ev[0].record()
+                parts = W.draft_attn(W.FULL | flag, self.sh, self.q_draft[j], [n], self.ws_full,
+                                     paged=self.layers[0][2], chunk_tokens=self.chunk_full)
+            else:
+                W.ring_append(self.sh, self.ring, self.k_draft[j], self.v_draft[j], [pos])
+                if ev is not None:
+                    ev[0].record()
+                parts = W.draft_attn(W.SINK_WINDOW | flag, self.sh, self.q_draft[j], [n], self.ws_win,
+                                     ring=self.ring, chunk_tokens=self.chunk_win)
+            if ev is not None:
+                ev[1].record()
+                ev = None
+            W.combine(parts, self.out_d, self.lse_d)
+
+    def verify(self, ev_list=None):
+        g, n0 = self.wl.gamma, self.n0
+        for l in range(len(self.layers) - 1):
+            desc = self.layers[l + 1][2]
+            W.paged_append(self.sh, desc, self.k_ver, self.v_ver, [n0])
+            if ev_list is not None:
+                ev_list[l][0].record()
+            parts = W.verify_attn(self.sh, self.q_ver[l], g + 1, desc, [n0 + g + 1], self.ws_ver, self.split)
+            if ev_list is not None:
+                ev_list[l][1].record()
+            W.combine(parts, self.out_v, self.lse_v)
+
+
+def kv_bytes(tokens, wl):
+    return tokens * wl.num_kv_heads * wl.head_dim * 2 * 2
+
+
+def verify_launch_bytes(n, wl, t_q):
+    """Algorithmic bytes of one verify launch: visible K/V, queries, block-table entries."""
+    return kv_bytes(n, wl) + t_q * wl.num_q_heads * wl.head_dim * 2 + synth.blocks_for(n, 16) * 4
+
+
+def draft_launch_bytes(entries, wl, paged):
+    b = kv_bytes(entries, wl) + wl.num_q_heads * wl.head_dim * 2
+    return b + (synth.blocks_for(entries, 16) * 4 if paged else entries * 4)
+
+
+def time_steps(step, mode, flag, steps, warmup):
+    """Warmup, then time `steps` decode steps; per-launch events on the dominant kernels."""
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        step.draft(mode, flag)
+        step.verify()
+    torch.cuda.synchronize()
+    L = len(step.layers) - 1
+    ev_v = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+            for _ in range(steps)]
+    ev_d = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(steps):
+        step.draft(mode, flag, ev_d[s])
+        step.verify(ev_v[s])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ver_ms = [a.elapsed_time(b) for row in ev_v for a, b in row]
+    draft_ms = [a.elapsed_time(b) for a, b in ev_d]
+    return total_ms / steps, float(np.mean(ver_ms)), float(np.mean(draft_ms))
+
+
+def cpu_baseline(wl, n0):
+    """The float64 oracle on a bounded sample, scaled to one decode step (both draft modes)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    Hk, D, G = wl.num_kv_heads, wl.head_dim, wl.group
+    sample_n = 131072
+    k = (rng.standard_normal((sample_n, 1, D), dtype=np.float32) * 0.5)
+    v = (rng.standard_normal((sample_n, 1, D), dtype=np.float32) * 0.5)
+    kb = torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    vb = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q = rng.standard_normal((wl.gamma + 1, G, D))
+    src_k, src_v = O.LogicalKV(kb, "bf16"), O.LogicalKV(vb, "bf16")
+    t0 = time.perf_counter()
+    for i in range(wl.gamma + 1):                 # one verify layer, one KV head, 131,072 keys
+        O.attention_over(q[i], src_k, src_v, np.arange(sample_n - wl.gamma + i), 0, wl.scale)
+    t_verify = time.perf_counter() - t0
+    win = wl.sink + wl.window
+    t0 = time.perf_counter()
+    O.attention_over(q[0], src_k, src_v, O.visible_positions(sample_n, O.SINK_WINDOW, wl.sink, wl.window), 0,
+                     wl.scale)
+    t_win = time.perf_counter() - t0
+    # scale: verify cost is linear in keys; per step = target_layers x Hk heads; draft native = one
+    # query token per step over n0 keys (a quarter of a verify head-layer's work), window = as measured
+    per_key = t_verify / (sample_n * (wl.gamma + 1))
+    verify_step = per_key * (n0 + wl.gamma + 1) * (wl.gamma + 1) * Hk * wl.target_layers
+    native_draft = per_key * (n0 + 2) * Hk * wl.gamma
+    win_draft = t_win * Hk * wl.gamma
+    return {
+        "value": round((verify_step + win_draft) * 1e6, 1),
+        "unit": "us/decode-step",
+        "native_value": round((verify_step + native_draft) * 1e6, 1),
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 oracle, 1 KV head x {sample_n} keys x {wl.gamma + 1} causal queries (verify) and "
+                   f"1 KV head x {win} window entries (draft); scaled linearly in keys to {wl.target_layers} "
+                   f"layers x {Hk} KV heads x {n0} keys + {wl.gamma} draft steps; measured "
+                   f"{t_verify + t_win:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--context", type=int, default=1 << 20)
+    ap.add_argument("--chunk-full", type=int, default=0, help="draft split size, native mode (0 = library default)")
+    ap.add_argument("--chunk-window", type=int, default=0, help="draft split size, window mode (0 = default)")
+    ap.add_argument("--split", type=int, default=0, help="verify split size (0 = library default)")
+    ap.add_argument("--exact-pv", action="store_true", help="draft PV with fp32 weights instead of bf16 pairs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    W.load()
+    dev = "cuda"
+    wl = synth.workload("step_1m_bf16", contexts=(args.context,))
+    n0 = args.context
+    flag = 0 if args.exact_pv else W.DRAFT_FAST_PV
+    log(f"setup: {wl.target_layers} target layers + 1 draft layer at {n0} tokens")
+    step = Step(wl, n0, wl.target_layers, args.chunk_full, args.chunk_window,
+                args.split, dev)
+
+    log("timing windowed step")
+    win_ms, ver_ms, dwin_ms = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup)
+    log("timing native step")
+    nat_ms, ver_ms2, dnat_ms = time_steps(step, W.FULL, flag, args.steps, args.warmup)
+
+    g = wl.gamma
+    bytes_win = sum(kv_bytes(min(n0 + j, wl.sink + wl.window), wl) for j in range(1, g + 1)) + \
+        wl.target_layers * kv_bytes(n0 + g + 1, wl)
+    bytes_nat = sum(kv_bytes(n0 + j, wl) for j in range(1, g + 1)) + wl.target_layers * kv_bytes(n0 + g + 1, wl)
+    ver_bytes = verify_launch_bytes(n0 + g + 1, wl, g + 1)
+    ver_avg_ms = (ver_ms + ver_ms2) / 2
+    achieved = ver_bytes / (ver_avg_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(win_ms * 1e3, 1),
+        "unit": "us/decode-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(win_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"per-decode-step attention at {n0} tokens: {wl.target_layers} target layers x verify "
+                         f"({g + 1} causal queries) + 1 draft layer x {g} steps, 16 q heads / 2 KV heads, "
+                         f"d=256, bf16 KV, paged 16-token blocks (random permutation); draft in sink_window "
+                         f"mode S={wl.sink} W={wl.window}"),
+            "context": n0, "gamma": g, "target_layers": wl.target_layers,
+            "draft_pv": "fp32 weights" if args.exact_pv else "bf16 weight pairs",
+        },
+        "windowed_us_per_step": round(win_ms * 1e3, 1),
+        "native_us_per_step": round(nat_ms * 1e3, 1),
+        "ratio_native_over_windowed": round(nat_ms / win_ms, 4),
+        "windowed_gbps": round(bytes_win / (win_ms * 1e-3) / 1e9, 1),
+        "native_gbps": round(bytes_nat / (nat_ms * 1e-3) / 1e9, 1),
+        "windowed_pct_peak": round(100 * bytes_win / (win_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "native_pct_peak": round(100 * bytes_nat / (nat_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "kernels_us": {
+            "verify_per_layer": round(ver_avg_ms * 1e3, 2),
+            "draft_window_per_step": round(dwin_ms * 1e3, 2),
+            "draft_native_per_step": round(dnat_ms * 1e3, 2),
+        },
+        "roofline": {
+            "kernel": "verify_kernel<8> (10 launches per step)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+    }
+    native_draft_bytes = draft_launch_bytes(n0 + 1, wl, True)
+    res["draft_native_gbps"] = round(native_draft_bytes / (dnat_ms * 1e-3) / 1e9, 1)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)")
+        res["cpu_baseline"] = cpu_baseline(wl, n0)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+/*
+ * wmtp.h - Windowed-MTP decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the problem statement of "Windowed-MTP: Removing the
+ * Full-Context Draft-KV Tax at Million-Token Context" (arxivlens.com summary,
+ * Abstract): a Multi-Token-Prediction draft head runs gamma draft forwards per
+ * decode step, each attending either over the whole KV cache (native MTP) or
+ * over attention-sink tokens plus a window of recent tokens kept in a compact
+ * ring buffer (Windowed-MTP); the target verifies gamma+1 tokens with
+ * full-context attention.  The case study "Does speculative decode still pay
+ * at 128K context?" (howtospark.com, Method) fixes one verify cycle as three
+ * draft forwards plus one batched verify.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Ownership: the caller allocates and owns every buffer.  The library never
+ *    allocates, frees or keeps a pointer after a call returns.
+ *  - Pointers: arguments documented "device" are HIP device pointers; "host"
+ *    arguments are read on the host before the call returns.
+ *  - Streams: `stream` is a hipStream_t passed as void*; NULL is the default
+ *    stream.  Every call that launches work is asynchronous, performs no host
+ *    synchronisation and copies nothing host-to-device, so a sequence of calls
+ *    can be captured in a HIP graph.
+ *  - Errors: every int-returning call returns WMTP_OK (0) or a negative
+ *    WMTP_E* code.  Argument checks run before any HIP call; on an error no
+ *    work is enqueued.  No call aborts, prints, or throws across the boundary.
+ *    WMTP_ELAUNCH reports a failed kernel launch (hipGetLastError).
+ *  - Thread safety: the library has no mutable global state.
+ *
+ * Numbers
+ * -------
+ *  - dtype WMTP_F32: IEEE binary32.  dtype WMTP_BF16: bfloat16 (upper half of
+ *    a binary32).  q, k and v share one dtype; accumulation is always fp32.
+ *  - head_dim D is 64, 128 or 256; G = num_q_heads / num_kv_heads is 1, 2, 4
+ *    or 8; query head h uses KV head h / G.
+ *  - scale multiplies q.k (the usual value is 1/sqrt(D)).
+ *  - lse outputs are natural logs of sum_t exp(scale * q.k_t).
+ *
+ * Memory layouts (row-major, innermost last)
+ * ------------------------------------------
+ *  paged pool   k, v: [num_blocks][num_kv_heads][block_size][D], block_size 16
+ *  block table  [batch][max_blocks_per_seq] int32 physical block ids
+ *  ring         k, v: [batch][num_kv_heads][sink + window][D]
+ *               slot_pos: [batch][sink + window] int32 (absolute position, -1 empty)
+ *               slot(p) = p for p < sink, else sink + (p - sink) % window
+ *  draft q      [batch][num_q_heads][D]
+ *  verify q     [batch][t_q][num_q_heads][D]
+ *  new k, v     [batch][t_new][num_kv_heads][D]
+ *  partials     o: [total_splits][rows_per_seq][D] fp32, lse: [total_splits][rows_per_seq] fp32
+ *  combine out  [batch][rows_per_seq][D] (fp32 or bf16), lse [batch][rows_per_seq] fp32
+ *               rows_per_seq = num_q_heads for the draft, t_q * num_q_heads for
+ *               verify (row = i * num_q_heads + h for query token i, head h).
+ */
+#ifndef WMTP_H
+#define WMTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+#define WMTP_OK             0
+#define WMTP_EINVAL        -1   /* null pointer, bad size, bad enum, inconsistent shapes      */
+#define WMTP_EUNSUPPORTED  -2   /* head_dim, group size, dtype or row count not built         */
+#define WMTP_EALIGN        -3   /* a k/v/q/output base pointer is not 16-byte aligned          */
+#define WMTP_EWORKSPACE    -4   /* workspace too small for the planned splits                  */
+#define WMTP_ELAUNCH       -5   /* a kernel launch failed                                      */
+
+/* ---------------------------------------------------------------- enums */
+#define WMTP_F32   0
+#define WMTP_BF16  1
+
+#define WMTP_FULL         0     /* native MTP draft: every cached entry                       */
+#define WMTP_SINK_WINDOW  1     /* Windowed-MTP draft: sink + window entries from the ring     */
+/* Optional flag OR-ed into the draft mode (bf16 only): the PV product takes the
+ * softmax weights rounded to bf16 and uses v_dot2_f32_bf16 over key pairs
+ * instead of fp32 FMAs.  The normaliser is summed from the same rounded
+ * weights.  Without it the PV product uses the fp32 weights. */
+#define WMTP_DRAFT_FAST_PV 0x10
+
+#define WMTP_MAX_BATCH   64     /* sequences per call                                         */
+#define WMTP_BLOCK_SIZE  16     /* tokens per paged block                                     */
+#define WMTP_MAX_VERIFY_ROWS 32 /* t_q * G per KV head in one verify call                     */
+
+/* ---------------------------------------------------------------- descriptors */
+typedef struct wmtp_shape {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float   scale;          /* multiplies q.k                                    */
+  int32_t dtype;          /* WMTP_F32 or WMTP_BF16, for q, k and v             */
+} wmtp_shape;
+
+typedef struct wmtp_paged {
+  void*          k;                   /* device, [num_blocks][H_kv][16][D]        */
+  void*          v;                   /* device, same layout as k                 */
+  const int32_t* block_table;         /* device, [batch][max_blocks_per_seq]      */
+  int32_t        block_size;          /* must be WMTP_BLOCK_SIZE                  */
+  int32_t        max_blocks_per_seq;  /* row stride of block_table                */
+  int64_t        num_blocks;          /* physical blocks in k and v               */
+} wmtp_paged;
+
+typedef struct wmtp_ring {
+  void*    k;          /* device, [batch][H_kv][sink+window][D]  */
+  void*    v;          /* device, same layout as k               */
+  int32_t* slot_pos;   /* device, [batch][sink+window]           */
+  int32_t  sink;       /* S >= 0                                 */
+  int32_t  window;     /* W >= 1                                 */
+} wmtp_ring;
+
+/* Split-K partial results, written by wmtp_draft_attn / wmtp_verify_attn into
+ * the caller's workspace and read by wmtp_combine.  Sequence b owns splits
+ * split_base[b] .. split_base[b+1]-1; every split holds all rows of b.  The
+ * struct is plain data (host memory) and may be copied. */
+typedef struct wmtp_partials {
+  float*  o;                                /* device, [total_splits][rows_per_seq][D] */
+  float*  lse;                              /* device, [total_splits][rows_per_seq]    */
+  int32_t batch;
+  int32_t rows_per_seq;
+  int32_t head_dim;
+  int32_t total_splits;
+  int32_t split_base[WMTP_MAX_BATCH + 1];   /* host copy of the per-sequence offsets   */
+} wmtp_partials;
+
+/* ---------------------------------------------------------------- planning (host only) */
+
+/* Bytes of workspace wmtp_draft_attn needs.  Arguments as for wmtp_draft_attn
+ * (sink/window are read only in WMTP_SINK_WINDOW mode).  Returns >= 0 bytes or
+ * a negative WMTP_E* code.  Makes no HIP call. */
+int64_t wmtp_draft_workspace_bytes(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens_host,
+                                   int32_t batch, int32_t chunk_tokens, int32_t sink, int32_t window);
+
+/* Bytes of workspace wmtp_verify_attn needs.  Makes no HIP call. */
+int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const int32_t* seq_lens_host,
+                                    int32_t batch, int32_t split_tokens);
+
+/* ---------------------------------------------------------------- the hot path */
+
+/* One draft-attention step for `batch` sequences (Windowed-MTP summary,
+ * Abstract; readpriors.com post, What happened).
+ *
+ *  mode (low 4 bits) == WMTP_FULL: sequence b attends to positions 0..n_b-1 read from
+ *                            the paged pool `kv` (`ring` may be NULL).
+ *  mode (low 4 bits) == WMTP_SINK_WINDOW: sequence b attends to positions {0..S-1} and
+ *                            {n_b-W..n_b-1}, read from `ring` (`kv` may be NULL).
+ *                            Ring slots whose slot_pos tag is not one of those
+ *                            positions are ignored.
+ *  n_b = seq_lens_host[b] (host) is the length after this step's own entry was
+ *  appended, so the query attends to itself.  q: device [batch][H_q][D].
+ *  chunk_tokens: entries per split (a multiple of 64; 0 = library default).
+ *  The call writes split partials into `workspace` (device, >= the size from
+ *  wmtp_draft_workspace_bytes, 256-byte aligned) and describes them in
+ *  *parts (host).  Finish with wmtp_combine. */
+int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv,
+                    const wmtp_ring* ring, const int32_t* seq_lens_host, int32_t batch,
+                    int32_t chunk_tokens, void* workspace, size_t workspace_bytes,
+                    wmtp_partials* parts, void* stream);
+
+/* Full-context verify attention of t_q query tokens for one target layer
+ * (Windowed-MTP summary, Abstract: verification stays full-context).
+ *  q: device [batch][t_q][H_q][D].  n_b = seq_lens_host[b] includes the t_q
+ *  query tokens' own entries; query token i attends causally to positions
+ *  0..n_b-t_q+i.  Requires t_q * G <= WMTP_MAX_VERIFY_ROWS, dtype bf16 and
+ *  head_dim 256 (other shapes return WMTP_EUNSUPPORTED).
+ *  split_tokens: entries per split (a multiple of 32; 0 = library default).
+ *  Workspace and *parts as for wmtp_draft_attn. */
+int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv,
+                     const int32_t* seq_lens_host, int32_t batch, int32_t split_tokens,
+                     void* workspace, size_t workspace_bytes, wmtp_partials* parts, void* stream);
+
+/* Log-sum-exp merge of split partials (flash-decoding combine):
+ *  L = log sum_i exp(lse_i),  out = sum_i exp(lse_i - L) * o_i  per row.
+ *  Splits with lse = -inf carry no keys and are skipped; a row with no live
+ *  split gets out = 0 and lse = -inf.
+ *  out: device [batch][rows_per_seq][D], dtype out_dtype (WMTP_F32 or
+ *  WMTP_BF16, round-to-nearest-even).  lse_out: device [batch][rows_per_seq]
+ *  fp32, or NULL. */
+int wmtp_combine(const wmtp_partials* parts, void* out, int32_t out_dtype, float* lse_out, void* stream);
+
+/* Append t_new tokens per sequence to the compact ring (Windowed-MTP summary,
+ * Abstract: the ring holds the draft's window).  Token i of sequence b has
+ * absolute position p = pos_host[b] + i (pos_host: host, >= 0) and is written
+ * to slot(p), with slot_pos[b][slot(p)] = p, only if p < sink or
+ * p > pos_host[b] + t_new - 1 - window (it can still be visible after the
+ * append); so an append longer than the window writes each slot once.
+ * k_new, v_new: device [batch][t_new][H_kv][D]. */
+int wmtp_ring_append(const wmtp_shape* shape, const wmtp_ring* ring, const void* k_new, const void* v_new,
+                     const int32_t* pos_host, int32_t batch, int32_t t_new, void* stream);
+
+/* Write t_new tokens per sequence into the paged pool at positions
+ * pos_host[b] + i through the block table (the native draft's pool and each
+ * target layer's cache).  The block-table row must already cover the
+ * positions.  k_new, v_new: device [batch][t_new][H_kv][D]. */
+int wmtp_paged_append(const wmtp_shape* shape, const wmtp_paged* kv, const void* k_new, const void* v_new,
+                      const int32_t* pos_host, int32_t batch, int32_t t_new, void* stream);
+
+/* ---------------------------------------------------------------- index resolution (test hooks) */
+
+/* Element offsets of (sequence b, position positions[i], KV head h, d = 0) in
+ * the paged pool, computed on the GPU by the same device code the kernels
+ * use.  positions: device int32 [n]; offsets_out: device int64 [n].  A
+ * position that is negative or past the block-table row gets -1. */
+int wmtp_debug_resolve_paged(const wmtp_paged* kv, int32_t num_kv_heads, int32_t head_dim, int32_t b,
+                             int32_t h, const int32_t* positions, int32_t n, int64_t* offsets_out,
+                             void* stream);
+
+/* Ring slot of every listed position: slots_out[i] = slot(positions[i]).
+ * positions: device int32 [n] (>= 0); slots_out: device int32 [n]. */
+int wmtp_debug_resolve_ring(int32_t sink, int32_t window, const int32_t* positions, int32_t n,
+                            int32_t* slots_out, void* stream);
+
+/* For a query at length n, the position each ring slot must hold for the
+ * sink+window visible set (-1 if the slot holds none).  out: device int32 [sink+window]. */
+int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t n, int32_t* out, void* stream);
+
+/* ---------------------------------------------------------------- misc */
+const char* wmtp_status_str(int status);
+const char* wmtp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WMTP_H */

@@ -1,0 +1,375 @@
+// C ABI of libwmtp: argument checks, split planning and kernel dispatch.
+//
+// Every entry point validates all of its arguments before making any HIP call,
+// so an invalid call enqueues nothing and can be tested on a machine without a
+// GPU.  Nothing here allocates, synchronises or keeps state between calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "wmtp.h"
+#include "wmtp_launch.hpp"
+
+using namespace wmtp;
+
+namespace {
+
+constexpr int kDraftDefaultChunkFull = 1024;
+constexpr int kDraftDefaultChunkWindow = 256;
+constexpr int kVerifyDefaultSplit = 2048;
+constexpr int kDraftTile = 64;
+constexpr int kVerifyTile = 32;    // keys per verify tile
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int elem_bytes(int dtype) { return dtype == WMTP_BF16 ? 2 : 4; }
+
+int check_shape(const wmtp_shape* s) {
+  if (!s) return WMTP_EINVAL;
+  if (s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->num_q_heads % s->num_kv_heads != 0) return WMTP_EINVAL;
+  if (s->dtype != WMTP_F32 && s->dtype != WMTP_BF16) return WMTP_EINVAL;
+  if (!std::isfinite(s->scale)) return WMTP_EINVAL;
+  const int g = s->num_q_heads / s->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return WMTP_EUNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256) return WMTP_EUNSUPPORTED;
+  return WMTP_OK;
+}
+
+int check_paged(const wmtp_paged* kv, bool need_table) {
+  if (!kv || !kv->k || !kv->v) return WMTP_EINVAL;
+  if (need_table && !kv->block_table) return WMTP_EINVAL;
+  if (kv->block_size != WMTP_BLOCK_SIZE) return WMTP_EUNSUPPORTED;
+  if (kv->max_blocks_per_seq <= 0 || kv->num_blocks <= 0) return WMTP_EINVAL;
+  if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return WMTP_EALIGN;
+  return WMTP_OK;
+}
+
+int check_ring(const wmtp_ring* r) {
+  if (!r || !r->k || !r->v || !r->slot_pos) return WMTP_EINVAL;
+  if (r->sink < 0 || r->window < 1) return WMTP_EINVAL;
+  if ((int64_t)r->sink + r->window > (int64_t)INT32_MAX / 2) return WMTP_EINVAL;
+  if (!aligned(r->k, 16) || !aligned(r->v, 16) || !aligned(r->slot_pos, 4)) return WMTP_EALIGN;
+  return WMTP_OK;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+struct Plan {
+  int32_t total = 0;
+  int32_t rows = 0;
+  int32_t split_base[WMTP_MAX_BATCH + 1] = {};
+  int64_t lse_off = 0;
+  int64_t bytes = 0;
+};
+
+// Splits of `chunk` entries over per-sequence visible counts `vis`.
+int make_plan(const int64_t* vis, int batch, int chunk, int rows, int head_dim, int kv_heads, Plan* p) {
+  int64_t total = 0;
+  p->split_base[0] = 0;
+  for (int b = 0; b < batch; ++b) {
+    total += (vis[b] + chunk - 1) / chunk;
+    if (total * kv_heads > INT32_MAX) return WMTP_EINVAL;
+    p->split_base[b + 1] = (int32_t)total;
+  }
+  p->total = (int32_t)total;
+  p->rows = rows;
+  const int64_t o_bytes = total * rows * (int64_t)head_dim * 4;
+  p->lse_off = align256(o_bytes);
+  p->bytes = p->lse_off + align256(total * rows * 4);
+  return WMTP_OK;
+}
+
+int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, int32_t batch, int32_t chunk,
+               int32_t sink, int32_t window, Plan* p, int32_t* chunk_out) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const int base_mode = mode & 0xF;
+  if (base_mode != WMTP_FULL && base_mode != WMTP_SINK_WINDOW) return WMTP_EINVAL;
+  if ((mode & ~0xF) & ~WMTP_DRAFT_FAST_PV) return WMTP_EINVAL;
+  if (!seq_lens || batch < 1 || batch > WMTP_MAX_BATCH) return WMTP_EINVAL;
+  if (chunk == 0) chunk = base_mode == WMTP_FULL ? kDraftDefaultChunkFull : kDraftDefaultChunkWindow;
+  if (chunk < kDraftTile || chunk % kDraftTile != 0) return WMTP_EINVAL;
+  if (base_mode == WMTP_SINK_WINDOW && (sink < 0 || window < 1)) return WMTP_EINVAL;
+  int64_t vis[WMTP_MAX_BATCH];
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 0) return WMTP_EINVAL;
+    vis[b] = base_mode == WMTP_FULL ? seq_lens[b] : std::min<int64_t>(seq_lens[b], (int64_t)sink + window);
+  }
+  *chunk_out = chunk;
+  return make_plan(vis, batch, chunk, shape->num_q_heads, shape->head_dim, shape->num_kv_heads, p);
+}
+
+int verify_plan(const wmtp_shape* shape, int32_t t_q, const int32_t* seq_lens, int32_t batch, int32_t split,
+                Plan* p, int32_t* split_out) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (shape->dtype != WMTP_BF16 || shape->head_dim != 256) return WMTP_EUNSUPPORTED;
+  if (!seq_lens || batch < 1 || batch > WMTP_MAX_BATCH) return WMTP_EINVAL;
+  if (t_q < 1) return WMTP_EINVAL;
+  const int g = shape->num_q_heads / shape->num_kv_heads;
+  if ((int64_t)t_q * g > WMTP_MAX_VERIFY_ROWS) return WMTP_EUNSUPPORTED;
+  if (split == 0) split = kVerifyDefaultSplit;
+  if (split < kVerifyTile || split % kVerifyTile != 0) return WMTP_EINVAL;
+  int64_t vis[WMTP_MAX_BATCH];
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens[b] < t_q) return WMTP_EINVAL;   // the queries' own keys are in the cache
+    vis[b] = seq_lens[b];
+  }
+  *split_out = split;
+  return make_plan(vis, batch, split, t_q * shape->num_q_heads, shape->head_dim, shape->num_kv_heads, p);
+}
+
+void fill_parts(const Plan& p, void* ws, int batch, int head_dim, wmtp_partials* parts) {
+  parts->o = static_cast<float*>(ws);
+  parts->lse = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.lse_off);
+  parts->batch = batch;
+  parts->rows_per_seq = p.rows;
+  parts->head_dim = head_dim;
+  parts->total_splits = p.total;
+  std::memset(parts->split_base, 0, sizeof(parts->split_base));
+  for (int b = 0; b <= batch; ++b) parts->split_base[b] = p.split_base[b];
+}
+
+void fill_split_args(SplitArgs& a, const wmtp_shape* s, const Plan& p, const int32_t* seq_lens, int batch, int chunk,
+                     const wmtp_partials* parts) {
+  std::memset(&a, 0, sizeof(a));
+  a.part_o = parts->o;
+  a.part_lse = parts->lse;
+  a.num_q_heads = s->num_q_heads;
+  a.num_kv_heads = s->num_kv_heads;
+  a.chunk = chunk;
+  a.batch = batch;
+  a.scale_log2 = s->scale * 1.44269504088896340736f;
+  for (int b = 0; b <= batch; ++b) a.split_base[b] = p.split_base[b];
+  for (int b = 0; b < batch; ++b) a.seq_len[b] = seq_lens[b];
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? WMTP_OK : WMTP_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t wmtp_draft_workspace_bytes(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens_host, int32_t batch,
+                                   int32_t chunk_tokens, int32_t sink, int32_t window) {
+  Plan p;
+  int32_t chunk = 0;
+  const int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, &p, &chunk);
+  return st ? st : p.bytes;
+}
+
+int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const int32_t* seq_lens_host, int32_t batch,
+                                    int32_t split_tokens) {
+  Plan p;
+  int32_t split = 0;
+  const int st = verify_plan(shape, t_q, seq_lens_host, batch, split_tokens, &p, &split);
+  return st ? st : p.bytes;
+}
+
+int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv, const wmtp_ring* ring,
+                    const int32_t* seq_lens_host, int32_t batch, int32_t chunk_tokens, void* workspace,
+                    size_t workspace_bytes, wmtp_partials* parts, void* stream) {
+  const int base_mode = mode & 0xF;
+  int32_t sink = 0, window = 1;
+  if (base_mode == WMTP_SINK_WINDOW) {
+    const int st = check_ring(ring);
+    if (st) return st;
+    sink = ring->sink;
+    window = ring->window;
+  }
+  Plan p;
+  int32_t chunk = 0;
+  int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, &p, &chunk);
+  if (st) return st;
+  if (!q || !parts) return WMTP_EINVAL;
+  if (!aligned(q, 16)) return WMTP_EALIGN;
+  if (base_mode == WMTP_FULL) {
+    st = check_paged(kv, true);
+    if (st) return st;
+    for (int b = 0; b < batch; ++b)
+      if ((int64_t)(seq_lens_host[b] + WMTP_BLOCK_SIZE - 1) / WMTP_BLOCK_SIZE > kv->max_blocks_per_seq)
+        return WMTP_EINVAL;
+  }
+  if (!workspace && p.bytes > 0) return WMTP_EINVAL;
+  if (!aligned(workspace, 256)) return WMTP_EALIGN;
+  if ((int64_t)workspace_bytes < p.bytes) return WMTP_EWORKSPACE;
+
+  fill_parts(p, workspace, batch, shape->head_dim, parts);
+  SplitArgs a;
+  fill_split_args(a, shape, p, seq_lens_host, batch, chunk, parts);
+  a.q = q;
+  if (base_mode == WMTP_FULL) {
+    a.k = kv->k;
+    a.v = kv->v;
+    a.block_table = kv->block_table;
+    a.bt_stride = kv->max_blocks_per_seq;
+    a.max_block = kv->num_blocks - 1;
+  } else {
+    a.k = ring->k;
+    a.v = ring->v;
+    a.slot_pos = ring->slot_pos;
+    a.slots = ring->sink + ring->window;
+    a.sink = ring->sink;
+    a.window = ring->window;
+  }
+  const int grid = p.total * shape->num_kv_heads;
+  const bool fast_pv = (mode & WMTP_DRAFT_FAST_PV) != 0 && shape->dtype == WMTP_BF16;
+  return launch_status(launch_draft(shape->dtype, shape->head_dim, shape->num_q_heads / shape->num_kv_heads,
+                                    base_mode == WMTP_SINK_WINDOW, fast_pv, a, grid,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv,
+                     const int32_t* seq_lens_host, int32_t batch, int32_t split_tokens, void* workspace,
+                     size_t workspace_bytes, wmtp_partials* parts, void* stream) {
+  Plan p;
+  int32_t split = 0;
+  int st = verify_plan(shape, t_q, seq_lens_host, batch, split_tokens, &p, &split);
+  if (st) return st;
+  if (!q || !parts) return WMTP_EINVAL;
+  if (!aligned(q, 16)) return WMTP_EALIGN;
+  st = check_paged(kv, true);
+  if (st) return st;
+  for (int b = 0; b < batch; ++b)
+    if ((int64_t)(seq_lens_host[b] + WMTP_BLOCK_SIZE - 1) / WMTP_BLOCK_SIZE > kv->max_blocks_per_seq)
+      return WMTP_EINVAL;
+  if (!workspace && p.bytes > 0) return WMTP_EINVAL;
+  if (!aligned(workspace, 256)) return WMTP_EALIGN;
+  if ((int64_t)workspace_bytes < p.bytes) return WMTP_EWORKSPACE;
+
+  fill_parts(p, workspace, batch, shape->head_dim, parts);
+  SplitArgs a;
+  fill_split_args(a, shape, p, seq_lens_host, batch, split, parts);
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.block_table = kv->block_table;
+  a.bt_stride = kv->max_blocks_per_seq;
+  a.max_block = kv->num_blocks - 1;
+  a.t_q = t_q;
+  const int grid = p.total * shape->num_kv_heads;
+  return launch_status(launch_verify(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, a, grid,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int wmtp_combine(const wmtp_partials* parts, void* out, int32_t out_dtype, float* lse_out, void* stream) {
+  if (!parts || !out) return WMTP_EINVAL;
+  if (out_dtype != WMTP_F32 && out_dtype != WMTP_BF16) return WMTP_EINVAL;
+  if (parts->batch < 1 || parts->batch > WMTP_MAX_BATCH || parts->rows_per_seq < 1) return WMTP_EINVAL;
+  if (parts->head_dim != 64 && parts->head_dim != 128 && parts->head_dim != 256) return WMTP_EUNSUPPORTED;
+  if (parts->split_base[0] != 0 || parts->split_base[parts->batch] != parts->total_splits) return WMTP_EINVAL;
+  for (int b = 0; b < parts->batch; ++b)
+    if (parts->split_base[b + 1] < parts->split_base[b]) return WMTP_EINVAL;
+  if (parts->total_splits > 0 && (!parts->o || !parts->lse)) return WMTP_EINVAL;
+  if (!aligned(parts->o, 16) || !aligned(out, 16) || !aligned(lse_out, 4)) return WMTP_EALIGN;
+  CombineArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.part_o = parts->o;
+  a.part_lse = parts->lse;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.rows = parts->rows_per_seq;
+  a.head_dim = parts->head_dim;
+  a.batch = parts->batch;
+  a.out_bf16 = out_dtype == WMTP_BF16;
+  for (int b = 0; b <= parts->batch; ++b) a.split_base[b] = parts->split_base[b];
+  return launch_status(launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+static int append_common(const wmtp_shape* shape, const void* k_new, const void* v_new, const int32_t* pos_host,
+                         int32_t batch, int32_t t_new, AppendArgs* a) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (!pos_host || batch < 1 || batch > WMTP_MAX_BATCH || t_new < 0) return WMTP_EINVAL;
+  if (t_new > 0 && (!k_new || !v_new)) return WMTP_EINVAL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return WMTP_EALIGN;
+  if ((int64_t)batch * t_new > INT32_MAX) return WMTP_EINVAL;
+  std::memset(a, 0, sizeof(*a));
+  for (int b = 0; b < batch; ++b) {
+    if (pos_host[b] < 0 || (int64_t)pos_host[b] + t_new > INT32_MAX) return WMTP_EINVAL;
+    a->pos[b] = pos_host[b];
+  }
+  a->k_new = k_new;
+  a->v_new = v_new;
+  a->num_kv_heads = shape->num_kv_heads;
+  a->row_bytes = shape->head_dim * elem_bytes(shape->dtype);
+  a->t_new = t_new;
+  return WMTP_OK;
+}
+
+int wmtp_ring_append(const wmtp_shape* shape, const wmtp_ring* ring, const void* k_new, const void* v_new,
+                     const int32_t* pos_host, int32_t batch, int32_t t_new, void* stream) {
+  int st = check_ring(ring);
+  if (st) return st;
+  AppendArgs a;
+  st = append_common(shape, k_new, v_new, pos_host, batch, t_new, &a);
+  if (st) return st;
+  a.k = ring->k;
+  a.v = ring->v;
+  a.slot_pos = ring->slot_pos;
+  a.sink = ring->sink;
+  a.window = ring->window;
+  return launch_status(launch_ring_append(a, batch, static_cast<hipStream_t>(stream)));
+}
+
+int wmtp_paged_append(const wmtp_shape* shape, const wmtp_paged* kv, const void* k_new, const void* v_new,
+                      const int32_t* pos_host, int32_t batch, int32_t t_new, void* stream) {
+  int st = check_paged(kv, true);
+  if (st) return st;
+  AppendArgs a;
+  st = append_common(shape, k_new, v_new, pos_host, batch, t_new, &a);
+  if (st) return st;
+  for (int b = 0; b < batch; ++b)
+    if (((int64_t)pos_host[b] + t_new + WMTP_BLOCK_SIZE - 1) / WMTP_BLOCK_SIZE > kv->max_blocks_per_seq)
+      return WMTP_EINVAL;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.block_table = kv->block_table;
+  a.bt_stride = kv->max_blocks_per_seq;
+  a.max_block = kv->num_blocks - 1;
+  return launch_status(launch_paged_append(a, batch, static_cast<hipStream_t>(stream)));
+}
+
+int wmtp_debug_resolve_paged(const wmtp_paged* kv, int32_t num_kv_heads, int32_t head_dim, int32_t b, int32_t h,
+                             const int32_t* positions, int32_t n, int64_t* offsets_out, void* stream) {
+  if (!kv || !kv->block_table || kv->block_size != WMTP_BLOCK_SIZE || kv->num_blocks <= 0) return WMTP_EINVAL;
+  if (kv->max_blocks_per_seq <= 0 || num_kv_heads <= 0 || head_dim <= 0 || b < 0 || h < 0 || h >= num_kv_heads)
+    return WMTP_EINVAL;
+  if (n < 0 || (n > 0 && (!positions || !offsets_out))) return WMTP_EINVAL;
+  if (!aligned(offsets_out, 8)) return WMTP_EALIGN;
+  const int32_t* row = kv->block_table + (int64_t)b * kv->max_blocks_per_seq;
+  return launch_status(launch_debug_resolve_paged(row, kv->max_blocks_per_seq, kv->num_blocks - 1, num_kv_heads,
+                                                  head_dim, h, positions, n, offsets_out,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int wmtp_debug_resolve_ring(int32_t sink, int32_t window, const int32_t* positions, int32_t n, int32_t* slots_out,
+                            void* stream) {
+  if (sink < 0 || window < 1 || n < 0 || (n > 0 && (!positions || !slots_out))) return WMTP_EINVAL;
+  return launch_status(
+      launch_debug_resolve_ring(sink, window, positions, n, slots_out, static_cast<hipStream_t>(stream)));
+}
+
+int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t n, int32_t* out, void* stream) {
+  if (sink < 0 || window < 1 || n < 0 || !out) return WMTP_EINVAL;
+  if ((int64_t)sink + window > INT32_MAX / 2) return WMTP_EINVAL;
+  return launch_status(launch_debug_window_positions(sink, window, n, out, static_cast<hipStream_t>(stream)));
+}
+
+const char* wmtp_status_str(int status) {
+  switch (status) {
+    case WMTP_OK: return "ok";
+    case WMTP_EINVAL: return "invalid argument";
+    case WMTP_EUNSUPPORTED: return "unsupported shape or dtype";
+    case WMTP_EALIGN: return "pointer not aligned";
+    case WMTP_EWORKSPACE: return "workspace too small";
+    case WMTP_ELAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* wmtp_version(void) { return "wmtp 0.1 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// Device-side building blocks of the Windowed-MTP decode-attention kernels
+// (gfx950 / CDNA4, wave64): kernel argument blocks, the paged and ring index
+// resolvers, bf16 helpers and wave-level reductions.
+//
+// Index resolution follows the problem statement of "Windowed-MTP: Removing
+// the Full-Context Draft-KV Tax at Million-Token Context" (arxivlens.com
+// summary, Abstract): the native draft reads the whole paged cache, the
+// windowed draft reads sink + window entries kept in a compact ring buffer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wmtp.h"
+
+namespace wmtp {
+
+// ----------------------------------------------------------------------------- vector types
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = WMTP_BLOCK_SIZE;   // tokens per paged block
+
+// Read-only data that every lane of a wave reads at the same address (the
+// query rows) is read through the constant address space, which the compiler
+// turns into scalar loads into SGPRs.  Only for buffers no kernel writes.
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ const_u32_ptr as_const_u32(const void* p) {
+  return reinterpret_cast<const_u32_ptr>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ const_i32_ptr as_const_i32(const void* p) {
+  return reinterpret_cast<const_i32_ptr>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Load from a wave-uniform 64-bit base plus a 32-bit per-lane byte offset, the
+// form the global_load "saddr + voffset" addressing mode takes directly.
+template <typename T>
+__device__ __forceinline__ T load_at(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+
+// ----------------------------------------------------------------------------- kernel arguments
+// Passed by value (kernarg segment); per-sequence lengths and split offsets ride
+// along so that no host-to-device copy is needed before a launch.
+struct SplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;   // paged source
+  const int32_t* slot_pos;      // ring source
+  float* part_o;
+  float* part_lse;
+  int64_t max_block;            // num_blocks - 1: block ids are clamped to this
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t bt_stride;            // max_blocks_per_seq
+  int32_t slots;                // ring slots (sink + window)
+  int32_t sink;
+  int32_t window;
+  int32_t chunk;                // entries per split
+  int32_t batch;
+  int32_t t_q;                  // verify: query tokens per sequence
+  float scale_log2;             // scale * log2(e)
+  int32_t split_base[WMTP_MAX_BATCH + 1];
+  int32_t seq_len[WMTP_MAX_BATCH];
+};
+
+// ----------------------------------------------------------------------------- resolvers
+// Paged pool layout [block][kv_head][16][D]: the byte offset of the start of a
+// (block, head) run of 16 token rows.
+__device__ __forceinline__ int64_t paged_block_run(int64_t blk, int h, int num_kv_heads, int row_bytes) {
+  return (blk * num_kv_heads + h) * (int64_t)kBlock * row_bytes;
+}
+
+// Physical block of logical token t of a sequence (block-table row `bt_row`),
+// clamped to the pool so a corrupt table cannot send a load out of bounds.
+__device__ __forceinline__ int64_t clamp_block(int64_t blk, int64_t max_block) {
+  blk = blk < 0 ? 0 : blk;
+  return blk > max_block ? max_block : blk;
+}
+__device__ __forceinline__ int64_t paged_block_of(const int32_t* bt_row, int64_t t, int64_t max_block) {
+  return clamp_block(bt_row[t / kBlock], max_block);
+}
+// Same, for a wave-uniform token: the table entry comes in through a scalar load.
+__device__ __forceinline__ int64_t paged_block_uniform(const_i32_ptr bt_row, int64_t t, int64_t max_block) {
+  return clamp_block(bt_row[t / kBlock], max_block);
+}
+
+// Element offset of (token t, head h, d = 0) in the paged pool.
+__device__ __forceinline__ int64_t paged_elem_offset(const int32_t* bt_row, int64_t t, int h, int num_kv_heads,
+                                                     int head_dim, int64_t max_block) {
+  const int64_t blk = paged_block_of(bt_row, t, max_block);
+  return ((blk * num_kv_heads + h) * kBlock + (t % kBlock)) * (int64_t)head_dim;
+}
+
+// Compact ring: sinks keep slots 0..S-1, later positions cycle through S..S+W-1.
+__device__ __forceinline__ int32_t ring_slot(int32_t p, int32_t sink, int32_t window) {
+  return p < sink ? p : sink + (p - sink) % window;
+}
+
+// Is absolute position p in the sink + window visible set of a query at length n?
+__device__ __forceinline__ bool window_visible(int32_t p, int32_t n, int32_t sink, int32_t window) {
+  return p >= 0 && p < n && (p < sink || p >= n - window);
+}
+
+// Sequence owning global split `sg` (split_base is ascending; batch <= 64).
+__device__ __forceinline__ int seq_of_split(const SplitArgs& a, int sg) {
+  int b = 0;
+  while (b + 1 < a.batch && a.split_base[b + 1] <= sg) ++b;
+  return b;
+}
+
+// ----------------------------------------------------------------------------- numbers
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to bf16 (RNE) and return the rounded value as fp32.
+__device__ __forceinline__ float round_bf16(float x) {
+  const __bf16 b = (__bf16)x;
+  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Two fp32 values -> packed bf16x2 (RNE), `lo` in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ----------------------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+}  // namespace wmtp

@@ -1,0 +1,448 @@
+// Split-K flash-decoding for the MTP draft head on gfx950.
+//
+// The native MTP draft attends over the whole KV cache at every draft step, so
+// its read grows with context; Windowed-MTP attends over attention-sink tokens
+// plus a window of recent tokens held in a compact ring ("Windowed-MTP:
+// Removing the Full-Context Draft-KV Tax at Million-Token Context", arxivlens
+// summary, Abstract; readpriors.com post, What happened).  One kernel serves
+// both: the only difference is how a visible entry is located (block table vs
+// ring slot + tag check).
+//
+// Work item = (sequence b, KV head h, split of `chunk` visible entries); one
+// 256-thread workgroup (4 waves) per item.  The G query heads of the KV head
+// are packed, so each K/V byte is read from HBM once per group.
+//
+// Per 64-entry tile:
+//   1. K: every wave loads its quarter of the 64 rows (coalesced 16-byte loads,
+//      one tile ahead) and stores it into a wave-private LDS stage whose 16-byte
+//      pieces are XOR-swizzled so that "one lane per entry" reads are free of
+//      bank conflicts.
+//   2. QK: lane = entry; the wave's quarter of the G query rows comes from
+//      SGPRs (wave-uniform scalar loads), so bf16 pairs go straight into
+//      v_dot2_f32_bf16 with no unpacking and no cross-lane reduction.
+//   3. The 4 quarter-dot-products are summed through LDS (one barrier per tile).
+//   4. Online softmax in the log2 domain with a lazy maximum: the running max is
+//      only raised (and the accumulators rescaled) when a score exceeds it by
+//      more than 2^8, which is rare after the first tile; the result is the same
+//      up to rounding because numerator and denominator share the reference.
+//   5. PV: each wave owns a quarter of D; V rows are loaded into registers at
+//      the start of the tile; probabilities are handed from the entry lanes
+//      through LDS.
+// The split writes o = sum p v / sum p and lse = ln sum exp(s) for every packed
+// row; a separate LSE combine merges the splits.
+#include "wmtp_device.hpp"
+#include "wmtp_launch.hpp"
+
+namespace wmtp {
+
+template <int D, int G, bool BF16>
+struct DraftShape {
+  static constexpr int ES = BF16 ? 2 : 4;      // element bytes
+  static constexpr int ROWB = D * ES;          // bytes of one entry's row (one head)
+  static constexpr int QB = ROWB / 4;          // one wave's quarter of a row
+  static constexpr int NCH = QB / 16;          // 16-byte pieces per quarter row
+  static constexpr int EPP = 16 / ES;          // elements per piece
+  static constexpr int TILE = 64;
+  static constexpr int TPI = 64 / NCH;         // entries covered by one 1 KiB wave load
+  static constexpr int GP = (G + 3) / 4 * 4;   // G padded to whole float4 planes
+  static constexpr int KSTAGE = TILE * QB;     // bytes of one wave's K stage
+  // PV layout: each lane loads 8 bytes of a V row per load (EV elements);
+  // LPR lanes cover one quarter row, TPV entries per wave load, NV loads per tile.
+  static constexpr int VB = 8;
+  static constexpr int EV = VB / ES;
+  static constexpr int LPR = QB / VB;
+  static constexpr int TPV = 64 / LPR;
+  static constexpr int NV = TILE / TPV;
+  static_assert(NCH >= 2 && NCH <= 16, "quarter row must hold 2..16 pieces");
+  static_assert(GP * TILE * 4 <= KSTAGE, "probability tile must fit in a K stage");
+};
+
+// Physical 16-byte piece of logical piece c of tile entry t in a wave's K stage.
+// Entry t owns NCH consecutive pieces; 8 consecutive entries read by 8
+// consecutive lanes land in 8 different bank groups (one 128-byte bank sweep).
+template <int NCH>
+__device__ __forceinline__ int k_piece(int t, int c) {
+  if constexpr (NCH >= 8) {
+    return t * NCH + ((c & ~7) | ((c ^ t) & 7));
+  } else {
+    constexpr int per_sweep = 8 / NCH;            // entries sharing one 128-byte sweep
+    return t * NCH + (c ^ ((t / per_sweep) % NCH));
+  }
+}
+
+template <int D, int G, bool BF16, bool WINDOW, bool PV_DOT2>
+__global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a) {
+  using S = DraftShape<D, G, BF16>;
+  constexpr int NCH = S::NCH, TPI = S::TPI, GP = S::GP, QB = S::QB, ROWB = S::ROWB;
+  constexpr int EV = S::EV, LPR = S::LPR, TPV = S::TPV, NV = S::NV;
+  constexpr float TAU = 8.0f;   // lazy-max slack, log2 units
+  static_assert(!PV_DOT2 || BF16, "dot2 PV needs bf16 values");
+
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[4 * 2 * S::KSTAGE];
+  __shared__ __attribute__((aligned(16))) float sc_lds[2 * 4 * GP * S::TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Hkv = a.num_kv_heads;
+  const int h = blockIdx.x % Hkv;
+  const int sg = blockIdx.x / Hkv;
+  const int b = seq_of_split(a, sg);
+  const int n = a.seq_len[b];
+  const int nvis = WINDOW ? min(n, a.slots) : n;
+  const int t_begin = (sg - a.split_base[b]) * a.chunk;
+  const int t_end = min(t_begin + a.chunk, nvis);
+  const int ntiles = (t_end - t_begin + S::TILE - 1) / S::TILE;
+
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + wave * QB;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + wave * QB;
+  const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
+  const int64_t ring_seq = ((int64_t)b * Hkv + h) * a.slots * (int64_t)ROWB;
+  const int32_t* tags = a.slot_pos + (int64_t)b * a.slots;
+  const int last_blk_idx = (t_end - 1) >> 4;
+
+  // query rows of this KV head, this wave's quarter of D (wave-uniform -> SGPRs)
+  const int64_t qrow0 = (int64_t)b * a.num_q_heads + (int64_t)h * G;
+  const_u32_ptr q32 = as_const_u32(a.q) + qrow0 * (D * S::ES / 4) + wave * (QB / 4);
+
+  uint8_t* my_k = k_lds + wave * 2 * S::KSTAGE;
+  const int kl_tok = lane / NCH, kl_c = lane % NCH;   // K load lane roles: entry, piece
+  const int pv_tok = lane / LPR, pv_d = lane % LPR;   // PV lane roles: entry group, 8-byte slot
+
+  // ---- addressing.  A tile's entries live in up to 4 runs of 16 rows (paged) or
+  // one run of 64 rows (ring).  run[j] is the uniform byte offset of run j; a lane
+  // adds a 32-bit offset.  Entries past the split end are clamped to a valid row.
+  auto tile_runs = [&](int t0, int64_t (&run)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (WINDOW) {
+        run[j] = ring_seq + (int64_t)t0 * ROWB;
+      } else {
+        const int bi = min((t0 >> 4) + j, last_blk_idx);
+        run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, ROWB);
+      }
+    }
+  };
+  // byte offset of tile entry tt inside its run; `first` is the first entry of the
+  // wave load (compile-time after unrolling) and SPAN the entries it covers
+  auto lane_off = [&](int t0, int tt) -> uint32_t {
+    if constexpr (WINDOW) return (uint32_t)min(tt, a.slots - 1 - t0) * ROWB;
+    return (uint32_t)(tt & 15) * ROWB;
+  };
+  auto run_base = [&](const uint8_t* base, const int64_t (&run)[4], int first, int span, int tt) -> const uint8_t* {
+    if constexpr (WINDOW) return base + run[0];
+    if (span <= 16) return base + run[first >> 4];
+    const int j = tt >> 4;                      // entries of one load straddle blocks
+    int64_t r = run[0];
+    r = j == 1 ? run[1] : r;
+    r = j == 2 ? run[2] : r;
+    r = j == 3 ? run[3] : r;
+    return base + r;
+  };
+
+  u32x4 kreg[NCH];
+  uint2 vreg[NV];
+  int tag_cur = 0, tag_next = 0;
+
+  auto load_k = [&](int t0, const int64_t (&run)[4]) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int tt = i * TPI + kl_tok;
+      kreg[i] = load_at<u32x4>(run_base(kbase, run, i * TPI, TPI, tt), lane_off(t0, tt) + kl_c * 16);
+    }
+  };
+  // V: load k brings entry k*TPV + pv_tok (fp32 PV) or, for the paired bf16 PV,
+  // entry 2 (k/2 * TPV + pv_tok) + k%2, bytes [8 pv_d, 8 pv_d + 8) of the quarter.
+  auto load_v = [&](int t0, const int64_t (&run)[4], uint2 (&dst)[NV]) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if constexpr (PV_DOT2) {
+        const int first = 2 * (k >> 1) * TPV;
+        const int tt = first + 2 * pv_tok + (k & 1);
+        dst[k] = load_at<uint2>(run_base(vbase, run, first, 2 * TPV, tt), lane_off(t0, tt) + pv_d * 8);
+      } else {
+        const int tt = k * TPV + pv_tok;
+        dst[k] = load_at<uint2>(run_base(vbase, run, k * TPV, TPV, tt), lane_off(t0, tt) + pv_d * 8);
+      }
+    }
+  };
+  auto load_tag = [&](int t0) -> int {
+    if constexpr (WINDOW) return tags[min(t0 + lane, a.slots - 1)];
+    return 0;
+  };
+  auto store_k = [&](int stage) {
+    uint8_t* dst = my_k + stage * S::KSTAGE;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int tt = i * TPI + kl_tok;
+      *reinterpret_cast<u32x4*>(dst + k_piece<NCH>(tt, kl_c) * 16) = kreg[i];
+    }
+  };
+
+  float o[G][EV];
+  float l_lane[G], M[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    l_lane[g] = 0.f;
+    M[g] = kNegInf;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) o[g][e] = 0.f;
+  }
+
+  if (ntiles > 0) {
+    int64_t run[4];
+    tile_runs(t_begin, run);
+    load_k(t_begin, run);
+    tag_next = load_tag(t_begin);
+    store_k(0);
+  }
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = t_begin + it * S::TILE;
+    const int stage = it & 1;
+    const bool has_next = it + 1 < ntiles;
+    tag_cur = tag_next;
+    {
+      // V of this tile (consumed after QK and the softmax), then K of the next one
+      int64_t run[4];
+      tile_runs(t0, run);
+      load_v(t0, run, vreg);
+    }
+    if (has_next) {
+      int64_t run[4];
+      tile_runs(t0 + S::TILE, run);
+      load_k(t0 + S::TILE, run);
+      tag_next = load_tag(t0 + S::TILE);
+    }
+
+    // ---- QK: lane = entry, partial dot over this wave's quarter of D
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+    const uint8_t* kst = my_k + stage * S::KSTAGE;
+    // q is re-read from the scalar cache every tile: hoisting it out of the loop
+    // would need G * D / 8 registers for the wave's quarter.
+    const_u32_ptr qt = q32;
+    asm volatile("" : "+s"(qt));
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(kst + k_piece<NCH>(lane, c) * 16);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const_u32_ptr qg = qt + (int64_t)g * (D * S::ES / 4) + c * 4;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[g] = dot2_bf16(qg[e], kk[e], acc[g]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[g] = fmaf(__uint_as_float(qg[e]), __uint_as_float(kk[e]), acc[g]);
+        }
+      }
+    }
+
+    // ---- sum the 4 quarter products through LDS
+    float* sc = sc_lds + stage * (4 * GP * S::TILE);
+#pragma unroll
+    for (int pl = 0; pl < GP / 4; ++pl) {
+      f32x4 w4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w4[e] = (pl * 4 + e < G) ? acc[pl * 4 + e] : 0.f;
+      *reinterpret_cast<f32x4*>(sc + ((wave * (GP / 4) + pl) * S::TILE + lane) * 4) = w4;
+    }
+    __syncthreads();
+    float s2[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) s2[g] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+      for (int pl = 0; pl < GP / 4; ++pl) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(sc + ((w * (GP / 4) + pl) * S::TILE + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (pl * 4 + e < G) s2[pl * 4 + e] += w4[e];
+      }
+    }
+
+    // ---- online softmax (log2 domain, lazy maximum)
+    bool valid = t0 + lane < t_end;
+    if constexpr (WINDOW) valid = valid && window_visible(tag_cur, n, a.sink, a.window);
+    bool exceed = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      s2[g] = valid ? s2[g] * a.scale_log2 : kNegInf;
+      exceed = exceed || (s2[g] > M[g] + TAU);
+    }
+    if (__ballot(exceed) != 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mt = wave_max(s2[g]);
+        const float mn = fmaxf(M[g], mt);
+        const float alpha = (M[g] == kNegInf) ? 0.f : exp2f(M[g] - mn);
+        M[g] = mn;
+        l_lane[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) o[g][e] *= alpha;
+      }
+    }
+    float p[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      p[g] = valid ? exp2f(s2[g] - M[g]) : 0.f;
+      if constexpr (PV_DOT2) p[g] = round_bf16(p[g]);   // PV consumes bf16 p: keep l consistent
+      l_lane[g] += p[g];
+    }
+
+    // ---- hand p to the PV lanes through the (now free) K stage
+    float* pl_lds = reinterpret_cast<float*>(my_k + stage * S::KSTAGE);
+#pragma unroll
+    for (int pl = 0; pl < GP / 4; ++pl) {
+      f32x4 w4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w4[e] = (pl * 4 + e < G) ? p[pl * 4 + e] : 0.f;
+      *reinterpret_cast<f32x4*>(pl_lds + (pl * S::TILE + lane) * 4) = w4;
+    }
+
+    // ---- PV over this wave's quarter of D
+    if constexpr (PV_DOT2) {
+#pragma unroll
+      for (int k = 0; k < NV / 2; ++k) {
+        const int ta = 2 * (k * TPV + pv_tok);
+        float pa[GP], pb[GP];
+#pragma unroll
+        for (int pl = 0; pl < GP / 4; ++pl) {
+          const f32x4 xa = *reinterpret_cast<const f32x4*>(pl_lds + (pl * S::TILE + ta) * 4);
+          const f32x4 xb = *reinterpret_cast<const f32x4*>(pl_lds + (pl * S::TILE + ta + 1) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { pa[pl * 4 + e] = xa[e]; pb[pl * 4 + e] = xb[e]; }
+        }
+        const uint2 va = vreg[2 * k], vb = vreg[2 * k + 1];
+        uint32_t vp[4];
+        vp[0] = __builtin_amdgcn_perm(vb.x, va.x, 0x05040100u);
+        vp[1] = __builtin_amdgcn_perm(vb.x, va.x, 0x07060302u);
+        vp[2] = __builtin_amdgcn_perm(vb.y, va.y, 0x05040100u);
+        vp[3] = __builtin_amdgcn_perm(vb.y, va.y, 0x07060302u);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint32_t pp = pack_bf16x2(pa[g], pb[g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[g][e] = dot2_bf16(pp, vp[e], o[g][e]);
+        }
+        if ((k & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the hoisting of p reads
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int tt = k * TPV + pv_tok;
+        float pp[GP];
+#pragma unroll
+        for (int pl = 0; pl < GP / 4; ++pl) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(pl_lds + (pl * S::TILE + tt) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pp[pl * 4 + e] = x[e];
+        }
+        float vf[EV];
+        if constexpr (BF16) {
+          vf[0] = bf16lo(vreg[k].x);
+          vf[1] = bf16hi(vreg[k].x);
+          vf[2] = bf16lo(vreg[k].y);
+          vf[3] = bf16hi(vreg[k].y);
+        } else {
+          vf[0] = __uint_as_float(vreg[k].x);
+          vf[1] = __uint_as_float(vreg[k].y);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < EV; ++e) o[g][e] = fmaf(pp[g], vf[e], o[g][e]);
+        if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the hoisting of p reads
+      }
+    }
+
+    if (has_next) store_k(stage ^ 1);
+  }
+
+  // ---- reduce over the lanes that share a D slot, normalise, write the partial
+  float l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) l[g] = wave_sum(l_lane[g]);
+#pragma unroll
+  for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < EV; ++e) o[g][e] += __shfl_xor(o[g][e], m);
+
+  const int rows = a.num_q_heads;
+  float* po = a.part_o + ((int64_t)sg * rows + (int64_t)h * G) * D + wave * (D / 4) + pv_d * EV;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (g % TPV == pv_tok) {
+      const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
+      float* dst = po + (int64_t)g * D;
+      if constexpr (EV == 4) {
+        const f32x4 w4 = {o[g][0] * inv, o[g][1] * inv, o[g][2] * inv, o[g][3] * inv};
+        *reinterpret_cast<f32x4*>(dst) = w4;
+      } else {
+        const float2 w2 = {o[g][0] * inv, o[g][1] * inv};
+        *reinterpret_cast<float2*>(dst) = w2;
+      }
+    }
+  }
+  if (wave == 0 && lane < G) {
+    float lv = 0.f, mv = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (g == lane) { lv = l[g]; mv = M[g]; }
+    a.part_lse[(int64_t)sg * rows + (int64_t)h * G + lane] = lv > 0.f ? (mv + __log2f(lv)) * kLn2 : kNegInf;
+  }
+}
+
+// ----------------------------------------------------------------------------- dispatch
+template <int D, int G, bool BF16>
+static hipError_t launch_dg(bool window, bool dot2, const SplitArgs& a, int grid, hipStream_t st) {
+  if (window) {
+    if constexpr (BF16) {
+      if (dot2) { draft_splitk_kernel<D, G, BF16, true, true><<<grid, 256, 0, st>>>(a); return hipGetLastError(); }
+    }
+    draft_splitk_kernel<D, G, BF16, true, false><<<grid, 256, 0, st>>>(a);
+  } else {
+    if constexpr (BF16) {
+      if (dot2) { draft_splitk_kernel<D, G, BF16, false, true><<<grid, 256, 0, st>>>(a); return hipGetLastError(); }
+    }
+    draft_splitk_kernel<D, G, BF16, false, false><<<grid, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+static hipError_t launch_d(int G, bool window, bool dot2, const SplitArgs& a, int grid, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_dg<D, 1, BF16>(window, dot2, a, grid, st);
+    case 2: return launch_dg<D, 2, BF16>(window, dot2, a, grid, st);
+    case 4: return launch_dg<D, 4, BF16>(window, dot2, a, grid, st);
+    case 8: return launch_dg<D, 8, BF16>(window, dot2, a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_draft(int dtype, int head_dim, int group, bool window, bool pv_dot2, const SplitArgs& a,
+                        int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  const bool bf16 = dtype == WMTP_BF16;
+  if (bf16) {
+    switch (head_dim) {
+      case 64: return launch_d<64, true>(group, window, pv_dot2, a, grid, st);
+      case 128: return launch_d<128, true>(group, window, pv_dot2, a, grid, st);
+      case 256: return launch_d<256, true>(group, window, pv_dot2, a, grid, st);
+    }
+  } else {
+    switch (head_dim) {
+      case 64: return launch_d<64, false>(group, window, false, a, grid, st);
+      case 128: return launch_d<128, false>(group, window, false, a, grid, st);
+      case 256: return launch_d<256, false>(group, window, false, a, grid, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace wmtp

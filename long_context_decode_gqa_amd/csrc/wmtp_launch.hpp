@@ -1,0 +1,54 @@
+// Host-side launchers of the Windowed-MTP kernels (internal to libwmtp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wmtp.h"
+#include "wmtp_device.hpp"
+
+namespace wmtp {
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  void* out;
+  float* lse_out;
+  int32_t rows;          // rows per sequence
+  int32_t head_dim;
+  int32_t batch;
+  int32_t out_bf16;
+  int32_t split_base[WMTP_MAX_BATCH + 1];
+};
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k;
+  void* v;
+  const int32_t* block_table;   // paged
+  int32_t* slot_pos;            // ring
+  int64_t max_block;
+  int32_t num_kv_heads;
+  int32_t row_bytes;            // head_dim * element bytes
+  int32_t t_new;
+  int32_t bt_stride;
+  int32_t sink;
+  int32_t window;
+  int32_t pos[WMTP_MAX_BATCH];
+};
+
+hipError_t launch_draft(int dtype, int head_dim, int group, bool window, bool pv_dot2, const SplitArgs& a,
+                        int grid, hipStream_t st);
+hipError_t launch_verify(int head_dim, int group, const SplitArgs& a, int grid, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+hipError_t launch_ring_append(const AppendArgs& a, int batch, hipStream_t st);
+hipError_t launch_paged_append(const AppendArgs& a, int batch, hipStream_t st);
+hipError_t launch_debug_resolve_paged(const int32_t* bt_row, int32_t row_len, int64_t max_block, int num_kv_heads,
+                                      int head_dim, int h, const int32_t* positions, int n, int64_t* out,
+                                      hipStream_t st);
+hipError_t launch_debug_resolve_ring(int sink, int window, const int32_t* positions, int n, int32_t* out,
+                                     hipStream_t st);
+hipError_t launch_debug_window_positions(int sink, int window, int n, int32_t* out, hipStream_t st);
+
+}  // namespace wmtp

@@ -1,0 +1,211 @@
+// LSE combine, ring / paged append and index-resolution kernels for gfx950.
+#include "wmtp_device.hpp"
+#include "wmtp_launch.hpp"
+
+namespace wmtp {
+
+// ----------------------------------------------------------------------------- combine
+// Flash-decoding merge of split partials.  A split holding the keys K_i gives
+// (o_i, lse_i); the result over the union is
+//   L = log sum_i exp(lse_i),  o = sum_i exp(lse_i - L) o_i.
+// Workgroup = (sequence b, row r, 16-float slice of D).  Its 256 threads are 4
+// lanes across the slice (16 bytes each) x 64 split lanes; every thread keeps a
+// running (max, weight, acc) over its splits, and the 64 split lanes are merged
+// through LDS at the end.
+constexpr int kCombineDL = 4;                     // lanes across a D slice
+constexpr int kCombineSL = 256 / kCombineDL;      // split lanes
+
+__global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
+  __shared__ float sm[kCombineSL][kCombineDL][6];
+  const int slices = a.head_dim / (4 * kCombineDL);
+  const int slice = blockIdx.x % slices;
+  const int br = blockIdx.x / slices;             // b * rows + r
+  const int b = br / a.rows;
+  const int r = br % a.rows;
+  const int dl = threadIdx.x % kCombineDL;
+  const int sl = threadIdx.x / kCombineDL;
+  const int s0 = a.split_base[b], s1 = a.split_base[b + 1];
+  const int d0 = slice * 4 * kCombineDL + dl * 4;
+
+  float m = kNegInf, w = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = s0 + sl; s < s1; s += kCombineSL) {
+    const float ls = a.part_lse[(int64_t)s * a.rows + r] * kLog2e;
+    if (ls == kNegInf) continue;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)s * a.rows + r) * a.head_dim + d0);
+    if (ls > m) {
+      const float c = exp2f(m - ls);          // m = -inf gives 0
+      acc *= c;
+      w *= c;
+      m = ls;
+    }
+    const float e = exp2f(ls - m);
+    acc += e * x;
+    w += e;
+  }
+  sm[sl][dl][0] = m;
+  sm[sl][dl][1] = w;
+  sm[sl][dl][2] = acc[0];
+  sm[sl][dl][3] = acc[1];
+  sm[sl][dl][4] = acc[2];
+  sm[sl][dl][5] = acc[3];
+  __syncthreads();
+  if (sl != 0) return;
+  float M = kNegInf;
+  for (int i = 0; i < kCombineSL; ++i) M = fmaxf(M, sm[i][dl][0]);
+  float W = 0.f;
+  f32x4 A = {0.f, 0.f, 0.f, 0.f};
+  if (M != kNegInf) {
+    for (int i = 0; i < kCombineSL; ++i) {
+      const float mi = sm[i][dl][0];
+      if (mi == kNegInf) continue;
+      const float c = exp2f(mi - M);
+      W += c * sm[i][dl][1];
+      A[0] += c * sm[i][dl][2];
+      A[1] += c * sm[i][dl][3];
+      A[2] += c * sm[i][dl][4];
+      A[3] += c * sm[i][dl][5];
+    }
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  const int64_t orow = ((int64_t)b * a.rows + r) * a.head_dim + d0;
+  if (a.out_bf16) {
+    uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<__bf16*>(a.out) + orow);
+    o[0] = pack_bf16x2(A[0] * inv, A[1] * inv);
+    o[1] = pack_bf16x2(A[2] * inv, A[3] * inv);
+  } else {
+    f32x4 res = A * inv;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow) = res;
+  }
+  if (a.lse_out && slice == 0 && dl == 0)
+    a.lse_out[(int64_t)b * a.rows + r] = W > 0.f ? (M + __log2f(W)) * kLn2 : kNegInf;
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+  const int slices = a.head_dim / (4 * kCombineDL);
+  const int grid = a.batch * a.rows * slices;
+  if (grid <= 0) return hipSuccess;
+  combine_kernel<<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- appends
+// One workgroup per (sequence, new token); threads copy 16-byte pieces of the
+// token's H_kv rows of K and V.
+__global__ __launch_bounds__(256) void ring_append_kernel(const AppendArgs a) {
+  const int b = blockIdx.x / a.t_new;
+  const int i = blockIdx.x % a.t_new;
+  const int p = a.pos[b] + i;
+  const int last = a.pos[b] + a.t_new - 1;
+  if (!(p < a.sink || p > last - a.window)) return;       // overwritten later in this append
+  const int slots = a.sink + a.window;
+  const int slot = ring_slot(p, a.sink, a.window);
+  const int pieces = a.row_bytes / 16;                     // per head
+  const int64_t src_tok = ((int64_t)b * a.t_new + i) * a.num_kv_heads * a.row_bytes;
+  for (int j = threadIdx.x; j < 2 * a.num_kv_heads * pieces; j += blockDim.x) {
+    const int which = j / (a.num_kv_heads * pieces);       // 0 = K, 1 = V
+    const int hp = j % (a.num_kv_heads * pieces);
+    const int h = hp / pieces, pc = hp % pieces;
+    const uint8_t* src = static_cast<const uint8_t*>(which ? a.v_new : a.k_new) + src_tok +
+                         (int64_t)h * a.row_bytes + pc * 16;
+    uint8_t* dst = static_cast<uint8_t*>(which ? a.v : a.k) +
+                   (((int64_t)b * a.num_kv_heads + h) * slots + slot) * a.row_bytes + pc * 16;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  }
+  if (threadIdx.x == 0) a.slot_pos[(int64_t)b * slots + slot] = p;
+}
+
+__global__ __launch_bounds__(256) void paged_append_kernel(const AppendArgs a) {
+  const int b = blockIdx.x / a.t_new;
+  const int i = blockIdx.x % a.t_new;
+  const int64_t p = (int64_t)a.pos[b] + i;
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.bt_stride;
+  const int64_t blk = paged_block_of(bt_row, p, a.max_block);
+  const int pieces = a.row_bytes / 16;
+  const int64_t src_tok = ((int64_t)b * a.t_new + i) * a.num_kv_heads * a.row_bytes;
+  for (int j = threadIdx.x; j < 2 * a.num_kv_heads * pieces; j += blockDim.x) {
+    const int which = j / (a.num_kv_heads * pieces);
+    const int hp = j % (a.num_kv_heads * pieces);
+    const int h = hp / pieces, pc = hp % pieces;
+    const uint8_t* src = static_cast<const uint8_t*>(which ? a.v_new : a.k_new) + src_tok +
+                         (int64_t)h * a.row_bytes + pc * 16;
+    uint8_t* dst = static_cast<uint8_t*>(which ? a.v : a.k) + paged_block_run(blk, h, a.num_kv_heads, a.row_bytes) +
+                   (p % kBlock) * a.row_bytes + pc * 16;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
+hipError_t launch_ring_append(const AppendArgs& a, int batch, hipStream_t st) {
+  const int grid = batch * a.t_new;
+  if (grid <= 0) return hipSuccess;
+  ring_append_kernel<<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_append(const AppendArgs& a, int batch, hipStream_t st) {
+  const int grid = batch * a.t_new;
+  if (grid <= 0) return hipSuccess;
+  paged_append_kernel<<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- index-resolution hooks
+__global__ void debug_resolve_paged_kernel(const int32_t* bt_row, int32_t row_len, int64_t max_block,
+                                           int num_kv_heads, int head_dim, int h, const int32_t* positions, int n,
+                                           int64_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t p = positions[i];
+  out[i] = (p < 0 || p / kBlock >= row_len) ? -1
+                                             : paged_elem_offset(bt_row, p, h, num_kv_heads, head_dim, max_block);
+}
+
+__global__ void debug_resolve_ring_kernel(int sink, int window, const int32_t* positions, int n, int32_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = ring_slot(positions[i], sink, window);
+}
+
+// Slot -> visible position for a query at length n: slot s < S holds sink s;
+// ring slot s holds the most recent p < n with slot(p) = s, if it is visible.
+__global__ void debug_window_positions_kernel(int sink, int window, int n, int32_t* out) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= sink + window) return;
+  int32_t p;
+  if (s < sink) {
+    p = s < n ? s : -1;
+  } else if (n <= sink) {
+    p = -1;
+  } else {
+    const int32_t last = n - 1;                          // newest position, last >= sink
+    const int32_t r = (last - sink) % window;            // its ring index
+    const int32_t d = ((r - (s - sink)) % window + window) % window;
+    p = last - d;                                        // newest position mapped to slot s
+    if (p < sink || !window_visible(p, n, sink, window)) p = -1;
+  }
+  out[s] = p;
+}
+
+hipError_t launch_debug_resolve_paged(const int32_t* bt_row, int32_t row_len, int64_t max_block, int num_kv_heads,
+                                      int head_dim, int h, const int32_t* positions, int n, int64_t* out,
+                                      hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  debug_resolve_paged_kernel<<<(n + 255) / 256, 256, 0, st>>>(bt_row, row_len, max_block, num_kv_heads, head_dim, h,
+                                                             positions, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_resolve_ring(int sink, int window, const int32_t* positions, int n, int32_t* out,
+                                     hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  debug_resolve_ring_kernel<<<(n + 255) / 256, 256, 0, st>>>(sink, window, positions, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_window_positions(int sink, int window, int n, int32_t* out, hipStream_t st) {
+  const int slots = sink + window;
+  if (slots <= 0) return hipSuccess;
+  debug_window_positions_kernel<<<(slots + 255) / 256, 256, 0, st>>>(sink, window, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace wmtp

@@ -1,0 +1,287 @@
+// Full-context verify attention of the target on gfx950 matrix cores.
+//
+// The target keeps full attention while it verifies the gamma+1 drafted
+// positions ("Windowed-MTP: Removing the Full-Context Draft-KV Tax at
+// Million-Token Context", arxivlens summary, Abstract; howtospark case study,
+// Method: one batched verify per cycle).  Per KV head the t_q query tokens x G
+// query heads form up to 32 packed rows, so QK^T and PV are real dense
+// contractions (32 rows x head_dim against each key tile) and run on
+// v_mfma_f32_32x32x16_bf16.
+//
+// Work item = (sequence, KV head, split of `chunk` keys); one 256-thread
+// workgroup whose 4 waves each own a quarter of head_dim.  Per 32-key tile:
+//   S^T = K Q^T     each wave contracts its quarter of D: A = its quarter of
+//                   the K rows from a swizzled wave-private LDS stage (lane =
+//                   key), B = its quarter of Q^T held in registers.  The 4
+//                   partial score tiles are summed through LDS (one barrier per
+//                   tile), so every wave holds the full scores: lane l has
+//                   packed row l % 32 for 16 keys.
+//   softmax         row max over 16 registers + the partner half-wave; causal
+//                   mask for query token i: key <= n - t_q + i; lazy running
+//                   maximum (rescale only on a 2^8 jump).  Identical in all
+//                   waves, so the waves share one softmax state.
+//   O += P V        A = P straight from the score accumulator (bf16); B = V of
+//                   the wave's quarter of D, 2 values per lane and key,
+//                   regrouped into key pairs with v_perm_b32.
+// The split writes o and lse for every packed row; the LSE combine merges
+// splits.
+#include "wmtp_device.hpp"
+#include "wmtp_launch.hpp"
+
+namespace wmtp {
+
+namespace {
+
+constexpr int kVD = 256;                 // head_dim served by the MFMA verify
+constexpr int kVTile = 32;               // keys per tile
+constexpr int kVQ = kVD / 4;             // d per wave (64)
+constexpr int kVNQ = kVQ * 2 / 16;       // 16-byte pieces per quarter row (8)
+constexpr int kVKS = kVQ / 16;           // k-steps per quarter (4)
+constexpr int kVStage = kVTile * kVQ * 2;   // bytes of one wave's K stage (4 KiB)
+constexpr int kVLoads = kVStage / 1024;  // 16-byte loads per lane per K tile (4)
+
+// Swizzled piece (16 bytes) of logical piece p of key row i (8 pieces per row):
+// 8 consecutive keys read by 8 consecutive lanes hit 8 different bank groups.
+__device__ __forceinline__ int vpiece(int i, int p) { return i * kVNQ + ((p ^ i) & 7); }
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+}  // namespace
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
+  constexpr int ROWB = kVD * 2;
+  constexpr float TAU = 8.0f;
+
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[4 * 2 * kVStage];
+  __shared__ __attribute__((aligned(16))) float sc_lds[2 * 4 * 16 * 64];   // [buf][wave][r/4][lane][4]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, tq = a.t_q;
+  const int rows = tq * G;
+  const int h = blockIdx.x % Hkv;
+  const int sg = blockIdx.x / Hkv;
+  const int b = seq_of_split(a, sg);
+  const int n = a.seq_len[b];
+  const int t_begin = (sg - a.split_base[b]) * a.chunk;
+  const int t_end = min(t_begin + a.chunk, n);
+  const int ntiles = (t_end - t_begin + kVTile - 1) / kVTile;
+  const int last_blk_idx = (t_end - 1) >> 4;
+  const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + wave * (kVQ * 2);
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + wave * (kVQ * 2);
+
+  const int c32 = lane & 31;     // key (A rows) / packed query row (B, C columns)
+  const int kh = lane >> 5;      // which 8-element half of a k-step
+
+  // ---- this wave's quarter of Q^T: lane (row c32, half kh), k-step s -> piece 2s + kh
+  u32x4 qreg[kVKS];
+  {
+    const int j = c32;
+    const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
+    const int i = j / G, g = j % G;
+    const int64_t qrow = ((int64_t)b * tq + i) * Hq + (int64_t)h * G + g;
+#pragma unroll
+    for (int s = 0; s < kVKS; ++s) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (j < rows) x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + wave * (kVQ * 2) + (2 * s + kh) * 16);
+      qreg[s] = x;
+    }
+  }
+
+  uint8_t* my_k = k_lds + wave * 2 * kVStage;
+
+  // byte offsets of the two (block, head) runs of 16 keys covering a tile
+  auto tile_runs = [&](int t0, int64_t (&run)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int bi = min((t0 >> 4) + j, last_blk_idx);
+      run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, ROWB);
+    }
+  };
+
+  u32x4 kreg[kVLoads];
+  uint32_t vreg[2][8], vnext[2][8];
+
+  // K quarter tile: load l of a lane covers stage piece P = 64 l + lane, i.e. key
+  // P / 8, piece P % 8; its 8 keys share one 16-key block (uniform base).
+  auto load_k = [&](const int64_t (&run)[2]) {
+#pragma unroll
+    for (int l = 0; l < kVLoads; ++l) {
+      const int P = 64 * l + lane;
+      const int i = P / kVNQ, pp = P % kVNQ;
+      kreg[l] = load_at<u32x4>(kbase + run[(64 * l / kVNQ) >> 4], (uint32_t)((i & 15) * ROWB + pp * 16));
+    }
+  };
+  auto store_k = [&](int stage) {
+    uint8_t* dst = my_k + stage * kVStage;
+#pragma unroll
+    for (int l = 0; l < kVLoads; ++l) {
+      const int P = 64 * l + lane;
+      *reinterpret_cast<u32x4*>(dst + vpiece(P / kVNQ, P % kVNQ) * 16) = kreg[l];
+    }
+  };
+  // V: element jj (0..7) of k-step ks for this lane's half is key 16ks + 8(jj/4) + 4kh + jj%4;
+  // the lane holds d = 2 c32, 2 c32 + 1 of the wave's quarter (one dword).
+  auto load_v = [&](const int64_t (&run)[2], uint32_t (&dst)[2][8]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int tt = 8 * (jj >> 2) + 4 * kh + (jj & 3);   // key within block ks
+        dst[ks][jj] = load_at<uint32_t>(vbase + run[ks], (uint32_t)(tt * ROWB + c32 * 4));
+      }
+  };
+
+  f32x16 O[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[e][r] = 0.f;
+  float M = kNegInf, l_lane = 0.f;
+  const int row_limit = n - tq + c32 / G;     // last key packed row c32 may see
+  const bool row_live = c32 < rows;
+
+  if (ntiles > 0) {
+    int64_t run[2];
+    tile_runs(t_begin, run);
+    load_k(run);
+    load_v(run, vreg);
+    store_k(0);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = t_begin + it * kVTile;
+    const int stage = it & 1;
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) {
+      int64_t run[2];
+      tile_runs(t0 + kVTile, run);
+      load_k(run);
+      load_v(run, vnext);
+    }
+
+    // ---- partial S^T[key][row] over this wave's quarter of D
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    const uint8_t* kst = my_k + stage * kVStage;
+#pragma unroll
+    for (int s = 0; s < kVKS; ++s) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + vpiece(c32, 2 * s + kh) * 16);
+      sacc = mfma32(ka, qreg[s], sacc);
+    }
+    float* sc = sc_lds + stage * (4 * 16 * 64);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 w4 = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+      *reinterpret_cast<f32x4*>(sc + ((wave * 4 + q) * 64 + lane) * 4) = w4;
+    }
+    __syncthreads();
+    float s2[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s2[r] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sc + ((w * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s2[4 * q + e] += x[e];
+      }
+
+    // ---- scale, mask, lazy row maximum
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = t0 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      const bool ok = row_live && key < t_end && key <= row_limit;
+      s2[r] = ok ? s2[r] * a.scale_log2 : kNegInf;
+      mx = fmaxf(mx, s2[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__ballot(mx > M + TAU) != 0) {
+      const float mn = fmaxf(M, mx);
+      const float alpha = (M == kNegInf) ? 0.f : exp2f(M - mn);
+      M = mn;
+      l_lane *= alpha;
+      // register r of O holds row 8(r/4) + 4kh + r%4, whose factor sits in that lane
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ar = __shfl(alpha, 8 * (r >> 2) + 4 * kh + (r & 3));
+        O[0][r] *= ar;
+        O[1][r] *= ar;
+      }
+    }
+    uint32_t pk[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float p0 = s2[2 * q] == kNegInf ? 0.f : exp2f(s2[2 * q] - M);
+      const float p1 = s2[2 * q + 1] == kNegInf ? 0.f : exp2f(s2[2 * q + 1] - M);
+      pk[q] = pack_bf16x2(p0, p1);
+      l_lane += bf16lo(pk[q]) + bf16hi(pk[q]);
+    }
+
+    // ---- O += P V over this wave's quarter of D (2 output tiles, 2 k-steps of 16 keys)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 pa = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        u32x4 vb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          vb[q] = __builtin_amdgcn_perm(vreg[ks][2 * q + 1], vreg[ks][2 * q], e ? 0x07060302u : 0x05040100u);
+        O[e] = mfma32(pa, vb, O[e]);
+      }
+    }
+
+    if (has_next) {
+      store_k(stage ^ 1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) vreg[ks][jj] = vnext[ks][jj];
+    }
+  }
+
+  // ---- normalise and write this wave's quarter of every live row
+  const float l_row = l_lane + __shfl_xor(l_lane, 32);       // lanes c32 and c32 + 32 share a row
+  const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+    const float inv = __shfl(inv_row, row);
+    if (row < rows) {
+      const int i = row / G, g = row % G;
+      const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
+      float2 w2;
+      w2.x = O[0][r] * inv;
+      w2.y = O[1][r] * inv;
+      *reinterpret_cast<float2*>(a.part_o + orow * kVD + wave * kVQ + 2 * c32) = w2;
+    }
+  }
+  if (wave == 0 && lane < rows) {
+    const int i = lane / G, g = lane % G;
+    const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
+    a.part_lse[orow] = l_row > 0.f ? (M + __log2f(l_row)) * kLn2 : kNegInf;
+  }
+}
+
+hipError_t launch_verify(int head_dim, int group, const SplitArgs& a, int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim != kVD) return hipErrorInvalidValue;
+  switch (group) {
+    case 1: verify_kernel<1><<<grid, 256, 0, st>>>(a); break;
+    case 2: verify_kernel<2><<<grid, 256, 0, st>>>(a); break;
+    case 4: verify_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    case 8: verify_kernel<8><<<grid, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace wmtp

@@ -1,0 +1,236 @@
+"""Python binding of libwmtp (Windowed-MTP decode attention for gfx950).
+
+Argument marshalling only: every function turns torch tensors (device memory)
+and the current HIP stream into the raw pointers and sizes of the C ABI in
+include/wmtp.h, calls it, and raises on a non-zero status.  No attention
+arithmetic happens here.  If the built library is missing, loading fails
+loudly; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libwmtp.so")
+
+# ---------------------------------------------------------------- constants (wmtp.h)
+OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+FULL, SINK_WINDOW = 0, 1
+DRAFT_FAST_PV = 0x10
+MAX_BATCH = 64
+BLOCK_SIZE = 16
+MAX_VERIFY_ROWS = 32
+
+
+class WmtpError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {status} ({msg})")
+        self.status = status
+
+
+# ---------------------------------------------------------------- C structs
+class Shape(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class Paged(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64)]
+
+
+class Ring(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slot_pos", ctypes.c_void_p),
+                ("sink", ctypes.c_int32), ("window", ctypes.c_int32)]
+
+
+class Partials(ctypes.Structure):
+    _fields_ = [("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("rows_per_seq", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("total_splits", ctypes.c_int32), ("split_base", ctypes.c_int32 * (MAX_BATCH + 1))]
+
+
+EXPORTS = (
+    "wmtp_draft_workspace_bytes", "wmtp_verify_workspace_bytes", "wmtp_draft_attn", "wmtp_verify_attn",
+    "wmtp_combine", "wmtp_ring_append", "wmtp_paged_append", "wmtp_debug_resolve_paged",
+    "wmtp_debug_resolve_ring", "wmtp_debug_window_positions", "wmtp_status_str", "wmtp_version",
+)
+
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libwmtp.so (built in-tree by long_context_decode_gqa_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libwmtp.so not found at {p}; run `python -m long_context_decode_gqa_amd.build` first")
+    lib = ctypes.CDLL(p)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sp, pp, rp, tp = ctypes.POINTER(Shape), ctypes.POINTER(Paged), ctypes.POINTER(Ring), ctypes.POINTER(Partials)
+    lib.wmtp_draft_workspace_bytes.argtypes = [I32, sp, P, I32, I32, I32, I32]
+    lib.wmtp_draft_workspace_bytes.restype = I64
+    lib.wmtp_verify_workspace_bytes.argtypes = [sp, I32, P, I32, I32]
+    lib.wmtp_verify_workspace_bytes.restype = I64
+    lib.wmtp_draft_attn.argtypes = [I32, sp, P, pp, rp, P, I32, I32, P, SZ, tp, P]
+    lib.wmtp_draft_attn.restype = ctypes.c_int
+    lib.wmtp_verify_attn.argtypes = [sp, P, I32, pp, P, I32, I32, P, SZ, tp, P]
+    lib.wmtp_verify_attn.restype = ctypes.c_int
+    lib.wmtp_combine.argtypes = [tp, P, I32, P, P]
+    lib.wmtp_combine.restype = ctypes.c_int
+    lib.wmtp_ring_append.argtypes = [sp, rp, P, P, P, I32, I32, P]
+    lib.wmtp_ring_append.restype = ctypes.c_int
+    lib.wmtp_paged_append.argtypes = [sp, pp, P, P, P, I32, I32, P]
+    lib.wmtp_paged_append.restype = ctypes.c_int
+    lib.wmtp_debug_resolve_paged.argtypes = [pp, I32, I32, I32, I32, P, I32, P, P]
+    lib.wmtp_debug_resolve_paged.restype = ctypes.c_int
+    lib.wmtp_debug_resolve_ring.argtypes = [I32, I32, P, I32, P, P]
+    lib.wmtp_debug_resolve_ring.restype = ctypes.c_int
+    lib.wmtp_debug_window_positions.argtypes = [I32, I32, I32, P, P]
+    lib.wmtp_debug_window_positions.restype = ctypes.c_int
+    lib.wmtp_status_str.argtypes = [ctypes.c_int]
+    lib.wmtp_status_str.restype = ctypes.c_char_p
+    lib.wmtp_version.argtypes = []
+    lib.wmtp_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, st: int) -> int:
+    if st < 0:
+        raise WmtpError(fn, st, load().wmtp_status_str(int(st)).decode())
+    return st
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _lens(xs: Sequence[int]):
+    arr = (ctypes.c_int32 * max(1, len(xs)))(*[int(x) for x in xs])
+    return arr
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    return {torch.float32: F32, torch.bfloat16: BF16}[dt]
+
+
+def make_shape(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+               scale: Optional[float] = None) -> Shape:
+    return Shape(num_q_heads, num_kv_heads, head_dim, head_dim ** -0.5 if scale is None else scale, dtype_code(dtype))
+
+
+def make_paged(k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor) -> Paged:
+    """k, v: [num_blocks][H_kv][16][D]; block_table: int32 [batch][max_blocks] (device)."""
+    assert block_table.dtype == torch.int32 and block_table.dim() == 2
+    return Paged(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), BLOCK_SIZE, block_table.shape[1], k.shape[0])
+
+
+def make_ring(k: torch.Tensor, v: torch.Tensor, slot_pos: torch.Tensor, sink: int, window: int) -> Ring:
+    """k, v: [batch][H_kv][sink+window][D]; slot_pos: int32 [batch][sink+window] (device)."""
+    assert slot_pos.dtype == torch.int32
+    return Ring(k.data_ptr(), v.data_ptr(), slot_pos.data_ptr(), int(sink), int(window))
+
+
+# ---------------------------------------------------------------- planning
+def draft_workspace_bytes(mode: int, shape: Shape, seq_lens: Sequence[int], chunk_tokens: int = 0,
+                          sink: int = 0, window: int = 1) -> int:
+    return _check("wmtp_draft_workspace_bytes", load().wmtp_draft_workspace_bytes(
+        mode, ctypes.byref(shape), ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), chunk_tokens,
+        sink, window))
+
+
+def verify_workspace_bytes(shape: Shape, t_q: int, seq_lens: Sequence[int], split_tokens: int = 0) -> int:
+    return _check("wmtp_verify_workspace_bytes", load().wmtp_verify_workspace_bytes(
+        ctypes.byref(shape), t_q, ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), split_tokens))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte aligned uint8 buffer of at least nbytes (torch's allocator aligns to 512)."""
+    return torch.empty(max(256, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- hot path
+def draft_attn(mode: int, shape: Shape, q: torch.Tensor, seq_lens: Sequence[int], ws: torch.Tensor,
+               paged: Optional[Paged] = None, ring: Optional[Ring] = None, chunk_tokens: int = 0,
+               stream=None) -> Partials:
+    parts = Partials()
+    _check("wmtp_draft_attn", load().wmtp_draft_attn(
+        mode, ctypes.byref(shape), q.data_ptr(), ctypes.byref(paged) if paged is not None else None,
+        ctypes.byref(ring) if ring is not None else None, ctypes.cast(_lens(seq_lens), ctypes.c_void_p),
+        len(seq_lens), chunk_tokens, ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(parts),
+        _stream(stream)))
+    return parts
+
+
+def verify_attn(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, seq_lens: Sequence[int], ws: torch.Tensor,
+                split_tokens: int = 0, stream=None) -> Partials:
+    parts = Partials()
+    _check("wmtp_verify_attn", load().wmtp_verify_attn(
+        ctypes.byref(shape), q.data_ptr(), t_q, ctypes.byref(paged), ctypes.cast(_lens(seq_lens), ctypes.c_void_p),
+        len(seq_lens), split_tokens, ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(parts),
+        _stream(stream)))
+    return parts
+
+
+def combine(parts: Partials, out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check("wmtp_combine", load().wmtp_combine(ctypes.byref(parts), out.data_ptr(), dtype_code(out.dtype),
+                                               _ptr(lse), _stream(stream)))
+
+
+def ring_append(shape: Shape, ring: Ring, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
+                stream=None) -> None:
+    """k_new, v_new: [batch][t_new][H_kv][D]; pos[b]: absolute position of the first new token."""
+    _check("wmtp_ring_append", load().wmtp_ring_append(
+        ctypes.byref(shape), ctypes.byref(ring), k_new.data_ptr(), v_new.data_ptr(),
+        ctypes.cast(_lens(pos), ctypes.c_void_p), len(pos), k_new.shape[1], _stream(stream)))
+
+
+def paged_append(shape: Shape, paged: Paged, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
+                 stream=None) -> None:
+    _check("wmtp_paged_append", load().wmtp_paged_append(
+        ctypes.byref(shape), ctypes.byref(paged), k_new.data_ptr(), v_new.data_ptr(),
+        ctypes.cast(_lens(pos), ctypes.c_void_p), len(pos), k_new.shape[1], _stream(stream)))
+
+
+# ---------------------------------------------------------------- index resolution hooks
+def debug_resolve_paged(paged: Paged, num_kv_heads: int, head_dim: int, b: int, h: int,
+                        positions: torch.Tensor, stream=None) -> torch.Tensor:
+    out = torch.empty(positions.numel(), dtype=torch.int64, device=positions.device)
+    _check("wmtp_debug_resolve_paged", load().wmtp_debug_resolve_paged(
+        ctypes.byref(paged), num_kv_heads, head_dim, b, h, positions.data_ptr(), positions.numel(), out.data_ptr(),
+        _stream(stream)))
+    return out
+
+
+def debug_resolve_ring(sink: int, window: int, positions: torch.Tensor, stream=None) -> torch.Tensor:
+    out = torch.empty(positions.numel(), dtype=torch.int32, device=positions.device)
+    _check("wmtp_debug_resolve_ring", load().wmtp_debug_resolve_ring(
+        sink, window, positions.data_ptr(), positions.numel(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def debug_window_positions(sink: int, window: int, n: int, device, stream=None) -> torch.Tensor:
+    out = torch.empty(sink + window, dtype=torch.int32, device=device)
+    _check("wmtp_debug_window_positions", load().wmtp_debug_window_positions(
+        sink, window, n, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def version() -> str:
+    return load().wmtp_version().decode()

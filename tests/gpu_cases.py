@@ -1,0 +1,79 @@
+"""Shared setup for the GPU parity tests: caches on the device, oracle views on the host.
+
+The paged pool is filled on the host by block-level slicing (independent of
+both the oracle's resolver and the kernels'), then copied to the GPU.  The
+ring is filled on the GPU through wmtp_ring_append; the oracle never sees the
+ring, only the logical token sequence.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+import synth
+from long_context_decode_gqa_amd import wmtp as W
+
+DEV = "cuda"
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def host_array(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Oracle view of a tensor: bf16 bit patterns or float32 values."""
+    if dtype == "bf16":
+        return synth.bf16_bits(t)
+    return t.detach().cpu().float().numpy()
+
+
+def place_paged(pool: torch.Tensor, logical: torch.Tensor, bt_row: np.ndarray, block_size: int = 16) -> None:
+    """Copy [n][H][D] tokens into pool [num_blocks][H][block_size][D] block by block (host)."""
+    n = logical.shape[0]
+    for j in range(-(-n // block_size)):
+        seg = logical[j * block_size:(j + 1) * block_size]
+        pool[int(bt_row[j]), :, :seg.shape[0], :] = seg.permute(1, 0, 2)
+
+
+class PagedCache:
+    """One layer's paged K/V for `batch` sequences (device), sized for n0 + extra tokens."""
+
+    def __init__(self, k_ctx, v_ctx, n0, extra, seed, permuted=True, spare=2):
+        B = k_ctx.shape[0]
+        self.n0 = list(n0)
+        blocks = [synth.blocks_for(n + extra, 16) for n in self.n0]
+        bt, total = synth.block_table(seed, blocks, permuted=permuted, spare_blocks=spare)
+        self.bt_np = bt
+        kpool = torch.zeros((total,) + (k_ctx.shape[2], 16, k_ctx.shape[3]), dtype=k_ctx.dtype)
+        vpool = torch.zeros_like(kpool)
+        for b in range(B):
+            place_paged(kpool, k_ctx[b, :self.n0[b]], bt[b])
+            place_paged(vpool, v_ctx[b, :self.n0[b]], bt[b])
+        self.k = kpool.to(DEV)
+        self.v = vpool.to(DEV)
+        self.bt = torch.from_numpy(bt).to(DEV)
+        self.desc = W.make_paged(self.k, self.v, self.bt)
+
+
+class RingCache:
+    def __init__(self, batch, hk, d, sink, window, dtype):
+        self.k = torch.zeros((batch, hk, sink + window, d), dtype=dtype, device=DEV)
+        self.v = torch.zeros_like(self.k)
+        self.tags = torch.full((batch, sink + window), -1, dtype=torch.int32, device=DEV)
+        self.desc = W.make_ring(self.k, self.v, self.tags, sink, window)
+
+
+def max_err(gpu: torch.Tensor, ref: np.ndarray) -> float:
+    g = gpu.detach().cpu().double().numpy()
+    if g.size == 0:
+        return 0.0
+    both_inf = np.isneginf(g) & np.isneginf(ref)
+    d = np.abs(np.where(both_inf, 0.0, g - np.where(both_inf, 0.0, ref)))
+    return float(np.nanmax(d)) if not np.isnan(d).any() else float("inf")
+
+
+def run_combine(parts, rows, D, batch, out_dtype=torch.float32):
+    out = torch.empty((batch, rows, D), dtype=out_dtype, device=DEV)
+    lse = torch.empty((batch, rows), dtype=torch.float32, device=DEV)
+    W.combine(parts, out, lse)
+    return out, lse

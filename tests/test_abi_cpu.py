@@ -1,0 +1,217 @@
+"""C-ABI checks that need no GPU: exports, argument validation, workspace sizing.
+
+Every call here returns before making any HIP call (the library validates all
+arguments first), so nothing is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from long_context_decode_gqa_amd import wmtp as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wmtp.h")
+
+FAKE = 1 << 20          # a 16-byte aligned non-null "device" address; never dereferenced
+FAKE_ODD = FAKE + 8     # not 16-byte aligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wmtp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = W.load()
+    declared = header_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(W.EXPORTS)
+    assert W.version().startswith("wmtp")
+
+
+def test_status_strings():
+    lib = W.load()
+    for st in (W.OK, W.EINVAL, W.EUNSUPPORTED, W.EALIGN, W.EWORKSPACE, W.ELAUNCH):
+        assert lib.wmtp_status_str(st).decode() not in ("", "unknown status")
+    assert lib.wmtp_status_str(-99).decode() == "unknown status"
+
+
+def shape(hq=16, hk=2, d=256, dt=W.BF16, scale=0.0625):
+    return W.Shape(hq, hk, d, scale, dt)
+
+
+def lens(*xs):
+    return ctypes.cast((ctypes.c_int32 * len(xs))(*xs), ctypes.c_void_p)
+
+
+def paged(k=FAKE, v=FAKE, bt=FAKE, bs=16, mb=100, nb=100):
+    return W.Paged(k, v, bt, bs, mb, nb)
+
+
+def ring(k=FAKE, v=FAKE, tags=FAKE, s=4, w=64):
+    return W.Ring(k, v, tags, s, w)
+
+
+def draft(mode=W.FULL, sh=None, q=FAKE, kv="default", rg="default", seq=(1000,), chunk=0, ws=FAKE, wsb=1 << 30,
+          parts=True):
+    lib = W.load()
+    sh = shape() if sh is None else sh
+    kv = paged() if kv == "default" else kv
+    rg = ring() if rg == "default" else rg
+    p = W.Partials()
+    return lib.wmtp_draft_attn(mode, ctypes.byref(sh) if sh is not False else None, q,
+                               ctypes.byref(kv) if kv is not None else None,
+                               ctypes.byref(rg) if rg is not None else None, lens(*seq), len(seq), chunk, ws, wsb,
+                               ctypes.byref(p) if parts else None, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(), None),                                             # valid (not launched here)
+    (dict(sh=False), W.EINVAL),
+    (dict(sh=shape(hq=12, hk=8)), W.EINVAL),                    # H_q % H_kv != 0
+    (dict(sh=shape(hq=48, hk=3)), W.EUNSUPPORTED),              # G = 16
+    (dict(sh=shape(d=96)), W.EUNSUPPORTED),
+    (dict(sh=shape(dt=7)), W.EINVAL),
+    (dict(sh=shape(scale=float("nan"))), W.EINVAL),
+    (dict(mode=5), W.EINVAL),
+    (dict(mode=W.FULL | 0x40), W.EINVAL),
+    (dict(q=None), W.EINVAL),
+    (dict(q=FAKE_ODD), W.EALIGN),
+    (dict(kv=None), W.EINVAL),
+    (dict(kv=paged(bs=32)), W.EUNSUPPORTED),
+    (dict(kv=paged(k=FAKE_ODD)), W.EALIGN),
+    (dict(kv=paged(mb=10)), W.EINVAL),                          # table too short for 1000 tokens
+    (dict(seq=(-1,)), W.EINVAL),
+    (dict(chunk=100), W.EINVAL),                                # not a multiple of 64
+    (dict(ws=None), W.EINVAL),
+    (dict(ws=FAKE + 16), W.EALIGN),
+    (dict(wsb=16), W.EWORKSPACE),
+    (dict(parts=False), W.EINVAL),
+    (dict(mode=W.SINK_WINDOW, rg=None), W.EINVAL),
+    (dict(mode=W.SINK_WINDOW, rg=ring(w=0)), W.EINVAL),
+    (dict(mode=W.SINK_WINDOW, rg=ring(s=-1)), W.EINVAL),
+    (dict(mode=W.SINK_WINDOW, rg=ring(k=FAKE_ODD)), W.EALIGN),
+])
+def test_draft_argument_checks(kwargs, status):
+    if status is None:
+        # the valid call must pass every check; planning alone shows that without launching
+        sh = shape()
+        n = W.load().wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(1000), 1, 0, 0, 1)
+        assert n > 0
+        return
+    assert draft(**kwargs) == status
+
+
+def test_draft_batch_limits():
+    lib = W.load()
+    sh = shape()
+    assert lib.wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(1), 0, 0, 0, 1) == W.EINVAL
+    big = (ctypes.c_int32 * 65)(*([10] * 65))
+    assert lib.wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), ctypes.cast(big, ctypes.c_void_p), 65, 0, 0,
+                                          1) == W.EINVAL
+
+
+def test_workspace_sizes_follow_the_split_plan():
+    sh = shape()
+    # full mode at 1M+1 tokens, 1024-token splits: 1025 splits x 16 rows x (256 + 1) floats, 256-byte aligned
+    n = W.draft_workspace_bytes(W.FULL, sh, [1048577], 1024)
+    o = 1025 * 16 * 256 * 4
+    assert n == o + ((1025 * 16 * 4 + 255) // 256) * 256
+    # window mode scans min(n, S+W) slots
+    assert W.draft_workspace_bytes(W.SINK_WINDOW, sh, [1048577], 256, 4, 4096) == \
+        W.draft_workspace_bytes(W.FULL, sh, [4100], 256)
+    assert W.draft_workspace_bytes(W.SINK_WINDOW, sh, [100], 256, 4, 4096) == \
+        W.draft_workspace_bytes(W.FULL, sh, [100], 256)
+    # verify: rows = t_q * H_q
+    nv = W.verify_workspace_bytes(sh, 4, [1048580], 2048)
+    splits = -(-1048580 // 2048)
+    assert nv == splits * 64 * 256 * 4 + ((splits * 64 * 4 + 255) // 256) * 256
+    # an empty sequence needs no split
+    assert W.draft_workspace_bytes(W.FULL, sh, [0, 64], 64) == W.draft_workspace_bytes(W.FULL, sh, [64], 64)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(sh=shape(dt=W.F32)), W.EUNSUPPORTED),
+    (dict(sh=shape(d=128)), W.EUNSUPPORTED),
+    (dict(t_q=0), W.EINVAL),
+    (dict(t_q=5), W.EUNSUPPORTED),                               # 5 x 8 rows > 32
+    (dict(seq=(3,)), W.EINVAL),                                  # fewer keys than queries
+    (dict(split=48), W.EINVAL),
+])
+def test_verify_argument_checks(args, status):
+    lib = W.load()
+    sh = args.get("sh", shape())
+    seq = args.get("seq", (1000,))
+    assert lib.wmtp_verify_workspace_bytes(ctypes.byref(sh), args.get("t_q", 4), lens(*seq), len(seq),
+                                           args.get("split", 0)) == status
+    p = W.Partials()
+    kv = paged()
+    assert lib.wmtp_verify_attn(ctypes.byref(sh), FAKE, args.get("t_q", 4), ctypes.byref(kv), lens(*seq), len(seq),
+                                args.get("split", 0), FAKE, 1 << 30, ctypes.byref(p), None) == status
+
+
+def test_verify_pointer_checks():
+    lib = W.load()
+    sh = shape()
+    p = W.Partials()
+    kv = paged()
+    call = lambda q=FAKE, kvp=ctypes.byref(kv), ws=FAKE, wsb=1 << 30: lib.wmtp_verify_attn(
+        ctypes.byref(sh), q, 4, kvp, lens(1000), 1, 0, ws, wsb, ctypes.byref(p), None)
+    assert call(q=None) == W.EINVAL
+    assert call(q=FAKE_ODD) == W.EALIGN
+    assert call(kvp=None) == W.EINVAL
+    assert call(wsb=64) == W.EWORKSPACE
+    bad = paged(mb=2)
+    assert call(kvp=ctypes.byref(bad)) == W.EINVAL
+
+
+def test_combine_checks():
+    lib = W.load()
+    p = W.Partials()
+    p.o, p.lse, p.batch, p.rows_per_seq, p.head_dim, p.total_splits = FAKE, FAKE, 1, 16, 256, 3
+    p.split_base[0], p.split_base[1] = 0, 3
+    assert lib.wmtp_combine(None, FAKE, W.F32, None, None) == W.EINVAL
+    assert lib.wmtp_combine(ctypes.byref(p), None, W.F32, None, None) == W.EINVAL
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE, 9, None, None) == W.EINVAL
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE_ODD, W.F32, None, None) == W.EALIGN
+    p.split_base[1] = 2
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE, W.F32, None, None) == W.EINVAL   # inconsistent total
+    p.split_base[1] = 3
+    p.head_dim = 80
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE, W.F32, None, None) == W.EUNSUPPORTED
+    p.head_dim = 256
+    p.batch = 0
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE, W.F32, None, None) == W.EINVAL
+
+
+def test_append_checks():
+    lib = W.load()
+    sh = shape()
+    r = ring()
+    kv = paged(mb=4)
+    pos = lens(10)
+    assert lib.wmtp_ring_append(ctypes.byref(sh), None, FAKE, FAKE, pos, 1, 1, None) == W.EINVAL
+    assert lib.wmtp_ring_append(ctypes.byref(sh), ctypes.byref(r), None, FAKE, pos, 1, 1, None) == W.EINVAL
+    assert lib.wmtp_ring_append(ctypes.byref(sh), ctypes.byref(r), FAKE_ODD, FAKE, pos, 1, 1, None) == W.EALIGN
+    assert lib.wmtp_ring_append(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, lens(-3), 1, 1, None) == W.EINVAL
+    assert lib.wmtp_ring_append(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, pos, 1, -1, None) == W.EINVAL
+    assert lib.wmtp_ring_append(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, pos, 0, 1, None) == W.EINVAL
+    # paged: 4 blocks cover positions < 64
+    assert lib.wmtp_paged_append(ctypes.byref(sh), ctypes.byref(kv), FAKE, FAKE, lens(60), 1, 5, None) == W.EINVAL
+    assert lib.wmtp_paged_append(ctypes.byref(sh), None, FAKE, FAKE, lens(0), 1, 1, None) == W.EINVAL
+
+
+def test_debug_hook_checks():
+    lib = W.load()
+    kv = paged()
+    assert lib.wmtp_debug_resolve_paged(ctypes.byref(kv), 2, 256, 0, 2, FAKE, 1, FAKE, None) == W.EINVAL   # h >= H_kv
+    assert lib.wmtp_debug_resolve_paged(None, 2, 256, 0, 0, FAKE, 1, FAKE, None) == W.EINVAL
+    assert lib.wmtp_debug_resolve_ring(4, 0, FAKE, 1, FAKE, None) == W.EINVAL
+    assert lib.wmtp_debug_window_positions(-1, 4, 10, FAKE, None) == W.EINVAL
+    assert lib.wmtp_debug_window_positions(4, 4, 10, None, None) == W.EINVAL
