@@ -36,6 +36,51 @@ from long_context_decode_gqa_amd import wmtp as W  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M context"
 
+# HBM bytes per verify launch at the 1M-token workload, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by the factors a plain
+# 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
+# for the kernel sources they were taken with (sha256 below); otherwise null.
+VERIFY_TRAFFIC = {"sources_sha256": "9b29d52b24f46ac05df163c0e8325c0aa8320dda035fc2113e705bc3df89bc13",
+                  "fetch_kib": 1049371.55, "write_kib": 16512.25, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
+
+
+def verify_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in VERIFY_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def verify_traffic_bytes():
+    t = VERIFY_TRAFFIC
+    if t["fetch_kib"] is None or t["sources_sha256"] != verify_sources_sha256():
+        return None
+    return int(round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024))
+
+
+def stream_ceiling_gbps(dev, nbytes=2 << 30):
+    """Best rate of the library's streaming-read probe over a 2 GiB buffer."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
+    best = 0.0
+    for wgs in (2048, 4096):
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            W.stream_read(src, sink, wgs)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(10):
+            W.stream_read(src, sink, wgs)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) / 10 * 1e-3) / 1e9)
+    del src
+    torch.cuda.empty_cache()
+    return best
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -163,7 +208,13 @@ def time_steps(step, mode, flag, steps, warmup):
 
 
 def cpu_baseline(wl, n0):
-    """The float64 oracle on a bounded sample, scaled to one decode step (both draft modes)."""
+    """The float64 oracle on a bounded sample, scaled to one decode step (both draft modes).
+
+    Sample: one verify layer over all n0 + gamma + 1 keys for one KV head (4
+    causal queries x G heads), one native draft step over n0 + 1 keys for the
+    same head, and one windowed draft step; scaled by KV heads, target layers and
+    draft steps.  Values are synthetic bf16 keys and values.
+    """
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -171,39 +222,36 @@ def cpu_baseline(wl, n0):
     except Exception:
         threads = os.cpu_count() or 1
     rng = np.random.default_rng(0)
-    Hk, D, G = wl.num_kv_heads, wl.head_dim, wl.group
-    sample_n = 131072
-    k = (rng.standard_normal((sample_n, 1, D), dtype=np.float32) * 0.5)
-    v = (rng.standard_normal((sample_n, 1, D), dtype=np.float32) * 0.5)
-    kb = torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    vb = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    q = rng.standard_normal((wl.gamma + 1, G, D))
-    src_k, src_v = O.LogicalKV(kb, "bf16"), O.LogicalKV(vb, "bf16")
+    D, G, g = wl.head_dim, wl.group, wl.gamma
+    n = n0 + g + 1
+    kb = torch.from_numpy(rng.standard_normal((n, 1, D), dtype=np.float32) * 0.5).to(torch.bfloat16)
+    vb = torch.from_numpy(rng.standard_normal((n, 1, D), dtype=np.float32) * 0.5).to(torch.bfloat16)
+    src_k = O.LogicalKV(kb.view(torch.int16).numpy().view(np.uint16), "bf16")
+    src_v = O.LogicalKV(vb.view(torch.int16).numpy().view(np.uint16), "bf16")
+    q = rng.standard_normal((g + 1, G, D))
     t0 = time.perf_counter()
-    for i in range(wl.gamma + 1):                 # one verify layer, one KV head, 131,072 keys
-        O.attention_over(q[i], src_k, src_v, np.arange(sample_n - wl.gamma + i), 0, wl.scale)
+    for i in range(g + 1):                         # one verify layer, one KV head
+        O.attention_over(q[i], src_k, src_v, np.arange(n0 + i + 1), 0, wl.scale)
     t_verify = time.perf_counter() - t0
-    win = wl.sink + wl.window
     t0 = time.perf_counter()
-    O.attention_over(q[0], src_k, src_v, O.visible_positions(sample_n, O.SINK_WINDOW, wl.sink, wl.window), 0,
+    O.attention_over(q[0], src_k, src_v, np.arange(n0 + 1), 0, wl.scale)
+    t_native = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.attention_over(q[0], src_k, src_v, O.visible_positions(n0 + 1, O.SINK_WINDOW, wl.sink, wl.window), 0,
                      wl.scale)
     t_win = time.perf_counter() - t0
-    # scale: verify cost is linear in keys; per step = target_layers x Hk heads; draft native = one
-    # query token per step over n0 keys (a quarter of a verify head-layer's work), window = as measured
-    per_key = t_verify / (sample_n * (wl.gamma + 1))
-    verify_step = per_key * (n0 + wl.gamma + 1) * (wl.gamma + 1) * Hk * wl.target_layers
-    native_draft = per_key * (n0 + 2) * Hk * wl.gamma
-    win_draft = t_win * Hk * wl.gamma
+    Hk, L = wl.num_kv_heads, wl.target_layers
+    verify_step = t_verify * Hk * L
     return {
-        "value": round((verify_step + win_draft) * 1e6, 1),
+        "value": round((verify_step + t_win * Hk * g) * 1e6, 1),
         "unit": "us/decode-step",
-        "native_value": round((verify_step + native_draft) * 1e6, 1),
+        "native_value": round((verify_step + t_native * Hk * g) * 1e6, 1),
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"float64 oracle, 1 KV head x {sample_n} keys x {wl.gamma + 1} causal queries (verify) and "
-                   f"1 KV head x {win} window entries (draft); scaled linearly in keys to {wl.target_layers} "
-                   f"layers x {Hk} KV heads x {n0} keys + {wl.gamma} draft steps; measured "
-                   f"{t_verify + t_win:.1f} s"),
+        "sample": (f"float64 oracle on 1 KV head: one verify layer ({g + 1} causal queries x {G} heads over "
+                   f"{n} keys), one native draft step ({n0 + 1} keys) and one windowed draft step "
+                   f"({wl.sink}+{wl.window} entries); scaled x{Hk} KV heads, x{L} target layers, x{g} draft steps; "
+                   f"measured {t_verify + t_native + t_win:.1f} s"),
     }
 
 
@@ -218,6 +266,8 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="verify split size (0 = library default)")
     ap.add_argument("--exact-pv", action="store_true", help="draft PV with fp32 weights instead of bf16 pairs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run a plain 256 MiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -230,9 +280,18 @@ def main():
         sys.exit(2)
     W.load()
     dev = "cuda"
+    if args.calibrate:
+        src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = synth.workload("step_1m_bf16", contexts=(args.context,))
     n0 = args.context
     flag = 0 if args.exact_pv else W.DRAFT_FAST_PV
+    log("streaming-read ceiling")
+    ceiling = stream_ceiling_gbps(dev)
     log(f"setup: {wl.target_layers} target layers + 1 draft layer at {n0} tokens")
     step = Step(wl, n0, wl.target_layers, args.chunk_full, args.chunk_window,
                 args.split, dev)
@@ -289,7 +348,10 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": verify_traffic_bytes(),
+            "algorithmic_bytes": ver_bytes,
+            "measured_read_ceiling": round(ceiling, 1),
+            "frac_of_measured_ceiling": round(achieved / ceiling, 4),
         },
     }
     native_draft_bytes = draft_launch_bytes(n0 + 1, wl, True)

@@ -216,6 +216,15 @@ int wmtp_debug_resolve_ring(int32_t sink, int32_t window, const int32_t* positio
  * sink+window visible set (-1 if the slot holds none).  out: device int32 [sink+window]. */
 int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t n, int32_t* out, void* stream);
 
+/* ---------------------------------------------------------------- measurement */
+
+/* Streaming-read probe: `workgroups` workgroups of 256 threads each read one
+ * contiguous part of src[0, bytes) with 16-byte loads and write one word per
+ * thread to sink (device, workgroups * 256 uint32).  It measures the practical
+ * HBM read ceiling that the attention kernels' bandwidth is compared with.
+ * bytes must be a positive multiple of 16; src 16-byte aligned. */
+int wmtp_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
+
 /* ---------------------------------------------------------------- misc */
 const char* wmtp_status_str(int status);
 const char* wmtp_version(void);

@@ -16,9 +16,9 @@ using namespace wmtp;
 
 namespace {
 
-constexpr int kDraftDefaultChunkFull = 1024;
-constexpr int kDraftDefaultChunkWindow = 256;
-constexpr int kVerifyDefaultSplit = 2048;
+constexpr int kDraftDefaultChunkFull = 4096;
+constexpr int kDraftDefaultChunkWindow = 64;
+constexpr int kVerifyDefaultSplit = 4096;
 constexpr int kDraftTile = 64;
 constexpr int kVerifyTile = 32;    // keys per verify tile
 
@@ -356,6 +356,12 @@ int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t n, int32_t
   if (sink < 0 || window < 1 || n < 0 || !out) return WMTP_EINVAL;
   if ((int64_t)sink + window > INT32_MAX / 2) return WMTP_EINVAL;
   return launch_status(launch_debug_window_positions(sink, window, n, out, static_cast<hipStream_t>(stream)));
+}
+
+int wmtp_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+  if (!src || !sink || bytes < 16 || workgroups < 1 || workgroups > (1 << 20)) return WMTP_EINVAL;
+  if (!aligned(src, 16) || !aligned(sink, 4) || bytes % 16 != 0) return WMTP_EALIGN;
+  return launch_status(launch_stream_read(src, bytes, sink, workgroups, static_cast<hipStream_t>(stream)));
 }
 
 const char* wmtp_status_str(int status) {

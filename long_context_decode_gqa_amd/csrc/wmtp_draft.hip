@@ -9,25 +9,28 @@
 // ring slot + tag check).
 //
 // Work item = (sequence b, KV head h, split of `chunk` visible entries); one
-// 256-thread workgroup (4 waves) per item.  The G query heads of the KV head
-// are packed, so each K/V byte is read from HBM once per group.
+// workgroup per item whose waves each own a 64-byte slice of every K/V row (8
+// waves for a 512-byte bf16 row of head_dim 256).  The G query heads of the KV
+// head are packed, so each K/V byte is read from HBM once per group.
 //
 // Per 64-entry tile:
-//   1. K: every wave loads its quarter of the 64 rows (coalesced 16-byte loads,
-//      one tile ahead) and stores it into a wave-private LDS stage whose 16-byte
-//      pieces are XOR-swizzled so that "one lane per entry" reads are free of
-//      bank conflicts.
-//   2. QK: lane = entry; the wave's quarter of the G query rows comes from
+//   1. K: every wave loads its slice of the 64 rows (coalesced 16-byte loads
+//      into registers, two tiles ahead) and at the start of the tile stores it
+//      into a wave-private LDS stage whose 16-byte pieces are XOR-swizzled so
+//      that "one lane per entry" reads are free of bank conflicts.
+//   2. QK: lane = entry; the wave's slice of the G query rows comes from
 //      SGPRs (wave-uniform scalar loads), so bf16 pairs go straight into
 //      v_dot2_f32_bf16 with no unpacking and no cross-lane reduction.
-//   3. The 4 quarter-dot-products are summed through LDS (one barrier per tile).
+//   3. The slice dot products are summed through LDS (one barrier per tile).
 //   4. Online softmax in the log2 domain with a lazy maximum: the running max is
 //      only raised (and the accumulators rescaled) when a score exceeds it by
 //      more than 2^8, which is rare after the first tile; the result is the same
 //      up to rounding because numerator and denominator share the reference.
-//   5. PV: each wave owns a quarter of D; V rows are loaded into registers at
-//      the start of the tile; probabilities are handed from the entry lanes
-//      through LDS.
+//   5. PV: each wave owns its slice of D; V rows arrive in registers two tiles
+//      ahead; probabilities are handed from the entry lanes through LDS.
+// K and V go through a 3-slot register ring; the loop body is unrolled over the
+// slots and every body issues the same loads, so the compiler's wait counts
+// keep two tiles in flight.
 // The split writes o = sum p v / sum p and lse = ln sum exp(s) for every packed
 // row; a separate LSE combine merges the splits.
 #include "wmtp_device.hpp"
@@ -39,21 +42,26 @@ template <int D, int G, bool BF16>
 struct DraftShape {
   static constexpr int ES = BF16 ? 2 : 4;      // element bytes
   static constexpr int ROWB = D * ES;          // bytes of one entry's row (one head)
-  static constexpr int QB = ROWB / 4;          // one wave's quarter of a row
-  static constexpr int NCH = QB / 16;          // 16-byte pieces per quarter row
+  // Each wave owns a slice of QB bytes of every row: 64 bytes (4 waves for a
+  // 256-byte row, 8 for 512, 16 for 1 KiB), or a quarter of shorter rows.
+  static constexpr int QB = ROWB >= 256 ? 64 : ROWB / 4;
+  static constexpr int NW = ROWB / QB;         // waves per workgroup
+  static constexpr int THREADS = NW * 64;
+  static constexpr int NCH = QB / 16;          // 16-byte pieces per row slice
   static constexpr int EPP = 16 / ES;          // elements per piece
   static constexpr int TILE = 64;
   static constexpr int TPI = 64 / NCH;         // entries covered by one 1 KiB wave load
   static constexpr int GP = (G + 3) / 4 * 4;   // G padded to whole float4 planes
   static constexpr int KSTAGE = TILE * QB;     // bytes of one wave's K stage
+  static constexpr int LDS_BYTES = NW * KSTAGE + 2 * NW * GP * TILE * 4;
   // PV layout: each lane loads 8 bytes of a V row per load (EV elements);
-  // LPR lanes cover one quarter row, TPV entries per wave load, NV loads per tile.
+  // LPR lanes cover one row slice, TPV entries per wave load, NV loads per tile.
   static constexpr int VB = 8;
   static constexpr int EV = VB / ES;
   static constexpr int LPR = QB / VB;
   static constexpr int TPV = 64 / LPR;
   static constexpr int NV = TILE / TPV;
-  static_assert(NCH >= 2 && NCH <= 16, "quarter row must hold 2..16 pieces");
+  static_assert(NCH >= 2 && NCH <= 16, "a row slice must hold 2..16 pieces");
   static_assert(GP * TILE * 4 <= KSTAGE, "probability tile must fit in a K stage");
 };
 
@@ -71,15 +79,15 @@ __device__ __forceinline__ int k_piece(int t, int c) {
 }
 
 template <int D, int G, bool BF16, bool WINDOW, bool PV_DOT2>
-__global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a) {
+__global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_splitk_kernel(const SplitArgs a) {
   using S = DraftShape<D, G, BF16>;
-  constexpr int NCH = S::NCH, TPI = S::TPI, GP = S::GP, QB = S::QB, ROWB = S::ROWB;
+  constexpr int NCH = S::NCH, TPI = S::TPI, GP = S::GP, QB = S::QB, ROWB = S::ROWB, NW = S::NW;
   constexpr int EV = S::EV, LPR = S::LPR, TPV = S::TPV, NV = S::NV;
   constexpr float TAU = 8.0f;   // lazy-max slack, log2 units
   static_assert(!PV_DOT2 || BF16, "dot2 PV needs bf16 values");
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[4 * 2 * S::KSTAGE];
-  __shared__ __attribute__((aligned(16))) float sc_lds[2 * 4 * GP * S::TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[NW * S::KSTAGE];
+  __shared__ __attribute__((aligned(16))) float sc_lds[2 * NW * GP * S::TILE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -100,13 +108,11 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
   const int32_t* tags = a.slot_pos + (int64_t)b * a.slots;
   const int last_blk_idx = (t_end - 1) >> 4;
 
-  // query rows of this KV head, this wave's quarter of D (wave-uniform -> SGPRs)
+  // query rows of this KV head, this wave's slice of D (wave-uniform -> SGPRs)
   const int64_t qrow0 = (int64_t)b * a.num_q_heads + (int64_t)h * G;
   const_u32_ptr q32 = as_const_u32(a.q) + qrow0 * (D * S::ES / 4) + wave * (QB / 4);
 
-  uint8_t* my_k = k_lds + wave * 2 * S::KSTAGE;
-  const int kl_tok = lane / NCH, kl_c = lane % NCH;   // K load lane roles: entry, piece
-  const int pv_tok = lane / LPR, pv_d = lane % LPR;   // PV lane roles: entry group, 8-byte slot
+  uint8_t* my_k = k_lds + wave * S::KSTAGE;
 
   // ---- addressing.  A tile's entries live in up to 4 runs of 16 rows (paged) or
   // one run of 64 rows (ring).  run[j] is the uniform byte offset of run j; a lane
@@ -122,8 +128,6 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
       }
     }
   };
-  // byte offset of tile entry tt inside its run; `first` is the first entry of the
-  // wave load (compile-time after unrolling) and SPAN the entries it covers
   auto lane_off = [&](int t0, int tt) -> uint32_t {
     if constexpr (WINDOW) return (uint32_t)min(tt, a.slots - 1 - t0) * ROWB;
     return (uint32_t)(tt & 15) * ROWB;
@@ -139,43 +143,41 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
     return base + r;
   };
 
-  u32x4 kreg[NCH];
-  uint2 vreg[NV];
-  int tag_cur = 0, tag_next = 0;
+  // Register ring: the K and V of tile i arrive in slot i % kRing, issued
+  // kRing - 1 tiles ahead, so two tiles per wave are in flight while one is
+  // computed.
+  constexpr int kRing = 3;
+  u32x4 kreg[kRing][NCH];
+  uint2 vreg[kRing][NV];
+  int tag[kRing] = {0, 0, 0};
 
-  auto load_k = [&](int t0, const int64_t (&run)[4]) {
+  // Loads of tile `it`, clamped to the last tile so every body issues the same
+  // number of loads.  `ln` is this lane's index.
+  auto issue = [&](int it, int slot, int ln) {
+    const int t0 = t_begin + min(it, ntiles - 1) * S::TILE;
+    int64_t run[4];
+    tile_runs(t0, run);
+    const int k_tok = ln / NCH, k_c = ln % NCH;
+    const int v_tok = ln / LPR, v_d = ln % LPR;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int tt = i * TPI + kl_tok;
-      kreg[i] = load_at<u32x4>(run_base(kbase, run, i * TPI, TPI, tt), lane_off(t0, tt) + kl_c * 16);
+      const int tt = i * TPI + k_tok;
+      kreg[slot][i] = load_at<u32x4>(run_base(kbase, run, i * TPI, TPI, tt), lane_off(t0, tt) + k_c * 16);
     }
-  };
-  // V: load k brings entry k*TPV + pv_tok (fp32 PV) or, for the paired bf16 PV,
-  // entry 2 (k/2 * TPV + pv_tok) + k%2, bytes [8 pv_d, 8 pv_d + 8) of the quarter.
-  auto load_v = [&](int t0, const int64_t (&run)[4], uint2 (&dst)[NV]) {
+    // V: load k brings entry k*TPV + v_tok (fp32 PV) or, for the paired bf16 PV,
+    // entry 2 (k/2 * TPV + v_tok) + k%2, bytes [8 v_d, 8 v_d + 8) of the slice.
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       if constexpr (PV_DOT2) {
         const int first = 2 * (k >> 1) * TPV;
-        const int tt = first + 2 * pv_tok + (k & 1);
-        dst[k] = load_at<uint2>(run_base(vbase, run, first, 2 * TPV, tt), lane_off(t0, tt) + pv_d * 8);
+        const int tt = first + 2 * v_tok + (k & 1);
+        vreg[slot][k] = load_at<uint2>(run_base(vbase, run, first, 2 * TPV, tt), lane_off(t0, tt) + v_d * 8);
       } else {
-        const int tt = k * TPV + pv_tok;
-        dst[k] = load_at<uint2>(run_base(vbase, run, k * TPV, TPV, tt), lane_off(t0, tt) + pv_d * 8);
+        const int tt = k * TPV + v_tok;
+        vreg[slot][k] = load_at<uint2>(run_base(vbase, run, k * TPV, TPV, tt), lane_off(t0, tt) + v_d * 8);
       }
     }
-  };
-  auto load_tag = [&](int t0) -> int {
-    if constexpr (WINDOW) return tags[min(t0 + lane, a.slots - 1)];
-    return 0;
-  };
-  auto store_k = [&](int stage) {
-    uint8_t* dst = my_k + stage * S::KSTAGE;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int tt = i * TPI + kl_tok;
-      *reinterpret_cast<u32x4*>(dst + k_piece<NCH>(tt, kl_c) * 16) = kreg[i];
-    }
+    if constexpr (WINDOW) tag[slot] = tags[min(t0 + ln, a.slots - 1)];
   };
 
   float o[G][EV];
@@ -188,44 +190,31 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
     for (int e = 0; e < EV; ++e) o[g][e] = 0.f;
   }
 
-  if (ntiles > 0) {
-    int64_t run[4];
-    tile_runs(t_begin, run);
-    load_k(t_begin, run);
-    tag_next = load_tag(t_begin);
-    store_k(0);
-  }
-
-  for (int it = 0; it < ntiles; ++it) {
+  auto body = [&](int it, int slot) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));     // recompute lane offsets per tile instead of holding them
     const int t0 = t_begin + it * S::TILE;
-    const int stage = it & 1;
-    const bool has_next = it + 1 < ntiles;
-    tag_cur = tag_next;
-    {
-      // V of this tile (consumed after QK and the softmax), then K of the next one
-      int64_t run[4];
-      tile_runs(t0, run);
-      load_v(t0, run, vreg);
-    }
-    if (has_next) {
-      int64_t run[4];
-      tile_runs(t0 + S::TILE, run);
-      load_k(t0 + S::TILE, run);
-      tag_next = load_tag(t0 + S::TILE);
-    }
+    issue(it + kRing - 1, (slot + kRing - 1) % kRing, ln);
+    __builtin_amdgcn_sched_barrier(0);   // loads stay in issue order at the top of the body
+    const int k_tok = ln / NCH, k_c = ln % NCH;
+    const int v_tok = ln / LPR;
 
-    // ---- QK: lane = entry, partial dot over this wave's quarter of D
+    // ---- K of this tile -> swizzled LDS stage
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      *reinterpret_cast<u32x4*>(my_k + k_piece<NCH>(i * TPI + k_tok, k_c) * 16) = kreg[slot][i];
+
+    // ---- QK: lane = entry, partial dot over this wave's slice of D
     float acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.f;
-    const uint8_t* kst = my_k + stage * S::KSTAGE;
     // q is re-read from the scalar cache every tile: hoisting it out of the loop
-    // would need G * D / 8 registers for the wave's quarter.
+    // would hold all of the wave's slice of the G query rows in registers.
     const_u32_ptr qt = q32;
     asm volatile("" : "+s"(qt));
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const u32x4 kk = *reinterpret_cast<const u32x4*>(kst + k_piece<NCH>(lane, c) * 16);
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(my_k + k_piece<NCH>(ln, c) * 16);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const_u32_ptr qg = qt + (int64_t)g * (D * S::ES / 4) + c * 4;
@@ -239,24 +228,24 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
       }
     }
 
-    // ---- sum the 4 quarter products through LDS
-    float* sc = sc_lds + stage * (4 * GP * S::TILE);
+    // ---- sum the NW slice products through LDS
+    float* sc = sc_lds + (it & 1) * (NW * GP * S::TILE);
 #pragma unroll
     for (int pl = 0; pl < GP / 4; ++pl) {
       f32x4 w4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w4[e] = (pl * 4 + e < G) ? acc[pl * 4 + e] : 0.f;
-      *reinterpret_cast<f32x4*>(sc + ((wave * (GP / 4) + pl) * S::TILE + lane) * 4) = w4;
+      *reinterpret_cast<f32x4*>(sc + ((wave * (GP / 4) + pl) * S::TILE + ln) * 4) = w4;
     }
     __syncthreads();
     float s2[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) s2[g] = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
 #pragma unroll
       for (int pl = 0; pl < GP / 4; ++pl) {
-        const f32x4 w4 = *reinterpret_cast<const f32x4*>(sc + ((w * (GP / 4) + pl) * S::TILE + lane) * 4);
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(sc + ((w * (GP / 4) + pl) * S::TILE + ln) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (pl * 4 + e < G) s2[pl * 4 + e] += w4[e];
@@ -264,8 +253,8 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
     }
 
     // ---- online softmax (log2 domain, lazy maximum)
-    bool valid = t0 + lane < t_end;
-    if constexpr (WINDOW) valid = valid && window_visible(tag_cur, n, a.sink, a.window);
+    bool valid = t0 + ln < t_end;
+    if constexpr (WINDOW) valid = valid && window_visible(tag[slot], n, a.sink, a.window);
     bool exceed = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -293,20 +282,20 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
     }
 
     // ---- hand p to the PV lanes through the (now free) K stage
-    float* pl_lds = reinterpret_cast<float*>(my_k + stage * S::KSTAGE);
+    float* pl_lds = reinterpret_cast<float*>(my_k);
 #pragma unroll
     for (int pl = 0; pl < GP / 4; ++pl) {
       f32x4 w4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w4[e] = (pl * 4 + e < G) ? p[pl * 4 + e] : 0.f;
-      *reinterpret_cast<f32x4*>(pl_lds + (pl * S::TILE + lane) * 4) = w4;
+      *reinterpret_cast<f32x4*>(pl_lds + (pl * S::TILE + ln) * 4) = w4;
     }
 
-    // ---- PV over this wave's quarter of D
+    // ---- PV over this wave's slice of D
     if constexpr (PV_DOT2) {
 #pragma unroll
       for (int k = 0; k < NV / 2; ++k) {
-        const int ta = 2 * (k * TPV + pv_tok);
+        const int ta = 2 * (k * TPV + v_tok);
         float pa[GP], pb[GP];
 #pragma unroll
         for (int pl = 0; pl < GP / 4; ++pl) {
@@ -315,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
 #pragma unroll
           for (int e = 0; e < 4; ++e) { pa[pl * 4 + e] = xa[e]; pb[pl * 4 + e] = xb[e]; }
         }
-        const uint2 va = vreg[2 * k], vb = vreg[2 * k + 1];
+        const uint2 va = vreg[slot][2 * k], vb = vreg[slot][2 * k + 1];
         uint32_t vp[4];
         vp[0] = __builtin_amdgcn_perm(vb.x, va.x, 0x05040100u);
         vp[1] = __builtin_amdgcn_perm(vb.x, va.x, 0x07060302u);
@@ -327,12 +316,11 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[g][e] = dot2_bf16(pp, vp[e], o[g][e]);
         }
-        if ((k & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the hoisting of p reads
       }
     } else {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        const int tt = k * TPV + pv_tok;
+        const int tt = k * TPV + v_tok;
         float pp[GP];
 #pragma unroll
         for (int pl = 0; pl < GP / 4; ++pl) {
@@ -342,23 +330,36 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
         }
         float vf[EV];
         if constexpr (BF16) {
-          vf[0] = bf16lo(vreg[k].x);
-          vf[1] = bf16hi(vreg[k].x);
-          vf[2] = bf16lo(vreg[k].y);
-          vf[3] = bf16hi(vreg[k].y);
+          vf[0] = bf16lo(vreg[slot][k].x);
+          vf[1] = bf16hi(vreg[slot][k].x);
+          vf[2] = bf16lo(vreg[slot][k].y);
+          vf[3] = bf16hi(vreg[slot][k].y);
         } else {
-          vf[0] = __uint_as_float(vreg[k].x);
-          vf[1] = __uint_as_float(vreg[k].y);
+          vf[0] = __uint_as_float(vreg[slot][k].x);
+          vf[1] = __uint_as_float(vreg[slot][k].y);
         }
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
           for (int e = 0; e < EV; ++e) o[g][e] = fmaf(pp[g], vf[e], o[g][e]);
-        if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the hoisting of p reads
       }
     }
+  };
 
-    if (has_next) store_k(stage ^ 1);
+  // Three bodies per trip over fixed slots; leaving early exits the loop, so the
+  // latch is only reached after all three and its pending loads always match.
+  if (ntiles > 0) {
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i) issue(i, i, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int it = 0;; it += kRing) {
+      body(it, 0);
+      if (it + 1 >= ntiles) break;
+      body(it + 1, 1);
+      if (it + 2 >= ntiles) break;
+      body(it + 2, 2);
+      if (it + 3 >= ntiles) break;
+    }
   }
 
   // ---- reduce over the lanes that share a D slot, normalise, write the partial
@@ -373,7 +374,8 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
       for (int e = 0; e < EV; ++e) o[g][e] += __shfl_xor(o[g][e], m);
 
   const int rows = a.num_q_heads;
-  float* po = a.part_o + ((int64_t)sg * rows + (int64_t)h * G) * D + wave * (D / 4) + pv_d * EV;
+  const int pv_tok = lane / LPR, pv_d = lane % LPR;
+  float* po = a.part_o + ((int64_t)sg * rows + (int64_t)h * G) * D + wave * (QB / S::ES) + pv_d * EV;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (g % TPV == pv_tok) {
@@ -400,16 +402,17 @@ __global__ __launch_bounds__(256, 2) void draft_splitk_kernel(const SplitArgs a)
 // ----------------------------------------------------------------------------- dispatch
 template <int D, int G, bool BF16>
 static hipError_t launch_dg(bool window, bool dot2, const SplitArgs& a, int grid, hipStream_t st) {
+  constexpr int T = DraftShape<D, G, BF16>::THREADS;
   if (window) {
     if constexpr (BF16) {
-      if (dot2) { draft_splitk_kernel<D, G, BF16, true, true><<<grid, 256, 0, st>>>(a); return hipGetLastError(); }
+      if (dot2) { draft_splitk_kernel<D, G, BF16, true, true><<<grid, T, 0, st>>>(a); return hipGetLastError(); }
     }
-    draft_splitk_kernel<D, G, BF16, true, false><<<grid, 256, 0, st>>>(a);
+    draft_splitk_kernel<D, G, BF16, true, false><<<grid, T, 0, st>>>(a);
   } else {
     if constexpr (BF16) {
-      if (dot2) { draft_splitk_kernel<D, G, BF16, false, true><<<grid, 256, 0, st>>>(a); return hipGetLastError(); }
+      if (dot2) { draft_splitk_kernel<D, G, BF16, false, true><<<grid, T, 0, st>>>(a); return hipGetLastError(); }
     }
-    draft_splitk_kernel<D, G, BF16, false, false><<<grid, 256, 0, st>>>(a);
+    draft_splitk_kernel<D, G, BF16, false, false><<<grid, T, 0, st>>>(a);
   }
   return hipGetLastError();
 }

@@ -50,5 +50,6 @@ hipError_t launch_debug_resolve_paged(const int32_t* bt_row, int32_t row_len, in
 hipError_t launch_debug_resolve_ring(int sink, int window, const int32_t* positions, int n, int32_t* out,
                                      hipStream_t st);
 hipError_t launch_debug_window_positions(int sink, int window, int n, int32_t* out, hipStream_t st);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t st);
 
 }  // namespace wmtp

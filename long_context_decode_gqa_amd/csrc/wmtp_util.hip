@@ -8,15 +8,29 @@ namespace wmtp {
 // Flash-decoding merge of split partials.  A split holding the keys K_i gives
 // (o_i, lse_i); the result over the union is
 //   L = log sum_i exp(lse_i),  o = sum_i exp(lse_i - L) o_i.
-// Workgroup = (sequence b, row r, 16-float slice of D).  Its 256 threads are 4
-// lanes across the slice (16 bytes each) x 64 split lanes; every thread keeps a
-// running (max, weight, acc) over its splits, and the 64 split lanes are merged
-// through LDS at the end.
-constexpr int kCombineDL = 4;                     // lanes across a D slice
+// Workgroup = (sequence b, row r, 32-float slice of D: one 128-byte line per
+// split).  Its 256 threads are 8 lanes across the slice (16 bytes each) x 32
+// split lanes.  Every thread merges its own splits (all loads independent),
+// then the 8 split lanes of a wave are merged with a shuffle tree and the 4
+// waves through LDS.
+constexpr int kCombineDL = 8;                     // lanes across a D slice (128 bytes)
 constexpr int kCombineSL = 256 / kCombineDL;      // split lanes
 
+struct MergeState {
+  float m, w;
+  f32x4 acc;
+};
+
+// Merge (m, w, acc) states that describe disjoint key sets (log2 domain).
+__device__ __forceinline__ MergeState merge_state(const MergeState& x, const MergeState& y) {
+  const float m = fmaxf(x.m, y.m);
+  if (m == kNegInf) return x;
+  const float fx = exp2f(x.m - m), fy = exp2f(y.m - m);
+  return {m, x.w * fx + y.w * fy, x.acc * fx + y.acc * fy};
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  __shared__ float sm[kCombineSL][kCombineDL][6];
+  __shared__ MergeState sm[4][kCombineDL];
   const int slices = a.head_dim / (4 * kCombineDL);
   const int slice = blockIdx.x % slices;
   const int br = blockIdx.x / slices;             // b * rows + r
@@ -27,58 +41,52 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int s0 = a.split_base[b], s1 = a.split_base[b + 1];
   const int d0 = slice * 4 * kCombineDL + dl * 4;
 
-  float m = kNegInf, w = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = s0 + sl; s < s1; s += kCombineSL) {
-    const float ls = a.part_lse[(int64_t)s * a.rows + r] * kLog2e;
-    if (ls == kNegInf) continue;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)s * a.rows + r) * a.head_dim + d0);
-    if (ls > m) {
-      const float c = exp2f(m - ls);          // m = -inf gives 0
-      acc *= c;
-      w *= c;
-      m = ls;
+  // Two passes over this thread's splits with independent loads: first the
+  // maximum lse, then the weighted sum.  Empty splits carry lse = -inf and
+  // o = 0, so they add exactly nothing.
+  MergeState st;
+  st.m = kNegInf;
+#pragma unroll 8
+  for (int s = s0 + sl; s < s1; s += kCombineSL) st.m = fmaxf(st.m, a.part_lse[(int64_t)s * a.rows + r] * kLog2e);
+  st.w = 0.f;
+  st.acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (st.m != kNegInf) {
+#pragma unroll 4
+    for (int s = s0 + sl; s < s1; s += kCombineSL) {
+      const float e = exp2f(a.part_lse[(int64_t)s * a.rows + r] * kLog2e - st.m);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)s * a.rows + r) * a.head_dim + d0);
+      st.acc += e * x;
+      st.w += e;
     }
-    const float e = exp2f(ls - m);
-    acc += e * x;
-    w += e;
   }
-  sm[sl][dl][0] = m;
-  sm[sl][dl][1] = w;
-  sm[sl][dl][2] = acc[0];
-  sm[sl][dl][3] = acc[1];
-  sm[sl][dl][4] = acc[2];
-  sm[sl][dl][5] = acc[3];
+  // shuffle tree over the 16 split lanes of this wave (lane = 4 sl + dl)
+#pragma unroll
+  for (int m = kCombineDL; m < 64; m <<= 1) {
+    MergeState o;
+    o.m = __shfl_xor(st.m, m);
+    o.w = __shfl_xor(st.w, m);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o.acc[e] = __shfl_xor(st.acc[e], m);
+    st = merge_state(st, o);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) < kCombineDL) sm[wave][dl] = st;
   __syncthreads();
-  if (sl != 0) return;
-  float M = kNegInf;
-  for (int i = 0; i < kCombineSL; ++i) M = fmaxf(M, sm[i][dl][0]);
-  float W = 0.f;
-  f32x4 A = {0.f, 0.f, 0.f, 0.f};
-  if (M != kNegInf) {
-    for (int i = 0; i < kCombineSL; ++i) {
-      const float mi = sm[i][dl][0];
-      if (mi == kNegInf) continue;
-      const float c = exp2f(mi - M);
-      W += c * sm[i][dl][1];
-      A[0] += c * sm[i][dl][2];
-      A[1] += c * sm[i][dl][3];
-      A[2] += c * sm[i][dl][4];
-      A[3] += c * sm[i][dl][5];
-    }
-  }
-  const float inv = W > 0.f ? 1.f / W : 0.f;
+  if (threadIdx.x >= kCombineDL) return;
+  MergeState t = sm[0][dl];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) t = merge_state(t, sm[w][dl]);
+  const float inv = t.w > 0.f ? 1.f / t.w : 0.f;
   const int64_t orow = ((int64_t)b * a.rows + r) * a.head_dim + d0;
   if (a.out_bf16) {
     uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<__bf16*>(a.out) + orow);
-    o[0] = pack_bf16x2(A[0] * inv, A[1] * inv);
-    o[1] = pack_bf16x2(A[2] * inv, A[3] * inv);
+    o[0] = pack_bf16x2(t.acc[0] * inv, t.acc[1] * inv);
+    o[1] = pack_bf16x2(t.acc[2] * inv, t.acc[3] * inv);
   } else {
-    f32x4 res = A * inv;
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow) = res;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow) = t.acc * inv;
   }
   if (a.lse_out && slice == 0 && dl == 0)
-    a.lse_out[(int64_t)b * a.rows + r] = W > 0.f ? (M + __log2f(W)) * kLn2 : kNegInf;
+    a.lse_out[(int64_t)b * a.rows + r] = t.w > 0.f ? (t.m + __log2f(t.w)) * kLn2 : kNegInf;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {

@@ -9,10 +9,13 @@
 // v_mfma_f32_32x32x16_bf16.
 //
 // Work item = (sequence, KV head, split of `chunk` keys); one 256-thread
-// workgroup whose 4 waves each own a quarter of head_dim.  Per 32-key tile:
+// workgroup whose 4 waves each own a quarter of head_dim.  Each wave keeps a
+// 3-slot register ring of K/V tiles, so two tiles are in flight while a third
+// is computed.  Per 32-key tile:
 //   S^T = K Q^T     each wave contracts its quarter of D: A = its quarter of
-//                   the K rows from a swizzled wave-private LDS stage (lane =
-//                   key), B = its quarter of Q^T held in registers.  The 4
+//                   the K rows, moved from registers into a swizzled
+//                   wave-private LDS stage and read back with lane = key,
+//                   B = its quarter of Q^T held in registers.  The 4
 //                   partial score tiles are summed through LDS (one barrier per
 //                   tile), so every wave holds the full scores: lane l has
 //                   packed row l % 32 for 16 keys.
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
   constexpr int ROWB = kVD * 2;
   constexpr float TAU = 8.0f;
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[4 * 2 * kVStage];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[4 * kVStage];
   __shared__ __attribute__((aligned(16))) float sc_lds[2 * 4 * 16 * 64];   // [buf][wave][r/4][lane][4]
 
   const int lane = threadIdx.x & 63;
@@ -91,9 +94,13 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
       if (j < rows) x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + wave * (kVQ * 2) + (2 * s + kh) * 16);
       qreg[s] = x;
     }
+    // Settle the query loads here, so no load issued before the main loop is
+    // still pending at its header (which would force a full drain per tile).
+#pragma unroll
+    for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(qreg[s]));
   }
 
-  uint8_t* my_k = k_lds + wave * 2 * kVStage;
+  uint8_t* my_k = k_lds + wave * kVStage;
 
   // byte offsets of the two (block, head) runs of 16 keys covering a tile
   auto tile_runs = [&](int t0, int64_t (&run)[2]) {
@@ -104,36 +111,34 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
     }
   };
 
-  u32x4 kreg[kVLoads];
-  uint32_t vreg[2][8], vnext[2][8];
+  // Register ring: tile i's K and V arrive in slot i % kRing, issued kRing - 1
+  // tiles ahead, so two tiles per wave are in flight while one is computed.
+  constexpr int kRing = 3;
+  u32x4 kreg[kRing][kVLoads];
+  uint32_t vreg[kRing][2][8];
 
   // K quarter tile: load l of a lane covers stage piece P = 64 l + lane, i.e. key
   // P / 8, piece P % 8; its 8 keys share one 16-key block (uniform base).
-  auto load_k = [&](const int64_t (&run)[2]) {
+  // Tiles past the end re-load the last tile (never consumed), so every body
+  // issues the same loads and the loop has no load-carrying branch.
+  auto issue = [&](int it, int slot) {
+    const int t0 = t_begin + min(it, ntiles - 1) * kVTile;
+    int64_t run[2];
+    tile_runs(t0, run);
 #pragma unroll
     for (int l = 0; l < kVLoads; ++l) {
       const int P = 64 * l + lane;
       const int i = P / kVNQ, pp = P % kVNQ;
-      kreg[l] = load_at<u32x4>(kbase + run[(64 * l / kVNQ) >> 4], (uint32_t)((i & 15) * ROWB + pp * 16));
+      kreg[slot][l] = load_at<u32x4>(kbase + run[(64 * l / kVNQ) >> 4], (uint32_t)((i & 15) * ROWB + pp * 16));
     }
-  };
-  auto store_k = [&](int stage) {
-    uint8_t* dst = my_k + stage * kVStage;
-#pragma unroll
-    for (int l = 0; l < kVLoads; ++l) {
-      const int P = 64 * l + lane;
-      *reinterpret_cast<u32x4*>(dst + vpiece(P / kVNQ, P % kVNQ) * 16) = kreg[l];
-    }
-  };
-  // V: element jj (0..7) of k-step ks for this lane's half is key 16ks + 8(jj/4) + 4kh + jj%4;
-  // the lane holds d = 2 c32, 2 c32 + 1 of the wave's quarter (one dword).
-  auto load_v = [&](const int64_t (&run)[2], uint32_t (&dst)[2][8]) {
+    // V: element jj (0..7) of k-step ks for this lane's half is key 16ks + 8(jj/4) + 4kh + jj%4;
+    // the lane holds d = 2 c32, 2 c32 + 1 of the wave's quarter (one dword).
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int tt = 8 * (jj >> 2) + 4 * kh + (jj & 3);   // key within block ks
-        dst[ks][jj] = load_at<uint32_t>(vbase + run[ks], (uint32_t)(tt * ROWB + c32 * 4));
+        vreg[slot][ks][jj] = load_at<uint32_t>(vbase + run[ks], (uint32_t)(tt * ROWB + c32 * 4));
       }
   };
 
@@ -146,35 +151,28 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
   const int row_limit = n - tq + c32 / G;     // last key packed row c32 may see
   const bool row_live = c32 < rows;
 
-  if (ntiles > 0) {
-    int64_t run[2];
-    tile_runs(t_begin, run);
-    load_k(run);
-    load_v(run, vreg);
-    store_k(0);
-  }
-  for (int it = 0; it < ntiles; ++it) {
+  auto body = [&](int it, int slot) {
     const int t0 = t_begin + it * kVTile;
-    const int stage = it & 1;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) {
-      int64_t run[2];
-      tile_runs(t0 + kVTile, run);
-      load_k(run);
-      load_v(run, vnext);
-    }
+    issue(it + kRing - 1, (slot + kRing - 1) % kRing);
+    // Keep the loads in issue order at the top of the body: the load order at
+    // the loop latch then matches the prologue's and the wait counts stay exact.
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- partial S^T[key][row] over this wave's quarter of D
+    // ---- K of this tile -> swizzled LDS stage, then partial S^T over this wave's quarter of D
+#pragma unroll
+    for (int l = 0; l < kVLoads; ++l) {
+      const int P = 64 * l + lane;
+      *reinterpret_cast<u32x4*>(my_k + vpiece(P / kVNQ, P % kVNQ) * 16) = kreg[slot][l];
+    }
     f32x16 sacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-    const uint8_t* kst = my_k + stage * kVStage;
 #pragma unroll
     for (int s = 0; s < kVKS; ++s) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + vpiece(c32, 2 * s + kh) * 16);
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(my_k + vpiece(c32, 2 * s + kh) * 16);
       sacc = mfma32(ka, qreg[s], sacc);
     }
-    float* sc = sc_lds + stage * (4 * 16 * 64);
+    float* sc = sc_lds + (it & 1) * (4 * 16 * 64);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 w4 = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
@@ -234,17 +232,26 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
         u32x4 vb;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          vb[q] = __builtin_amdgcn_perm(vreg[ks][2 * q + 1], vreg[ks][2 * q], e ? 0x07060302u : 0x05040100u);
+          vb[q] = __builtin_amdgcn_perm(vreg[slot][ks][2 * q + 1], vreg[slot][ks][2 * q],
+                                        e ? 0x07060302u : 0x05040100u);
         O[e] = mfma32(pa, vb, O[e]);
       }
     }
+  };
 
-    if (has_next) {
-      store_k(stage ^ 1);
+  // Three bodies per trip over fixed slots; leaving early exits the loop, so the
+  // latch is only reached after all three and its pending loads always match.
+  if (ntiles > 0) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) vreg[ks][jj] = vnext[ks][jj];
+    for (int i = 0; i < kRing - 1; ++i) issue(i, i);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int it = 0;; it += kRing) {
+      body(it, 0);
+      if (it + 1 >= ntiles) break;
+      body(it + 1, 1);
+      if (it + 2 >= ntiles) break;
+      body(it + 2, 2);
+      if (it + 3 >= ntiles) break;
     }
   }
 

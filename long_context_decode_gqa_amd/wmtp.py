@@ -59,7 +59,8 @@ class Partials(ctypes.Structure):
 EXPORTS = (
     "wmtp_draft_workspace_bytes", "wmtp_verify_workspace_bytes", "wmtp_draft_attn", "wmtp_verify_attn",
     "wmtp_combine", "wmtp_ring_append", "wmtp_paged_append", "wmtp_debug_resolve_paged",
-    "wmtp_debug_resolve_ring", "wmtp_debug_window_positions", "wmtp_status_str", "wmtp_version",
+    "wmtp_debug_resolve_ring", "wmtp_debug_window_positions", "wmtp_stream_read", "wmtp_status_str",
+    "wmtp_version",
 )
 
 _lib = None
@@ -96,6 +97,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.wmtp_debug_resolve_ring.restype = ctypes.c_int
     lib.wmtp_debug_window_positions.argtypes = [I32, I32, I32, P, P]
     lib.wmtp_debug_window_positions.restype = ctypes.c_int
+    lib.wmtp_stream_read.argtypes = [P, I64, P, I32, P]
+    lib.wmtp_stream_read.restype = ctypes.c_int
     lib.wmtp_status_str.argtypes = [ctypes.c_int]
     lib.wmtp_status_str.restype = ctypes.c_char_p
     lib.wmtp_version.argtypes = []
@@ -230,6 +233,12 @@ def debug_window_positions(sink: int, window: int, n: int, device, stream=None) 
     _check("wmtp_debug_window_positions", load().wmtp_debug_window_positions(
         sink, window, n, out.data_ptr(), _stream(stream)))
     return out
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=None) -> None:
+    """Read all of `src` once (bandwidth probe); sink: int32/uint32 [workgroups * 256]."""
+    _check("wmtp_stream_read", load().wmtp_stream_read(
+        src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), workgroups, _stream(stream)))
 
 
 def version() -> str:

@@ -207,6 +207,15 @@ def test_append_checks():
     assert lib.wmtp_paged_append(ctypes.byref(sh), None, FAKE, FAKE, lens(0), 1, 1, None) == W.EINVAL
 
 
+def test_stream_read_checks():
+    lib = W.load()
+    assert lib.wmtp_stream_read(None, 1024, FAKE, 4, None) == W.EINVAL
+    assert lib.wmtp_stream_read(FAKE, 8, FAKE, 4, None) == W.EINVAL
+    assert lib.wmtp_stream_read(FAKE, 1024, FAKE, 0, None) == W.EINVAL
+    assert lib.wmtp_stream_read(FAKE_ODD, 1024, FAKE, 4, None) == W.EALIGN
+    assert lib.wmtp_stream_read(FAKE, 1000, FAKE, 4, None) == W.EALIGN
+
+
 def test_debug_hook_checks():
     lib = W.load()
     kv = paged()
