@@ -39,18 +39,24 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # HBM bytes per verify launch at the 1M-token workload, from rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by the factors a plain
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
-# for the kernel sources they were taken with (sha256 below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "9b29d52b24f46ac05df163c0e8325c0aa8320dda035fc2113e705bc3df89bc13",
-                  "fetch_kib": 1049371.55, "write_kib": 16512.25, "fetch_factor": 2.0, "write_factor": 1.0}
+# for the kernel code they were taken with (sha256 of the sources without
+# comments and whitespace, below); otherwise null.
+VERIFY_TRAFFIC = {"sources_sha256": "7abbd80f229cb7437e21272986349cba653bbd7acdbd9a03e16ee5b3ae398509",
+                  "fetch_kib": 1049332.24, "write_kib": 8224.0, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
 
 def verify_sources_sha256() -> str:
+    """sha256 of the verify kernel's sources with comments and whitespace removed."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in VERIFY_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
@@ -65,7 +71,7 @@ def stream_ceiling_gbps(dev, nbytes=2 << 30):
     """Best rate of the library's streaming-read probe over a 2 GiB buffer."""
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
     best = 0.0
-    for wgs in (2048, 4096):
+    for wgs in (256, 512, 1024, 2048):
         sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
         for _ in range(3):
             W.stream_read(src, sink, wgs)
@@ -207,13 +213,26 @@ def time_steps(step, mode, flag, steps, warmup):
     return total_ms / steps, float(np.mean(ver_ms)), float(np.mean(draft_ms))
 
 
-def cpu_baseline(wl, n0):
+def _per_rep(fn, budget_s):
+    """Mean seconds per call of fn(rep), repeating until `budget_s` has passed (at least once)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn(reps)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return el / reps, reps, el
+
+
+def cpu_baseline(wl, n0, budget_s=12.0):
     """The float64 oracle on a bounded sample, scaled to one decode step (both draft modes).
 
-    Sample: one verify layer over all n0 + gamma + 1 keys for one KV head (4
-    causal queries x G heads), one native draft step over n0 + 1 keys for the
-    same head, and one windowed draft step; scaled by KV heads, target layers and
-    draft steps.  Values are synthetic bf16 keys and values.
+    Sample, for one KV head: verify layers over all n0 + gamma + 1 keys (gamma + 1
+    causal queries x G heads, a fresh query set each repetition), native draft
+    steps over n0 + 1 keys and windowed draft steps over the sink + window
+    entries, each repeated until its share of `budget_s` (3/4, 1/5, the rest)
+    has passed; the mean per repetition is scaled by KV heads, target layers and
+    draft steps.  Keys and values are synthetic bf16.
     """
     import oracle as O
     try:
@@ -228,18 +247,18 @@ def cpu_baseline(wl, n0):
     vb = torch.from_numpy(rng.standard_normal((n, 1, D), dtype=np.float32) * 0.5).to(torch.bfloat16)
     src_k = O.LogicalKV(kb.view(torch.int16).numpy().view(np.uint16), "bf16")
     src_v = O.LogicalKV(vb.view(torch.int16).numpy().view(np.uint16), "bf16")
-    q = rng.standard_normal((g + 1, G, D))
-    t0 = time.perf_counter()
-    for i in range(g + 1):                         # one verify layer, one KV head
-        O.attention_over(q[i], src_k, src_v, np.arange(n0 + i + 1), 0, wl.scale)
-    t_verify = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.attention_over(q[0], src_k, src_v, np.arange(n0 + 1), 0, wl.scale)
-    t_native = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.attention_over(q[0], src_k, src_v, O.visible_positions(n0 + 1, O.SINK_WINDOW, wl.sink, wl.window), 0,
-                     wl.scale)
-    t_win = time.perf_counter() - t0
+    qs = rng.standard_normal((4, g + 1, G, D))
+    win = O.visible_positions(n0 + 1, O.SINK_WINDOW, wl.sink, wl.window)
+
+    def verify_layer(r):
+        for i in range(g + 1):
+            O.attention_over(qs[r % 4, i], src_k, src_v, np.arange(n0 + i + 1), 0, wl.scale)
+
+    t_verify, r_v, e_v = _per_rep(verify_layer, 0.75 * budget_s)
+    t_native, r_n, e_n = _per_rep(
+        lambda r: O.attention_over(qs[r % 4, 0], src_k, src_v, np.arange(n0 + 1), 0, wl.scale), 0.2 * budget_s)
+    t_win, r_w, e_w = _per_rep(
+        lambda r: O.attention_over(qs[r % 4, 0], src_k, src_v, win, 0, wl.scale), 0.05 * budget_s)
     Hk, L = wl.num_kv_heads, wl.target_layers
     verify_step = t_verify * Hk * L
     return {
@@ -248,10 +267,10 @@ def cpu_baseline(wl, n0):
         "native_value": round((verify_step + t_native * Hk * g) * 1e6, 1),
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"float64 oracle on 1 KV head: one verify layer ({g + 1} causal queries x {G} heads over "
-                   f"{n} keys), one native draft step ({n0 + 1} keys) and one windowed draft step "
-                   f"({wl.sink}+{wl.window} entries); scaled x{Hk} KV heads, x{L} target layers, x{g} draft steps; "
-                   f"measured {t_verify + t_native + t_win:.1f} s"),
+        "sample": (f"float64 oracle on 1 KV head: {r_v} verify layer(s) ({g + 1} causal queries x {G} heads over "
+                   f"{n} keys), {r_n} native draft step(s) ({n0 + 1} keys), {r_w} windowed draft step(s) "
+                   f"({wl.sink}+{wl.window} entries); mean per repetition scaled x{Hk} KV heads, x{L} target "
+                   f"layers, x{g} draft steps; measured {e_v + e_n + e_w:.1f} s"),
     }
 
 
@@ -342,7 +361,7 @@ def main():
             "draft_native_per_step": round(dnat_ms * 1e3, 2),
         },
         "roofline": {
-            "kernel": "verify_kernel<8> (10 launches per step)",
+            "kernel": "mfma_attn_kernel<8, false> (verify, 10 launches per step)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -76,9 +76,12 @@ extern "C" {
 #define WMTP_FULL         0     /* native MTP draft: every cached entry                       */
 #define WMTP_SINK_WINDOW  1     /* Windowed-MTP draft: sink + window entries from the ring     */
 /* Optional flag OR-ed into the draft mode (bf16 only): the PV product takes the
- * softmax weights rounded to bf16 and uses v_dot2_f32_bf16 over key pairs
- * instead of fp32 FMAs.  The normaliser is summed from the same rounded
- * weights.  Without it the PV product uses the fp32 weights. */
+ * softmax weights rounded to bf16 (bf16 x bf16 products, fp32 sums) instead of
+ * fp32 weights.  The normaliser is summed from the same rounded weights.  With
+ * this flag, WMTP_FULL and head_dim 256 run on the matrix-core kernel of
+ * wmtp_verify_attn with one query token (the same arithmetic); other shapes use
+ * v_dot2_f32_bf16 over key pairs.  Without it the PV product uses the fp32
+ * weights. */
 #define WMTP_DRAFT_FAST_PV 0x10
 
 #define WMTP_MAX_BATCH   64     /* sequences per call                                         */
@@ -150,7 +153,10 @@ int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const 
  *                            positions are ignored.
  *  n_b = seq_lens_host[b] (host) is the length after this step's own entry was
  *  appended, so the query attends to itself.  q: device [batch][H_q][D].
- *  chunk_tokens: entries per split (a multiple of 64; 0 = library default).
+ *  chunk_tokens: entries per split (a multiple of 64).  0 = library default:
+ *  in WMTP_FULL mode, the keys of the whole batch times H_kv divided over 256
+ *  work items (one per MI355X compute unit), rounded up to a multiple of 64 and
+ *  clamped to [256, 65536]; in WMTP_SINK_WINDOW mode, 64.
  *  The call writes split partials into `workspace` (device, >= the size from
  *  wmtp_draft_workspace_bytes, 256-byte aligned) and describes them in
  *  *parts (host).  Finish with wmtp_combine. */
@@ -165,7 +171,8 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
  *  query tokens' own entries; query token i attends causally to positions
  *  0..n_b-t_q+i.  Requires t_q * G <= WMTP_MAX_VERIFY_ROWS, dtype bf16 and
  *  head_dim 256 (other shapes return WMTP_EUNSUPPORTED).
- *  split_tokens: entries per split (a multiple of 32; 0 = library default).
+ *  split_tokens: entries per split (a multiple of 32; 0 = the WMTP_FULL draft
+ *  default, one work item per compute unit).
  *  Workspace and *parts as for wmtp_draft_attn. */
 int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv,
                      const int32_t* seq_lens_host, int32_t batch, int32_t split_tokens,

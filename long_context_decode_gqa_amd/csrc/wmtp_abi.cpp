@@ -16,11 +16,26 @@ using namespace wmtp;
 
 namespace {
 
-constexpr int kDraftDefaultChunkFull = 4096;
 constexpr int kDraftDefaultChunkWindow = 64;
-constexpr int kVerifyDefaultSplit = 4096;
 constexpr int kDraftTile = 64;
 constexpr int kVerifyTile = 32;    // keys per verify tile
+
+// Default split of the full-context kernels: one work item per compute unit
+// (MI355X has 256), so every CU streams one long run of blocks; measured faster
+// than two co-resident work items per CU at 1M keys.  Clamped so that short
+// contexts still get several splits and long ones a bounded combine.
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kMinDefaultSplit = 256;
+constexpr int64_t kMaxDefaultSplit = 65536;
+
+int32_t default_split(const int32_t* seq_lens, int batch, int kv_heads) {
+  int64_t keys = 0;
+  for (int b = 0; b < batch; ++b) keys += seq_lens[b] > 0 ? seq_lens[b] : 0;
+  int64_t s = (keys * kv_heads + kComputeUnits - 1) / kComputeUnits;
+  s = (s + kDraftTile - 1) / kDraftTile * kDraftTile;   // a multiple of both tiles
+  s = s < kMinDefaultSplit ? kMinDefaultSplit : s;
+  return (int32_t)(s > kMaxDefaultSplit ? kMaxDefaultSplit : s);
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -89,7 +104,8 @@ int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, i
   if (base_mode != WMTP_FULL && base_mode != WMTP_SINK_WINDOW) return WMTP_EINVAL;
   if ((mode & ~0xF) & ~WMTP_DRAFT_FAST_PV) return WMTP_EINVAL;
   if (!seq_lens || batch < 1 || batch > WMTP_MAX_BATCH) return WMTP_EINVAL;
-  if (chunk == 0) chunk = base_mode == WMTP_FULL ? kDraftDefaultChunkFull : kDraftDefaultChunkWindow;
+  if (chunk == 0)
+    chunk = base_mode == WMTP_FULL ? default_split(seq_lens, batch, shape->num_kv_heads) : kDraftDefaultChunkWindow;
   if (chunk < kDraftTile || chunk % kDraftTile != 0) return WMTP_EINVAL;
   if (base_mode == WMTP_SINK_WINDOW && (sink < 0 || window < 1)) return WMTP_EINVAL;
   int64_t vis[WMTP_MAX_BATCH];
@@ -110,7 +126,7 @@ int verify_plan(const wmtp_shape* shape, int32_t t_q, const int32_t* seq_lens, i
   if (t_q < 1) return WMTP_EINVAL;
   const int g = shape->num_q_heads / shape->num_kv_heads;
   if ((int64_t)t_q * g > WMTP_MAX_VERIFY_ROWS) return WMTP_EUNSUPPORTED;
-  if (split == 0) split = kVerifyDefaultSplit;
+  if (split == 0) split = default_split(seq_lens, batch, shape->num_kv_heads);
   if (split < kVerifyTile || split % kVerifyTile != 0) return WMTP_EINVAL;
   int64_t vis[WMTP_MAX_BATCH];
   for (int b = 0; b < batch; ++b) {
@@ -216,6 +232,15 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
   }
   const int grid = p.total * shape->num_kv_heads;
   const bool fast_pv = (mode & WMTP_DRAFT_FAST_PV) != 0 && shape->dtype == WMTP_BF16;
+  if (base_mode == WMTP_FULL && fast_pv && shape->head_dim == 256) {
+    // The native draft is full-context attention of a single query token, i.e.
+    // the verify contraction with t_q = 1; both round p to bf16 before PV, so the
+    // G packed rows run on the matrix-core kernel, which spends fewer vector
+    // instructions per key than the dot-product kernel.
+    a.t_q = 1;
+    return launch_status(launch_verify(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, true, a, grid,
+                                       static_cast<hipStream_t>(stream)));
+  }
   return launch_status(launch_draft(shape->dtype, shape->head_dim, shape->num_q_heads / shape->num_kv_heads,
                                     base_mode == WMTP_SINK_WINDOW, fast_pv, a, grid,
                                     static_cast<hipStream_t>(stream)));
@@ -250,7 +275,7 @@ int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const 
   a.max_block = kv->num_blocks - 1;
   a.t_q = t_q;
   const int grid = p.total * shape->num_kv_heads;
-  return launch_status(launch_verify(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, a, grid,
+  return launch_status(launch_verify(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, false, a, grid,
                                      static_cast<hipStream_t>(stream)));
 }
 

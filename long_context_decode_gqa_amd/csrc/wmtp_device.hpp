@@ -17,6 +17,7 @@ namespace wmtp {
 
 // ----------------------------------------------------------------------------- vector types
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -127,8 +128,8 @@ __device__ __forceinline__ float round_bf16(float x) {
 
 // Two fp32 values -> packed bf16x2 (RNE), `lo` in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));   // one v_cvt_pk_bf16_f32
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -147,6 +148,24 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
   return x;
 }
+
+// max / sum of lane l and lane l ^ 32 (gfx950 v_permlane32_swap: a VALU swap
+// of the two 32-lane halves, no LDS round trip).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 2^x on the hardware exponential (v_exp_f32): exp2(-inf) = 0; results below
+// the fp32 normal range flush to zero, far below what a softmax weight of a
+// kept row can contribute.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr uint32_t kBf16One2 = 0x3f803f80u;   // bf16 pair (1, 1)
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.69314718055994530942f;

@@ -1,12 +1,15 @@
-// Full-context verify attention of the target on gfx950 matrix cores.
+// Full-context attention of a few query tokens on gfx950 matrix cores: the
+// target's verify of the gamma+1 drafted positions, and the native draft step
+// (one query token over the whole cache).
 //
-// The target keeps full attention while it verifies the gamma+1 drafted
-// positions ("Windowed-MTP: Removing the Full-Context Draft-KV Tax at
-// Million-Token Context", arxivlens summary, Abstract; howtospark case study,
-// Method: one batched verify per cycle).  Per KV head the t_q query tokens x G
-// query heads form up to 32 packed rows, so QK^T and PV are real dense
-// contractions (32 rows x head_dim against each key tile) and run on
-// v_mfma_f32_32x32x16_bf16.
+// The target keeps full attention while it verifies the drafted positions
+// ("Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token
+// Context", arxivlens summary, Abstract; howtospark case study, Method: one
+// batched verify per cycle).  Per KV head the t_q query tokens x G query heads
+// form up to 32 packed rows, so QK^T and PV are real dense contractions (rows x
+// head_dim against each key tile) and run on v_mfma_f32_32x32x16_bf16.  With
+// t_q = 1 this is the native MTP draft step, whose read grows with the context
+// (same summary, Abstract).
 //
 // Work item = (sequence, KV head, split of `chunk` keys); one 256-thread
 // workgroup whose 4 waves each own a quarter of head_dim.  Each wave keeps a
@@ -19,10 +22,12 @@
 //                   partial score tiles are summed through LDS (one barrier per
 //                   tile), so every wave holds the full scores: lane l has
 //                   packed row l % 32 for 16 keys.
-//   softmax         row max over 16 registers + the partner half-wave; causal
-//                   mask for query token i: key <= n - t_q + i; lazy running
-//                   maximum (rescale only on a 2^8 jump).  Identical in all
-//                   waves, so the waves share one softmax state.
+//   softmax         row max over 16 registers and the partner half-wave
+//                   (v_permlane32_swap); causal mask for query token i: key <=
+//                   n - t_q + i, applied only on tiles that reach a boundary;
+//                   lazy running maximum (rescale only on a 2^8 jump); the
+//                   score scale folds into the exponent, p = 2^(s c - M).
+//                   Identical in all waves, so the waves share one state.
 //   O += P V        A = P straight from the score accumulator (bf16); B = V of
 //                   the wave's quarter of D, 2 values per lane and key,
 //                   regrouped into key pairs with v_perm_b32.
@@ -54,8 +59,10 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 
 }  // namespace
 
-template <int G>
-__global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
+// SINGLE: one query token (t_q = 1, the native full-context draft step);
+// otherwise t_q comes from the arguments.
+template <int G, bool SINGLE>
+__global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
   constexpr int ROWB = kVD * 2;
   constexpr float TAU = 8.0f;
 
@@ -64,7 +71,7 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, tq = a.t_q;
+  const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, tq = SINGLE ? 1 : a.t_q;
   const int rows = tq * G;
   const int h = blockIdx.x % Hkv;
   const int sg = blockIdx.x / Hkv;
@@ -101,9 +108,19 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
   }
 
   uint8_t* my_k = k_lds + wave * kVStage;
+  const float c = a.scale_log2;
+  // Last key packed row c32 may see in this split (query token c32 / G is causal
+  // at n - t_q + c32 / G), and the last key every row sees: only tiles reaching
+  // past the latter need a mask.  Padding rows (c32 >= rows) have zero queries
+  // and are never written, so they are left unmasked.
+  const int row_last = min(n - tq + c32 / G, t_end - 1);
+  const int all_last = min(n - tq, t_end - 1);
 
-  // byte offsets of the two (block, head) runs of 16 keys covering a tile
-  auto tile_runs = [&](int t0, int64_t (&run)[2]) {
+  // Byte offsets of the two (block, head) runs of 16 keys covering tile `it`
+  // (clamped to the split's last tile and block).  The block ids come in through
+  // scalar loads one tile before the loads that use them.
+  auto tile_runs = [&](int it, int64_t (&run)[2]) {
+    const int t0 = t_begin + min(it, ntiles - 1) * kVTile;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int bi = min((t0 >> 4) + j, last_blk_idx);
@@ -116,30 +133,30 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
   constexpr int kRing = 3;
   u32x4 kreg[kRing][kVLoads];
   uint32_t vreg[kRing][2][8];
+  int64_t run_next[2];
 
   // K quarter tile: load l of a lane covers stage piece P = 64 l + lane, i.e. key
-  // P / 8, piece P % 8; its 8 keys share one 16-key block (uniform base).
+  // 8 l + lane / 8, piece lane % 8: loads 0, 1 read block run 0 and loads 2, 3
+  // run 1, at lane offset k_off (+ 4 KiB for odd l).
+  // V: element jj (0..7) of k-step ks for this lane's half is key 16 ks + 8 (jj / 4)
+  // + 4 kh + jj % 4 (block run ks); the lane holds d = 2 c32, 2 c32 + 1 of the
+  // wave's quarter (one dword), at lane offset v_off + (8 (jj / 4) + jj % 4) rows.
   // Tiles past the end re-load the last tile (never consumed), so every body
-  // issues the same loads and the loop has no load-carrying branch.
-  auto issue = [&](int it, int slot) {
-    const int t0 = t_begin + min(it, ntiles - 1) * kVTile;
-    int64_t run[2];
-    tile_runs(t0, run);
+  // issues the same loads and the loop has no load-carrying branch.  The two
+  // 32-bit lane offsets are passed opaque, so they are not widened and hoisted
+  // but feed the "uniform base + 32-bit offset" load form directly.
+  const uint32_t k_off0 = (uint32_t)((lane >> 3) * ROWB + (lane & 7) * 16);
+  const uint8_t* kbase_hi = kbase + 8 * ROWB;
+  const uint32_t v_off0 = (uint32_t)(4 * kh * ROWB + c32 * 4);
+  auto issue = [&](int slot, const int64_t (&run)[2], uint32_t k_off, uint32_t v_off) {
 #pragma unroll
-    for (int l = 0; l < kVLoads; ++l) {
-      const int P = 64 * l + lane;
-      const int i = P / kVNQ, pp = P % kVNQ;
-      kreg[slot][l] = load_at<u32x4>(kbase + run[(64 * l / kVNQ) >> 4], (uint32_t)((i & 15) * ROWB + pp * 16));
-    }
-    // V: element jj (0..7) of k-step ks for this lane's half is key 16ks + 8(jj/4) + 4kh + jj%4;
-    // the lane holds d = 2 c32, 2 c32 + 1 of the wave's quarter (one dword).
+    for (int l = 0; l < kVLoads; ++l)
+      kreg[slot][l] = load_at<u32x4>(((l & 1) ? kbase_hi : kbase) + run[l >> 1], k_off);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int tt = 8 * (jj >> 2) + 4 * kh + (jj & 3);   // key within block ks
-        vreg[slot][ks][jj] = load_at<uint32_t>(vbase + run[ks], (uint32_t)(tt * ROWB + c32 * 4));
-      }
+      for (int jj = 0; jj < 8; ++jj)
+        vreg[slot][ks][jj] = load_at<uint32_t>(vbase + run[ks] + (8 * (jj >> 2)) * ROWB, v_off + (jj & 3) * ROWB);
   };
 
   f32x16 O[2];
@@ -147,13 +164,15 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
   for (int e = 0; e < 2; ++e)
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[e][r] = 0.f;
+  // Running maximum M of row c32 in scaled log2 units (scores times c); both
+  // halves of the wave hold the same M for a row.
   float M = kNegInf, l_lane = 0.f;
-  const int row_limit = n - tq + c32 / G;     // last key packed row c32 may see
-  const bool row_live = c32 < rows;
 
   auto body = [&](int it, int slot) {
+    uint32_t k_off = k_off0, v_off = v_off0;
+    asm volatile("" : "+v"(k_off), "+v"(v_off));
     const int t0 = t_begin + it * kVTile;
-    issue(it + kRing - 1, (slot + kRing - 1) % kRing);
+    issue((slot + kRing - 1) % kRing, run_next, k_off, v_off);
     // Keep the loads in issue order at the top of the body: the load order at
     // the loop latch then matches the prologue's and the wait counts stay exact.
     __builtin_amdgcn_sched_barrier(0);
@@ -181,29 +200,34 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
     __syncthreads();
     float s2[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s2[r] = 0.f;
+    for (int q = 0; q < 4; ++q) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(sc + (q * 64 + lane) * 4);
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+      for (int w = 1; w < 4; ++w) x += *reinterpret_cast<const f32x4*>(sc + ((w * 4 + q) * 64 + lane) * 4);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(sc + ((w * 4 + q) * 64 + lane) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s2[4 * q + e] += x[e];
-      }
-
-    // ---- scale, mask, lazy row maximum
-    float mx = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = t0 + 8 * (r >> 2) + 4 * kh + (r & 3);
-      const bool ok = row_live && key < t_end && key <= row_limit;
-      s2[r] = ok ? s2[r] * a.scale_log2 : kNegInf;
-      mx = fmaxf(mx, s2[r]);
+      for (int e = 0; e < 4; ++e) s2[4 * q + e] = x[e];
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Block ids of the tile the next body issues: scalar loads placed after the
+    // last LDS wait of this body, so they complete behind the softmax and PV.
+    __builtin_amdgcn_sched_barrier(0);
+    tile_runs(it + kRing, run_next);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- mask (only tiles that reach a causal or split boundary), lazy row maximum
+    if (t0 + kVTile - 1 > all_last) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t0 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        s2[r] = key <= row_last ? s2[r] : kNegInf;
+      }
+    }
+    float mx = s2[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s2[r]);
+    mx = halves_max(mx) * c;       // c > 0 keeps the order and -inf
     if (__ballot(mx > M + TAU) != 0) {
       const float mn = fmaxf(M, mx);
-      const float alpha = (M == kNegInf) ? 0.f : exp2f(M - mn);
+      const float alpha = (M == kNegInf) ? 0.f : fast_exp2(M - mn);
       M = mn;
       l_lane *= alpha;
       // register r of O holds row 8(r/4) + 4kh + r%4, whose factor sits in that lane
@@ -214,13 +238,15 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
         O[1][r] *= ar;
       }
     }
+    // p = 2^(s c - M); a row with no visible key yet keeps M = -inf and gets p = 0.
+    const float negM = M == kNegInf ? 0.f : -M;
     uint32_t pk[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float p0 = s2[2 * q] == kNegInf ? 0.f : exp2f(s2[2 * q] - M);
-      const float p1 = s2[2 * q + 1] == kNegInf ? 0.f : exp2f(s2[2 * q + 1] - M);
+      const float p0 = fast_exp2(fmaf(s2[2 * q], c, negM));
+      const float p1 = fast_exp2(fmaf(s2[2 * q + 1], c, negM));
       pk[q] = pack_bf16x2(p0, p1);
-      l_lane += bf16lo(pk[q]) + bf16hi(pk[q]);
+      l_lane = dot2_bf16(pk[q], kBf16One2, l_lane);   // normaliser from the same bf16 weights
     }
 
     // ---- O += P V over this wave's quarter of D (2 output tiles, 2 k-steps of 16 keys)
@@ -239,24 +265,32 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
     }
   };
 
-  // Three bodies per trip over fixed slots; leaving early exits the loop, so the
-  // latch is only reached after all three and its pending loads always match.
+  // Three bodies per trip over fixed slots, the last one or two tiles after the
+  // loop.  With a single exit the loads pending at the loop header are the same
+  // from the prologue and from the latch, so every body waits for its own tile
+  // only (early exits inside the trip made the compiler drain one tile more).
   if (ntiles > 0) {
 #pragma unroll
-    for (int i = 0; i < kRing - 1; ++i) issue(i, i);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int it = 0;; it += kRing) {
-      body(it, 0);
-      if (it + 1 >= ntiles) break;
-      body(it + 1, 1);
-      if (it + 2 >= ntiles) break;
-      body(it + 2, 2);
-      if (it + 3 >= ntiles) break;
+    for (int i = 0; i < kRing - 1; ++i) {
+      tile_runs(i, run_next);
+      issue(i, run_next, k_off0, v_off0);
+      // tile by tile, in the order the loop issues them (exact wait counts)
+      __builtin_amdgcn_sched_barrier(0);
     }
+    tile_runs(kRing - 1, run_next);
+    __builtin_amdgcn_sched_barrier(0);
+    int it = 0;
+    for (; it + kRing <= ntiles; it += kRing) {
+      body(it, 0);
+      body(it + 1, 1);
+      body(it + 2, 2);
+    }
+    if (it < ntiles) body(it, 0);
+    if (it + 1 < ntiles) body(it + 1, 1);
   }
 
   // ---- normalise and write this wave's quarter of every live row
-  const float l_row = l_lane + __shfl_xor(l_lane, 32);       // lanes c32 and c32 + 32 share a row
+  const float l_row = halves_sum(l_lane);       // lanes c32 and c32 + 32 share a row
   const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -278,17 +312,22 @@ __global__ __launch_bounds__(256, 2) void verify_kernel(const SplitArgs a) {
   }
 }
 
-hipError_t launch_verify(int head_dim, int group, const SplitArgs& a, int grid, hipStream_t st) {
-  if (grid <= 0) return hipSuccess;
-  if (head_dim != kVD) return hipErrorInvalidValue;
+template <bool SINGLE>
+static hipError_t launch_g(int group, const SplitArgs& a, int grid, hipStream_t st) {
   switch (group) {
-    case 1: verify_kernel<1><<<grid, 256, 0, st>>>(a); break;
-    case 2: verify_kernel<2><<<grid, 256, 0, st>>>(a); break;
-    case 4: verify_kernel<4><<<grid, 256, 0, st>>>(a); break;
-    case 8: verify_kernel<8><<<grid, 256, 0, st>>>(a); break;
+    case 1: mfma_attn_kernel<1, SINGLE><<<grid, 256, 0, st>>>(a); break;
+    case 2: mfma_attn_kernel<2, SINGLE><<<grid, 256, 0, st>>>(a); break;
+    case 4: mfma_attn_kernel<4, SINGLE><<<grid, 256, 0, st>>>(a); break;
+    case 8: mfma_attn_kernel<8, SINGLE><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_verify(int head_dim, int group, bool single_query, const SplitArgs& a, int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim != kVD) return hipErrorInvalidValue;
+  return single_query ? launch_g<true>(group, a, grid, st) : launch_g<false>(group, a, grid, st);
 }
 
 }  // namespace wmtp

@@ -117,6 +117,24 @@ def test_draft_batch_limits():
                                           1) == W.EINVAL
 
 
+def test_default_split_gives_one_work_item_per_compute_unit():
+    # 0 = library default: keys x KV heads / 256 CUs, rounded up to 64, clamped to [256, 65536]
+    sh = shape()                                                   # 2 KV heads
+    for n in (1048577, 1048580):
+        assert W.draft_workspace_bytes(W.FULL, sh, [n], 0) == W.draft_workspace_bytes(W.FULL, sh, [n], 8256)
+        assert W.verify_workspace_bytes(sh, 4, [n], 0) == W.verify_workspace_bytes(sh, 4, [n], 8256)
+    assert -(-1048577 // 8256) * 2 == 256                          # work items = CUs
+    # a batch counts all its keys
+    assert W.verify_workspace_bytes(sh, 4, [262144] * 4, 0) == W.verify_workspace_bytes(sh, 4, [262144] * 4, 8192)
+    # short contexts: the 256-key floor; very long ones: the 65536-key cap
+    assert W.draft_workspace_bytes(W.FULL, sh, [1000], 0) == W.draft_workspace_bytes(W.FULL, sh, [1000], 256)
+    big = shape(hq=64, hk=8)
+    assert W.draft_workspace_bytes(W.FULL, big, [8 << 20], 0) == W.draft_workspace_bytes(W.FULL, big, [8 << 20], 65536)
+    # the window draft keeps its short fixed split
+    assert W.draft_workspace_bytes(W.SINK_WINDOW, sh, [1048577], 0, 4, 4096) == \
+        W.draft_workspace_bytes(W.SINK_WINDOW, sh, [1048577], 64, 4, 4096)
+
+
 def test_workspace_sizes_follow_the_split_plan():
     sh = shape()
     # full mode at 1M+1 tokens, 1024-token splits: 1025 splits x 16 rows x (256 + 1) floats, 256-byte aligned
