@@ -41,8 +41,8 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "7abbd80f229cb7437e21272986349cba653bbd7acdbd9a03e16ee5b3ae398509",
-                  "fetch_kib": 1049332.24, "write_kib": 8224.0, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_TRAFFIC = {"sources_sha256": "61e0a2dff6375097725b39de31783f90854e1a44864be1f0bb44f04b4b6da762",
+                  "fetch_kib": 1053702.05, "write_kib": 8224.0, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
 
@@ -122,6 +122,7 @@ class Step:
         tail_v = synth.normal((1, Wn, Hk, D), wl.seed, "ring_tail_v", wl.kv_scale, "bf16", dev)
         W.ring_append(self.sh, self.ring, sink_k, sink_v, [0])
         W.ring_append(self.sh, self.ring, tail_k, tail_v, [n0 - Wn])
+        self.tail_k, self.tail_v = tail_k, tail_v
         # per-step inputs
         self.q_draft = synth.normal((g, 1, Hq, D), wl.seed, "q_draft", 1.0, "bf16", dev)
         self.k_draft = synth.normal((g, 1, 1, Hk, D), wl.seed, "k_new", wl.kv_scale, "bf16", dev)
@@ -199,18 +200,175 @@ def time_steps(step, mode, flag, steps, warmup):
     ev_v = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
             for _ in range(steps)]
     ev_d = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    start.record()
+    ev_s[0].record()
     for s in range(steps):
         step.draft(mode, flag, ev_d[s])
         step.verify(ev_v[s])
-    end.record()
+        ev_s[s + 1].record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    total_ms = ev_s[0].elapsed_time(ev_s[-1])
+    step_ms = [ev_s[s].elapsed_time(ev_s[s + 1]) for s in range(steps)]
     ver_ms = [a.elapsed_time(b) for row in ev_v for a, b in row]
     draft_ms = [a.elapsed_time(b) for a, b in ev_d]
-    return total_ms / steps, float(np.mean(ver_ms)), float(np.mean(draft_ms))
+    return total_ms / steps, float(np.mean(ver_ms)), float(np.mean(draft_ms)), step_ms
+
+
+def pct(ms):
+    """median / p10 / p90 of a list of milliseconds, in microseconds."""
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median": round(float(np.median(a)), 1), "p10": round(float(np.percentile(a, 10)), 1),
+            "p90": round(float(np.percentile(a, 90)), 1), "n": int(a.size)}
+
+
+def _hold():
+    """Keep the GPU busy for a bounded spin (tens of µs) while the host queues the timed launches,
+    so the events measure device time rather than Python launch overhead."""
+    torch.cuda._sleep(100000)
+
+
+def _timed(fn, reps, before=_hold):
+    """Per-repetition milliseconds of fn() between events on the current stream (`before` runs untimed)."""
+    out = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def graph_step(step, mode, flag, reps):
+    """One whole decode step captured in a HIP graph and replayed.
+
+    Eager work (clearing the outputs) runs between replays, and every replay's
+    outputs are compared with an eager step's, bit for bit (the kernels are
+    deterministic).  Returns (per-replay ms, all replays matched).
+    """
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        step.draft(mode, flag)
+        step.verify()
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    ref_d, ref_v = step.out_d.clone(), step.out_v.clone()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step.draft(mode, flag)
+        step.verify()
+    torch.cuda.synchronize()
+    ok, times = True, []
+    for _ in range(reps):
+        step.out_d.zero_()
+        step.out_v.zero_()
+        times += _timed(gr.replay, 1)
+        ok = ok and torch.equal(step.out_d, ref_d) and torch.equal(step.out_v, ref_v)
+    del gr
+    torch.cuda.synchronize()
+    return times, ok
+
+
+def window_step_fn(step, flag, n):
+    """One windowed draft step at length n (append at n - 1, attend, combine)."""
+    g0 = 0
+
+    def run():
+        W.ring_append(step.sh, step.ring, step.k_draft[g0], step.v_draft[g0], [n - 1])
+        parts = W.draft_attn(W.SINK_WINDOW | flag, step.sh, step.q_draft[g0], [n], step.ws_win, ring=step.ring,
+                             chunk_tokens=step.chunk_win)
+        W.combine(parts, step.out_d, step.lse_d)
+    return run
+
+
+def window_measurements(step, flag, reps, dev, contexts):
+    """Windowed draft step: warm and cold (1 GiB written between repetitions), and across contexts."""
+    wl, n0 = step.wl, step.n0
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    run = window_step_fn(step, flag, n0 + 1)
+    run()
+    torch.cuda.synchronize()
+    res = {"warm": pct(_timed(run, reps)), "cold_after_1GiB_write": pct(_timed(run, reps, lambda: flush.fill_(1)))}
+    res["launches"] = "ring append + draft attention + combine; host launches queued behind a spin or the flush"
+    by_ctx = {}
+    for n in contexts:
+        # the ring of a sequence at length n: sinks at 0..S-1, the last W context tokens before n
+        W.ring_append(step.sh, step.ring, step.tail_k, step.tail_v, [n - wl.window])
+        r = window_step_fn(step, flag, n + 1)
+        r()
+        torch.cuda.synchronize()
+        by_ctx[str(n)] = pct(_timed(r, reps, lambda: flush.fill_(1)))["median"]
+    W.ring_append(step.sh, step.ring, step.tail_k, step.tail_v, [n0 - wl.window])   # back to n0
+    torch.cuda.synchronize()
+    del flush
+    res["cold_median_by_context"] = by_ctx
+    return res
+
+
+def native_split_measurements(step, flag, reps, dev):
+    """Native draft launch at 1M with literal 256-key splits and with the library default."""
+    n = step.n0 + 1
+    out = {}
+    for chunk, name in ((256, "split_256"), (0, "split_default")):
+        ws = W.workspace(W.draft_workspace_bytes(W.FULL, step.sh, [n], chunk), dev)
+        run = lambda: W.draft_attn(W.FULL | flag, step.sh, step.q_draft[0], [n], ws, paged=step.layers[0][2],
+                                   chunk_tokens=chunk)
+        run()
+        out[name] = pct(_timed(run, reps))["median"]
+        del ws
+    return out
+
+
+def mixed_batch(flag, reps, dev):
+    """Four sequences of mixed length in one call: native draft, then the window draft at three W."""
+    wl = synth.workload("mixed_4seq_bf16")
+    Hq, Hk, D, S = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.sink
+    sh = W.make_shape(Hq, Hk, D, torch.bfloat16, wl.scale)
+    lens = [n + 1 for n in wl.contexts]                 # after this step's append
+    B = len(lens)
+    bt, total = synth.block_table(wl.seed, [synth.blocks_for(n, 16) for n in lens], permuted=True)
+    k = synth.normal((total, Hk, 16, D), wl.seed, "pool_k", wl.kv_scale, "bf16", dev)
+    v = synth.normal((total, Hk, 16, D), wl.seed, "pool_v", wl.kv_scale, "bf16", dev)
+    desc = W.make_paged(k, v, torch.from_numpy(bt).to(dev))
+    q = synth.normal((B, Hq, D), wl.seed, "q_draft", 1.0, "bf16", dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = W.workspace(W.draft_workspace_bytes(W.FULL, sh, lens, 0), dev)
+
+    def native():
+        W.combine(W.draft_attn(W.FULL | flag, sh, q, lens, ws, paged=desc), out, lse)
+    native()
+    t = pct(_timed(native, reps))["median"]
+    res = {"contexts": list(wl.contexts), "native_draft_step_us": t,
+           "native_gbps": round(sum(lens) * Hk * D * 4 / (t * 1e-6) / 1e9, 1), "window_draft_step_us": {}}
+    del ws
+    for Wn in wl.windows:
+        rk = torch.zeros((B, Hk, S + Wn, D), dtype=torch.bfloat16, device=dev)
+        rv = torch.zeros_like(rk)
+        tags = torch.full((B, S + Wn), -1, dtype=torch.int32, device=dev)
+        ring = W.make_ring(rk, rv, tags, S, Wn)
+        sk = synth.normal((B, S, Hk, D), wl.seed, ("ring_sink_k", Wn), wl.kv_scale, "bf16", dev)
+        sv = synth.normal((B, S, Hk, D), wl.seed, ("ring_sink_v", Wn), wl.kv_scale, "bf16", dev)
+        tk = synth.normal((B, Wn, Hk, D), wl.seed, ("ring_tail_k", Wn), wl.kv_scale, "bf16", dev)
+        tv = synth.normal((B, Wn, Hk, D), wl.seed, ("ring_tail_v", Wn), wl.kv_scale, "bf16", dev)
+        W.ring_append(sh, ring, sk, sv, [0] * B)
+        W.ring_append(sh, ring, tk, tv, [n - Wn for n in lens])
+        wsw = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, lens, 0, S, Wn), dev)
+
+        def window():
+            W.combine(W.draft_attn(W.SINK_WINDOW | flag, sh, q, lens, wsw, ring=ring), out, lse)
+        window()
+        res["window_draft_step_us"][str(Wn)] = pct(_timed(window, reps))["median"]
+        del rk, rv, tags, wsw
+    del k, v
+    torch.cuda.empty_cache()
+    return res
 
 
 def _per_rep(fn, budget_s):
@@ -285,6 +443,8 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="verify split size (0 = library default)")
     ap.add_argument("--exact-pv", action="store_true", help="draft PV with fp32 weights instead of bf16 pairs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-details", action="store_true",
+                    help="skip the extra measurements (graph replay, cold window, split and batch variants)")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 256 MiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -316,9 +476,25 @@ def main():
                 args.split, dev)
 
     log("timing windowed step")
-    win_ms, ver_ms, dwin_ms = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup)
+    win_ms, ver_ms, dwin_ms, win_steps = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup)
     log("timing native step")
-    nat_ms, ver_ms2, dnat_ms = time_steps(step, W.FULL, flag, args.steps, args.warmup)
+    nat_ms, ver_ms2, dnat_ms, nat_steps = time_steps(step, W.FULL, flag, args.steps, args.warmup)
+    details = {"step_us": {"windowed": pct(win_steps), "native": pct(nat_steps)}}
+    if not args.no_details:
+        reps = 20
+        log("graph-captured steps")
+        gw, okw = graph_step(step, W.SINK_WINDOW, flag, 5)
+        gn, okn = graph_step(step, W.FULL, flag, 5)
+        details["graph_step_us"] = {"windowed": pct(gw), "native": pct(gn), "replays_match_eager": bool(okw and okn)}
+        log("window draft: warm, cold, across contexts")
+        details["window_draft_step_us"] = window_measurements(
+            step, flag, reps, dev, (32768, 131072, 524288, n0))
+        log("native draft launch: literal 256-key splits vs default")
+        details["native_draft_launch_us"] = native_split_measurements(step, flag, 10, dev)
+        del step
+        torch.cuda.empty_cache()
+        log("mixed batch (4 sequences)")
+        details["mixed_batch"] = mixed_batch(flag, reps, dev)
 
     g = wl.gamma
     bytes_win = sum(kv_bytes(min(n0 + j, wl.sink + wl.window), wl) for j in range(1, g + 1)) + \
@@ -375,6 +551,7 @@ def main():
     }
     native_draft_bytes = draft_launch_bytes(n0 + 1, wl, True)
     res["draft_native_gbps"] = round(native_draft_bytes / (dnat_ms * 1e-3) / 1e9, 1)
+    res["details"] = details
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
         res["cpu_baseline"] = cpu_baseline(wl, n0)

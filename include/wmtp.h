@@ -154,9 +154,11 @@ int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const 
  *  n_b = seq_lens_host[b] (host) is the length after this step's own entry was
  *  appended, so the query attends to itself.  q: device [batch][H_q][D].
  *  chunk_tokens: entries per split (a multiple of 64).  0 = library default:
- *  in WMTP_FULL mode, the keys of the whole batch times H_kv divided over 256
- *  work items (one per MI355X compute unit), rounded up to a multiple of 64 and
- *  clamped to [256, 65536]; in WMTP_SINK_WINDOW mode, 64.
+ *  the smallest multiple of 64 (at least 256 in WMTP_FULL mode, 64 in
+ *  WMTP_SINK_WINDOW mode, at most 65536) for which the work items
+ *  (sequence, KV head, split) fit one round of 256 (WMTP_FULL: one per MI355X
+ *  compute unit) or 512 (WMTP_SINK_WINDOW) items, or of the smallest multiple
+ *  of that holding one item per sequence and KV head.
  *  The call writes split partials into `workspace` (device, >= the size from
  *  wmtp_draft_workspace_bytes, 256-byte aligned) and describes them in
  *  *parts (host).  Finish with wmtp_combine. */
@@ -172,7 +174,7 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
  *  0..n_b-t_q+i.  Requires t_q * G <= WMTP_MAX_VERIFY_ROWS, dtype bf16 and
  *  head_dim 256 (other shapes return WMTP_EUNSUPPORTED).
  *  split_tokens: entries per split (a multiple of 32; 0 = the WMTP_FULL draft
- *  default, one work item per compute unit).
+ *  default: one round of one work item per compute unit).
  *  Workspace and *parts as for wmtp_draft_attn. */
 int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv,
                      const int32_t* seq_lens_host, int32_t batch, int32_t split_tokens,

@@ -16,25 +16,41 @@ using namespace wmtp;
 
 namespace {
 
-constexpr int kDraftDefaultChunkWindow = 64;
 constexpr int kDraftTile = 64;
 constexpr int kVerifyTile = 32;    // keys per verify tile
 
-// Default split of the full-context kernels: one work item per compute unit
-// (MI355X has 256), so every CU streams one long run of blocks; measured faster
-// than two co-resident work items per CU at 1M keys.  Clamped so that short
-// contexts still get several splits and long ones a bounded combine.
-constexpr int64_t kComputeUnits = 256;
-constexpr int64_t kMinDefaultSplit = 256;
+// Default splits.  A split is one work item (sequence, KV head, split).  The
+// default is the smallest split, a multiple of 64, whose work items fit one
+// round of `slots` co-resident items (or of the smallest multiple of `slots`
+// that holds one item per sequence and head), so no item waits for a second
+// round.  Full-context launches target 256 slots, one item per MI355X compute
+// unit: each CU streams one long run of blocks, measured faster than two
+// co-resident items per CU at 1M keys.  The window draft is latency-bound and
+// its 512-thread items fit two per CU, so it targets 512 slots with splits of
+// at least one 64-entry tile.
+constexpr int64_t kFullSlots = 256;
+constexpr int64_t kWindowSlots = 512;
+constexpr int64_t kFullMinSplit = 256;
+constexpr int64_t kWindowMinSplit = 64;
 constexpr int64_t kMaxDefaultSplit = 65536;
 
-int32_t default_split(const int32_t* seq_lens, int batch, int kv_heads) {
+int64_t work_items(const int64_t* vis, int batch, int kv_heads, int64_t split) {
+  int64_t n = 0;
+  for (int b = 0; b < batch; ++b) n += (vis[b] + split - 1) / split;
+  return n * kv_heads;
+}
+
+int32_t default_split(const int64_t* vis, int batch, int kv_heads, int64_t slots, int64_t min_split) {
   int64_t keys = 0;
-  for (int b = 0; b < batch; ++b) keys += seq_lens[b] > 0 ? seq_lens[b] : 0;
-  int64_t s = (keys * kv_heads + kComputeUnits - 1) / kComputeUnits;
+  for (int b = 0; b < batch; ++b) keys += vis[b];
+  int64_t target = slots;
+  while (target < (int64_t)batch * kv_heads) target += slots;
+  int64_t s = (keys * kv_heads + target - 1) / target;
   s = (s + kDraftTile - 1) / kDraftTile * kDraftTile;   // a multiple of both tiles
-  s = s < kMinDefaultSplit ? kMinDefaultSplit : s;
-  return (int32_t)(s > kMaxDefaultSplit ? kMaxDefaultSplit : s);
+  s = s < min_split ? min_split : s;
+  s = s > kMaxDefaultSplit ? kMaxDefaultSplit : s;
+  while (s < kMaxDefaultSplit && work_items(vis, batch, kv_heads, s) > target) s += kDraftTile;
+  return (int32_t)s;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -104,15 +120,16 @@ int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, i
   if (base_mode != WMTP_FULL && base_mode != WMTP_SINK_WINDOW) return WMTP_EINVAL;
   if ((mode & ~0xF) & ~WMTP_DRAFT_FAST_PV) return WMTP_EINVAL;
   if (!seq_lens || batch < 1 || batch > WMTP_MAX_BATCH) return WMTP_EINVAL;
-  if (chunk == 0)
-    chunk = base_mode == WMTP_FULL ? default_split(seq_lens, batch, shape->num_kv_heads) : kDraftDefaultChunkWindow;
-  if (chunk < kDraftTile || chunk % kDraftTile != 0) return WMTP_EINVAL;
   if (base_mode == WMTP_SINK_WINDOW && (sink < 0 || window < 1)) return WMTP_EINVAL;
   int64_t vis[WMTP_MAX_BATCH];
   for (int b = 0; b < batch; ++b) {
     if (seq_lens[b] < 0) return WMTP_EINVAL;
     vis[b] = base_mode == WMTP_FULL ? seq_lens[b] : std::min<int64_t>(seq_lens[b], (int64_t)sink + window);
   }
+  if (chunk == 0)
+    chunk = base_mode == WMTP_FULL ? default_split(vis, batch, shape->num_kv_heads, kFullSlots, kFullMinSplit)
+                                   : default_split(vis, batch, shape->num_kv_heads, kWindowSlots, kWindowMinSplit);
+  if (chunk < kDraftTile || chunk % kDraftTile != 0) return WMTP_EINVAL;
   *chunk_out = chunk;
   return make_plan(vis, batch, chunk, shape->num_q_heads, shape->head_dim, shape->num_kv_heads, p);
 }
@@ -126,13 +143,13 @@ int verify_plan(const wmtp_shape* shape, int32_t t_q, const int32_t* seq_lens, i
   if (t_q < 1) return WMTP_EINVAL;
   const int g = shape->num_q_heads / shape->num_kv_heads;
   if ((int64_t)t_q * g > WMTP_MAX_VERIFY_ROWS) return WMTP_EUNSUPPORTED;
-  if (split == 0) split = default_split(seq_lens, batch, shape->num_kv_heads);
-  if (split < kVerifyTile || split % kVerifyTile != 0) return WMTP_EINVAL;
   int64_t vis[WMTP_MAX_BATCH];
   for (int b = 0; b < batch; ++b) {
     if (seq_lens[b] < t_q) return WMTP_EINVAL;   // the queries' own keys are in the cache
     vis[b] = seq_lens[b];
   }
+  if (split == 0) split = default_split(vis, batch, shape->num_kv_heads, kFullSlots, kFullMinSplit);
+  if (split < kVerifyTile || split % kVerifyTile != 0) return WMTP_EINVAL;
   *split_out = split;
   return make_plan(vis, batch, split, t_q * shape->num_q_heads, shape->head_dim, shape->num_kv_heads, p);
 }

@@ -143,6 +143,9 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
     return base + r;
   };
 
+  // Ordinary loads, also for the paged pool: each wave reads a 64-byte half of
+  // 128-byte lines whose other half another wave reads, and non-temporal loads
+  // (which the matrix-core kernel uses) measured 10% slower here.
   // Register ring: the K and V of tile i arrive in slot i % kRing, issued
   // kRing - 1 tiles ahead, so two tiles per wave are in flight while one is
   // computed.

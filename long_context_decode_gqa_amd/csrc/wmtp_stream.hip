@@ -1,8 +1,8 @@
 // Streaming-read probe: the practical HBM read ceiling the attention kernels
 // are compared against.  Each workgroup streams one contiguous part of the
-// buffer; every thread keeps two stages of kStreamUnroll 16-byte loads in
-// flight (the next stage is issued before the current one is consumed) and
-// folds the data into one word, so no load can be dropped.  Loads past the
+// buffer; every thread keeps two stages of kStreamUnroll non-temporal 16-byte
+// loads in flight (the next stage is issued before the current one is
+// consumed) and folds the data into one word, so no load can be dropped.  Loads past the
 // part's end are clamped to its last element and not folded, so every load
 // stays in bounds and every stage issues the same loads.
 #include "wmtp_device.hpp"
@@ -10,7 +10,7 @@
 
 namespace wmtp {
 
-constexpr int kStreamUnroll = 8;
+constexpr int kStreamUnroll = 4;
 constexpr int kStreamThreads = 256;
 
 __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const u32x4* __restrict__ src, int64_t nvec,
@@ -25,7 +25,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const u32x4
     auto issue = [&](int64_t s, int slot) {
       const int64_t s0 = base + min(s, nsteps - 1) * kStep + threadIdx.x;
 #pragma unroll
-      for (int u = 0; u < kStreamUnroll; ++u) r[slot][u] = src[min(s0 + (int64_t)u * kStreamThreads, end - 1)];
+      for (int u = 0; u < kStreamUnroll; ++u)
+        r[slot][u] = __builtin_nontemporal_load(src + min(s0 + (int64_t)u * kStreamThreads, end - 1));
     };
     auto consume = [&](int64_t s, int slot) {
       const int64_t s0 = base + s * kStep + threadIdx.x;

@@ -141,6 +141,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
   // V: element jj (0..7) of k-step ks for this lane's half is key 16 ks + 8 (jj / 4)
   // + 4 kh + jj % 4 (block run ks); the lane holds d = 2 c32, 2 c32 + 1 of the
   // wave's quarter (one dword), at lane offset v_off + (8 (jj / 4) + jj % 4) rows.
+  // K and V are read once per launch: non-temporal loads.
   // Tiles past the end re-load the last tile (never consumed), so every body
   // issues the same loads and the loop has no load-carrying branch.  The two
   // 32-bit lane offsets are passed opaque, so they are not widened and hoisted
@@ -151,12 +152,12 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
   auto issue = [&](int slot, const int64_t (&run)[2], uint32_t k_off, uint32_t v_off) {
 #pragma unroll
     for (int l = 0; l < kVLoads; ++l)
-      kreg[slot][l] = load_at<u32x4>(((l & 1) ? kbase_hi : kbase) + run[l >> 1], k_off);
+      kreg[slot][l] = load_nt<u32x4>(((l & 1) ? kbase_hi : kbase) + run[l >> 1], k_off);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
-        vreg[slot][ks][jj] = load_at<uint32_t>(vbase + run[ks] + (8 * (jj >> 2)) * ROWB, v_off + (jj & 3) * ROWB);
+        vreg[slot][ks][jj] = load_nt<uint32_t>(vbase + run[ks] + (8 * (jj >> 2)) * ROWB, v_off + (jj & 3) * ROWB);
   };
 
   f32x16 O[2];

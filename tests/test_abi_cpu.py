@@ -117,22 +117,57 @@ def test_draft_batch_limits():
                                           1) == W.EINVAL
 
 
-def test_default_split_gives_one_work_item_per_compute_unit():
-    # 0 = library default: keys x KV heads / 256 CUs, rounded up to 64, clamped to [256, 65536]
+def _splits_of(ws_bytes, rows, d):
+    """Total splits recorded in a workspace size: align256(P rows d 4) + align256(P rows 4)."""
+    for p in range(1, 1 << 20):
+        if ((p * rows * d * 4 + 255) // 256 + (p * rows * 4 + 255) // 256) * 256 == ws_bytes:
+            return p
+    raise AssertionError(ws_bytes)
+
+
+def _rule(vis, hk, slots, lo):
+    """The default-split rule, by exhaustive search over multiples of 64."""
+    target = slots
+    while target < len(vis) * hk:
+        target += slots
+    items = lambda s: hk * sum(-(-v // s) for v in vis)
+    s = lo
+    while s < 65536 and items(s) > target:
+        s += 64
+    return s
+
+
+@pytest.mark.parametrize("lens", [[1048577], [1048580], [262144] * 4, [32769, 131073, 524289, 1048577], [1000],
+                                  [5, 70000, 3, 9000, 1 << 20]])
+def test_default_split_fits_one_round_of_work_items(lens):
+    # 0 = library default: the smallest split (multiple of 64, >= 256) whose work
+    # items (sequence, KV head, split) fit one round of 256 (one per compute unit)
     sh = shape()                                                   # 2 KV heads
-    for n in (1048577, 1048580):
-        assert W.draft_workspace_bytes(W.FULL, sh, [n], 0) == W.draft_workspace_bytes(W.FULL, sh, [n], 8256)
-        assert W.verify_workspace_bytes(sh, 4, [n], 0) == W.verify_workspace_bytes(sh, 4, [n], 8256)
-    assert -(-1048577 // 8256) * 2 == 256                          # work items = CUs
-    # a batch counts all its keys
-    assert W.verify_workspace_bytes(sh, 4, [262144] * 4, 0) == W.verify_workspace_bytes(sh, 4, [262144] * 4, 8192)
-    # short contexts: the 256-key floor; very long ones: the 65536-key cap
-    assert W.draft_workspace_bytes(W.FULL, sh, [1000], 0) == W.draft_workspace_bytes(W.FULL, sh, [1000], 256)
+    s = _rule(lens, 2, 256, 256)
+    assert W.draft_workspace_bytes(W.FULL, sh, lens, 0) == W.draft_workspace_bytes(W.FULL, sh, lens, s)
+    if min(lens) >= 4:
+        assert W.verify_workspace_bytes(sh, 4, lens, 0) == W.verify_workspace_bytes(sh, 4, lens, s)
+    total = _splits_of(W.draft_workspace_bytes(W.FULL, sh, lens, 0), 16, 256)
+    assert total * 2 <= 256
+    if s > 256:                                                    # minimal: one tile less does not fit
+        assert 2 * sum(-(-v // (s - 64)) for v in lens) > 256
+
+
+def test_default_split_values():
+    sh = shape()
+    assert _rule([1048577], 2, 256, 256) == 8256                   # 128 splits x 2 heads = 256 items
+    assert _rule([32769, 131073, 524289, 1048577], 2, 256, 256) > 13568   # plain division would give 260 items
+    # very long contexts hit the 65536 cap
     big = shape(hq=64, hk=8)
     assert W.draft_workspace_bytes(W.FULL, big, [8 << 20], 0) == W.draft_workspace_bytes(W.FULL, big, [8 << 20], 65536)
-    # the window draft keeps its short fixed split
+    # the window draft scans min(n, S+W) entries and targets 512 items of at least 64 entries
     assert W.draft_workspace_bytes(W.SINK_WINDOW, sh, [1048577], 0, 4, 4096) == \
         W.draft_workspace_bytes(W.SINK_WINDOW, sh, [1048577], 64, 4, 4096)
+    lens = [32769, 131073, 524289, 1048577]
+    s = _rule([min(n, 4 + 16384) for n in lens], 2, 512, 64)
+    assert s == 320                                                # 256 would give 520 items
+    assert W.draft_workspace_bytes(W.SINK_WINDOW, sh, lens, 0, 4, 16384) == \
+        W.draft_workspace_bytes(W.SINK_WINDOW, sh, lens, s, 4, 16384)
 
 
 def test_workspace_sizes_follow_the_split_plan():
