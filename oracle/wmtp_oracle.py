@@ -28,7 +28,11 @@ design notes):
   * a draft step appends its own new entry, then attends over it (causal decode);
   * the window holds the W most recent entries including the current one, the
     sinks are absolute positions 0..S-1, and the two sets are unioned;
-  * the ring has S+W slots, slot(p) = p for p < S, else S + (p - S) mod W;
+  * the ring has S+W+R slots, slot(p) = p for p < S, else S + (p - S) mod (W+R),
+    where R >= 0 headroom slots absorb drafted tokens that verification
+    rejects (R >= gamma - 1 keeps every entry a later window needs);
+  * rejected drafted tokens are forgotten by clearing the tags of positions at
+    or past the accepted length; a re-append at the same position overwrites;
   * query head h reads KV head h // G (consecutive query heads share a KV head);
   * the softmax scale is 1/sqrt(D);
   * the paged pool is laid out [block][kv_head][block_offset][D].
@@ -95,57 +99,77 @@ def draft_entries_read(n: int, mode: int, sink: int = 0, window: int = 0) -> int
 
 
 # --------------------------------------------------------------------------- ring
-def ring_slot(p: int, sink: int, window: int) -> int:
-    """Slot of absolute position p in the compact ring of S+W slots.
+def ring_slot(p: int, sink: int, window: int, headroom: int = 0) -> int:
+    """Slot of absolute position p in the compact ring of S + W + R slots.
 
     [P3 Abstract] names a compact ring buffer holding the draft's window; the
     layout is this build's reading: sinks occupy slots 0..S-1 in place, every
-    later position cycles through slots S..S+W-1.
+    later position cycles through the C = W + R slots S..S+C-1.  R >= 0 extra
+    slots ("headroom") let drafted tokens that verification rejects be written
+    without overwriting an entry that a later window still needs.
     """
     if p < 0:
         raise ValueError("negative position")
     if p < sink:
         return int(p)
-    return int(sink + (p - sink) % window)
+    return int(sink + (p - sink) % (window + headroom))
 
 
-def ring_append(tags: np.ndarray, pos: int, count: int, sink: int, window: int) -> List[Tuple[int, int]]:
+def ring_append(tags: np.ndarray, pos: int, count: int, sink: int, window: int,
+                headroom: int = 0) -> List[Tuple[int, int]]:
     """Apply an append of `count` tokens at positions pos..pos+count-1 to `tags`.
 
     tags[slot] holds the absolute position stored in the slot (-1 = empty).
     Returns the (token index, slot) writes in order.  A token is stored only if
-    it can still be visible once the append ends: p < S, or p among the W most
-    recent positions of this append.  That keeps an append of more than W
-    tokens deterministic (no slot is written twice).
+    it survives the append: p < S, or p among the C = W + R most recent
+    positions of this append.  That keeps an append of more than C tokens
+    deterministic (no slot is written twice) and equal to appending the tokens
+    one by one.
     """
     last = pos + count - 1
+    cycle = window + headroom
     writes = []
     for i in range(count):
         p = pos + i
-        if p < sink or p > last - window:
-            s = ring_slot(p, sink, window)
+        if p < sink or p > last - cycle:
+            s = ring_slot(p, sink, window, headroom)
             tags[s] = p
             writes.append((i, s))
     return writes
 
 
-def ring_expected_tags(n: int, sink: int, window: int) -> np.ndarray:
+def ring_rollback(tags: np.ndarray, n: int) -> List[int]:
+    """Forget every entry at a position >= n (drafted tokens that were not
+    accepted): their tags become -1.  Returns the cleared slots."""
+    cleared = [int(s) for s in np.nonzero(tags >= n)[0]]
+    tags[tags >= n] = -1
+    return cleared
+
+
+def ring_expected_tags(n: int, sink: int, window: int, headroom: int = 0) -> np.ndarray:
     """Tag of every slot (-1 = empty) after positions 0..n-1 were appended in order."""
-    tags = np.full(sink + window, -1, dtype=np.int64)
+    tags = np.full(sink + window + headroom, -1, dtype=np.int64)
     for p in range(n):
-        tags[ring_slot(p, sink, window)] = p
+        tags[ring_slot(p, sink, window, headroom)] = p
     return tags
 
 
-def window_slot_positions(n: int, sink: int, window: int) -> np.ndarray:
+def window_slot_positions(n: int, sink: int, window: int, headroom: int = 0) -> np.ndarray:
     """For each ring slot, the position it must hold for a query at length n (-1 if none).
 
     This is the sink_window visible set placed in ring order.
     """
-    out = np.full(sink + window, -1, dtype=np.int64)
+    out = np.full(sink + window + headroom, -1, dtype=np.int64)
     for p in visible_positions(n, SINK_WINDOW, sink, window):
-        out[ring_slot(int(p), sink, window)] = p
+        out[ring_slot(int(p), sink, window, headroom)] = p
     return out
+
+
+def ring_visible(tags: np.ndarray, n: int, sink: int, window: int) -> np.ndarray:
+    """Per slot, the position a draft query at length n reads there (-1 = masked):
+    the slot's tag if that position is in the sink_window visible set."""
+    vis = set(int(p) for p in visible_positions(n, SINK_WINDOW, sink, window))
+    return np.array([int(t) if int(t) in vis else -1 for t in tags], dtype=np.int64)
 
 
 # --------------------------------------------------------------------------- paging

@@ -107,6 +107,109 @@ def test_bulk_append_equals_sequential_appends(S, W, pos, T):
     assert len(slots) == len(set(slots))                # no slot written twice
 
 
+@pytest.mark.parametrize("S,W,R,N", [(4, 16, 3, 25), (4, 16, 2, 500), (0, 7, 1, 50), (1, 1, 4, 30), (3, 5, 7, 9)])
+def test_ring_with_headroom_holds_sinks_and_last_cycle(S, W, R, N):
+    """With R headroom slots the ring keeps the first S and the last W + R positions (list model)."""
+    tags = np.full(S + W + R, -1, dtype=np.int64)
+    kept = []
+    for p in range(N):
+        O.ring_append(tags, p, 1, S, W, R)
+        kept.append(p)
+        kept = kept[:S] + kept[S:][-(W + R):]
+        assert sorted(t for t in tags if t >= 0) == sorted(kept)
+    assert np.array_equal(tags, O.ring_expected_tags(N, S, W, R))
+    # what a query at length N reads: exactly its sink_window set, each in slot(p)
+    vis = O.ring_visible(tags, N, S, W)
+    assert sorted(int(t) for t in vis if t >= 0) == list(O.visible_positions(N, O.SINK_WINDOW, S, W))
+    assert np.array_equal(vis, O.window_slot_positions(N, S, W, R))
+
+
+@pytest.mark.parametrize("S,W,R,pos,T", [(4, 16, 3, 0, 100), (2, 8, 2, 30, 17), (0, 5, 4, 3, 12), (4, 16, 7, 19, 40)])
+def test_bulk_append_with_headroom_equals_sequential(S, W, R, pos, T):
+    a = np.full(S + W + R, -1, dtype=np.int64)
+    b = np.full(S + W + R, -1, dtype=np.int64)
+    if pos:
+        O.ring_append(a, 0, pos, S, W, R)
+        O.ring_append(b, 0, pos, S, W, R)
+    writes = O.ring_append(a, pos, T, S, W, R)
+    for i in range(T):
+        O.ring_append(b, pos + i, 1, S, W, R)
+    assert np.array_equal(a, b)
+    slots = [sl for _, sl in writes]
+    assert len(slots) == len(set(slots))
+
+
+def _speculate(S, W, R, gamma, n0, accepts, rollback):
+    """Run draft cycles on a ring and return the first (cycle, step, missing position) a
+    draft query fails to read with the right content, or None.
+
+    Content model: every slot holds (position, version).  The prefill writes version
+    "p"; cycle c drafts positions n..n+gamma-1 with version c.  After verification the
+    first a drafted tokens are accepted (they keep version c), the rest are rejected;
+    the next cycle starts at n + a (its first token is the target's correction).
+    """
+    C = S + W + R
+    tags = np.full(C, -1, dtype=np.int64)
+    content = {}
+    truth = {}                                           # position -> version of the accepted sequence
+    for i, sl in O.ring_append(tags, 0, n0, S, W, R):   # bulk init from the prefill
+        content[sl] = (i, "p")
+    for p in range(n0):
+        truth[p] = "p"
+    n = n0
+    for c, a in enumerate(accepts):
+        for j in range(gamma):                           # draft step j: append, then query at n + j + 1
+            p = n + j
+            (_, sl), = O.ring_append(tags, p, 1, S, W, R)
+            content[sl] = (p, c)
+            m = p + 1
+            want = {q: (truth[q] if q < n else c) for q in O.visible_positions(m, O.SINK_WINDOW, S, W)}
+            got = {}
+            for sl2, q in enumerate(O.ring_visible(tags, m, S, W)):
+                if q >= 0:
+                    got[int(q)] = content[sl2][1]
+            for q, ver in want.items():
+                if got.get(q) != ver:
+                    return (c, j, q)
+        for j in range(a):                               # accepted drafted tokens join the sequence
+            truth[n + j] = c
+        n += a
+        if rollback:
+            O.ring_rollback(tags, n)
+            assert all(t < n for t in tags)
+    return None
+
+
+@settings(max_examples=200, deadline=None)
+@given(S=st.integers(0, 6), W=st.integers(1, 24), gamma=st.integers(1, 6), extra=st.integers(0, 3),
+       n0=st.integers(1, 80), data=st.data())
+def test_rollback_with_headroom_keeps_every_needed_entry(S, W, gamma, extra, n0, data):
+    """With R >= gamma - 1 headroom slots, every draft query after any acceptance pattern reads
+    exactly its sink_window set with the accepted (or current-cycle) content."""
+    accepts = data.draw(st.lists(st.integers(1, gamma), min_size=1, max_size=8))
+    R = gamma - 1 + extra
+    assert _speculate(S, W, R, gamma, n0, accepts, rollback=True) is None
+    assert _speculate(S, W, R, gamma, n0, accepts, rollback=False) is None   # tags alone already hide rejects
+
+
+def test_rollback_without_headroom_loses_a_window_entry():
+    """The failure the headroom prevents: with R = 0 a rejected draft overwrites the slot of
+    position p - W, which the next cycle's window still needs."""
+    S, W, gamma = 4, 16, 3
+    assert _speculate(S, W, 0, gamma, 100, [1, 3], rollback=True) == (1, 0, 86)
+    assert _speculate(S, W, gamma - 1, gamma, 100, [1, 3], rollback=True) is None
+
+
+def test_ring_rollback_clears_exactly_the_rejected_positions():
+    S, W, R = 2, 5, 2
+    tags = np.full(S + W + R, -1, dtype=np.int64)
+    O.ring_append(tags, 0, 20, S, W, R)                 # holds 0, 1 and 13..19
+    cleared = O.ring_rollback(tags, 17)
+    assert sorted(cleared) == sorted(O.ring_slot(p, S, W, R) for p in (17, 18, 19))
+    assert sorted(t for t in tags if t >= 0) == [0, 1, 13, 14, 15, 16]
+    assert O.ring_rollback(tags, 17) == []              # idempotent
+
+
 def _place_paged(logical, bt_row, bs, num_blocks):
     """Build a paged pool from a logical [n][H][D] array by block-level slicing."""
     n, H, D = logical.shape
