@@ -111,10 +111,11 @@ class Step:
             self.layers.append((k, v, W.make_paged(k, v, self.bt)))
             log(f"  pool {layer} ready")
         S, Wn = wl.sink, wl.window
-        self.rk = torch.zeros((1, Hk, S + Wn, D), dtype=torch.bfloat16, device=dev)
+        self.R = R = g - 1                    # headroom for rolling back rejected drafts
+        self.rk = torch.zeros((1, Hk, S + Wn + R, D), dtype=torch.bfloat16, device=dev)
         self.rv = torch.zeros_like(self.rk)
-        self.tags = torch.full((1, S + Wn), -1, dtype=torch.int32, device=dev)
-        self.ring = W.make_ring(self.rk, self.rv, self.tags, S, Wn)
+        self.tags = torch.full((1, S + Wn + R), -1, dtype=torch.int32, device=dev)
+        self.ring = W.make_ring(self.rk, self.rv, self.tags, S, Wn, R)
         # ring holds the sinks and the last W context tokens of the draft layer's sequence
         sink_k = synth.normal((1, S, Hk, D), wl.seed, "ring_sink_k", wl.kv_scale, "bf16", dev)
         sink_v = synth.normal((1, S, Hk, D), wl.seed, "ring_sink_v", wl.kv_scale, "bf16", dev)
@@ -134,7 +135,7 @@ class Step:
         # workspaces and outputs
         lens_d = [n0 + g]
         self.ws_full = W.workspace(W.draft_workspace_bytes(W.FULL, self.sh, lens_d, chunk_full), dev)
-        self.ws_win = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, self.sh, lens_d, chunk_win, S, Wn), dev)
+        self.ws_win = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, self.sh, lens_d, chunk_win, S, Wn, R), dev)
         self.ws_ver = W.workspace(W.verify_workspace_bytes(self.sh, g + 1, [n0 + g + 1], split), dev)
         self.out_d = torch.empty((1, Hq, D), dtype=torch.float32, device=dev)
         self.lse_d = torch.empty((1, Hq), dtype=torch.float32, device=dev)
@@ -308,6 +309,8 @@ def window_measurements(step, flag, reps, dev, contexts):
     torch.cuda.synchronize()
     del flush
     res["cold_median_by_context"] = by_ctx
+    # rollback after a partial acceptance: forget the drafts past n0 + 1
+    res["ring_rollback_us"] = pct(_timed(lambda: W.ring_rollback(step.ring, [n0 + 1]), reps))["median"]
     return res
 
 
@@ -349,17 +352,18 @@ def mixed_batch(flag, reps, dev):
            "native_gbps": round(sum(lens) * Hk * D * 4 / (t * 1e-6) / 1e9, 1), "window_draft_step_us": {}}
     del ws
     for Wn in wl.windows:
-        rk = torch.zeros((B, Hk, S + Wn, D), dtype=torch.bfloat16, device=dev)
+        R = wl.gamma - 1
+        rk = torch.zeros((B, Hk, S + Wn + R, D), dtype=torch.bfloat16, device=dev)
         rv = torch.zeros_like(rk)
-        tags = torch.full((B, S + Wn), -1, dtype=torch.int32, device=dev)
-        ring = W.make_ring(rk, rv, tags, S, Wn)
+        tags = torch.full((B, S + Wn + R), -1, dtype=torch.int32, device=dev)
+        ring = W.make_ring(rk, rv, tags, S, Wn, R)
         sk = synth.normal((B, S, Hk, D), wl.seed, ("ring_sink_k", Wn), wl.kv_scale, "bf16", dev)
         sv = synth.normal((B, S, Hk, D), wl.seed, ("ring_sink_v", Wn), wl.kv_scale, "bf16", dev)
         tk = synth.normal((B, Wn, Hk, D), wl.seed, ("ring_tail_k", Wn), wl.kv_scale, "bf16", dev)
         tv = synth.normal((B, Wn, Hk, D), wl.seed, ("ring_tail_v", Wn), wl.kv_scale, "bf16", dev)
         W.ring_append(sh, ring, sk, sv, [0] * B)
         W.ring_append(sh, ring, tk, tv, [n - Wn for n in lens])
-        wsw = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, lens, 0, S, Wn), dev)
+        wsw = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, lens, 0, S, Wn, R), dev)
 
         def window():
             W.combine(W.draft_attn(W.SINK_WINDOW | flag, sh, q, lens, wsw, ring=ring), out, lse)

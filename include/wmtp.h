@@ -106,12 +106,21 @@ typedef struct wmtp_paged {
   int64_t        num_blocks;          /* physical blocks in k and v               */
 } wmtp_paged;
 
+/* The compact ring of the windowed draft (Windowed-MTP summary, Abstract).
+ * Sinks keep slots 0..S-1; position p >= S lives in slot S + (p - S) mod (W+R);
+ * slot_pos records the position a slot holds.  A draft query at length n
+ * reads every slot whose position is in {0..S-1} or {n-W..n-1} and < n.  The
+ * R headroom slots absorb drafted tokens that verification rejects: with
+ * R >= gamma - 1 (gamma drafted tokens per cycle, at least one accepted), a
+ * rejected token never overwrites an entry a later window still needs, so
+ * rolling back costs nothing but, optionally, wmtp_ring_rollback. */
 typedef struct wmtp_ring {
-  void*    k;          /* device, [batch][H_kv][sink+window][D]  */
-  void*    v;          /* device, same layout as k               */
-  int32_t* slot_pos;   /* device, [batch][sink+window]           */
-  int32_t  sink;       /* S >= 0                                 */
-  int32_t  window;     /* W >= 1                                 */
+  void*    k;          /* device, [batch][H_kv][S+W+R][D]                  */
+  void*    v;          /* device, same layout as k                         */
+  int32_t* slot_pos;   /* device, [batch][S+W+R]: position held, -1 = none */
+  int32_t  sink;       /* S >= 0                                           */
+  int32_t  window;     /* W >= 1                                           */
+  int32_t  headroom;   /* R >= 0 extra slots in the cycle                  */
 } wmtp_ring;
 
 /* Split-K partial results, written by wmtp_draft_attn / wmtp_verify_attn into
@@ -131,10 +140,11 @@ typedef struct wmtp_partials {
 /* ---------------------------------------------------------------- planning (host only) */
 
 /* Bytes of workspace wmtp_draft_attn needs.  Arguments as for wmtp_draft_attn
- * (sink/window are read only in WMTP_SINK_WINDOW mode).  Returns >= 0 bytes or
- * a negative WMTP_E* code.  Makes no HIP call. */
+ * (sink/window/headroom, the ring's S/W/R, are read only in WMTP_SINK_WINDOW
+ * mode).  Returns >= 0 bytes or a negative WMTP_E* code.  Makes no HIP call. */
 int64_t wmtp_draft_workspace_bytes(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens_host,
-                                   int32_t batch, int32_t chunk_tokens, int32_t sink, int32_t window);
+                                   int32_t batch, int32_t chunk_tokens, int32_t sink, int32_t window,
+                                   int32_t headroom);
 
 /* Bytes of workspace wmtp_verify_attn needs.  Makes no HIP call. */
 int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const int32_t* seq_lens_host,
@@ -192,12 +202,21 @@ int wmtp_combine(const wmtp_partials* parts, void* out, int32_t out_dtype, float
 /* Append t_new tokens per sequence to the compact ring (Windowed-MTP summary,
  * Abstract: the ring holds the draft's window).  Token i of sequence b has
  * absolute position p = pos_host[b] + i (pos_host: host, >= 0) and is written
- * to slot(p), with slot_pos[b][slot(p)] = p, only if p < sink or
- * p > pos_host[b] + t_new - 1 - window (it can still be visible after the
- * append); so an append longer than the window writes each slot once.
+ * to slot(p), with slot_pos[b][slot(p)] = p, only if p < S or
+ * p > pos_host[b] + t_new - 1 - (W + R) (it survives the append); so an append
+ * longer than the cycle writes each slot once and equals appending the tokens
+ * one by one.  t_new = n with pos 0 initialises the ring from a prefill.
  * k_new, v_new: device [batch][t_new][H_kv][D]. */
 int wmtp_ring_append(const wmtp_shape* shape, const wmtp_ring* ring, const void* k_new, const void* v_new,
                      const int32_t* pos_host, int32_t batch, int32_t t_new, void* stream);
+
+/* After verification accepted the first tokens of a draft cycle: forget every
+ * ring entry at a position >= seq_lens_host[b] (slot_pos becomes -1) for each
+ * sequence b.  Optional when appends stay in order (the draft query's
+ * position check already hides them, and the next append at a position
+ * overwrites it); it leaves the ring holding only accepted positions.
+ * Touches slot_pos only; seq_lens_host: host [batch], each >= 0. */
+int wmtp_ring_rollback(const wmtp_ring* ring, const int32_t* seq_lens_host, int32_t batch, void* stream);
 
 /* Write t_new tokens per sequence into the paged pool at positions
  * pos_host[b] + i through the block table (the native draft's pool and each
@@ -216,14 +235,17 @@ int wmtp_debug_resolve_paged(const wmtp_paged* kv, int32_t num_kv_heads, int32_t
                              int32_t h, const int32_t* positions, int32_t n, int64_t* offsets_out,
                              void* stream);
 
-/* Ring slot of every listed position: slots_out[i] = slot(positions[i]).
+/* Ring slot of every listed position: slots_out[i] = slot(positions[i]) for a
+ * ring of S = sink, W = window, R = headroom.
  * positions: device int32 [n] (>= 0); slots_out: device int32 [n]. */
-int wmtp_debug_resolve_ring(int32_t sink, int32_t window, const int32_t* positions, int32_t n,
+int wmtp_debug_resolve_ring(int32_t sink, int32_t window, int32_t headroom, const int32_t* positions, int32_t n,
                             int32_t* slots_out, void* stream);
 
 /* For a query at length n, the position each ring slot must hold for the
- * sink+window visible set (-1 if the slot holds none).  out: device int32 [sink+window]. */
-int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t n, int32_t* out, void* stream);
+ * sink+window visible set (-1 if the slot holds none).
+ * out: device int32 [sink+window+headroom]. */
+int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t headroom, int32_t n, int32_t* out,
+                                void* stream);
 
 /* ---------------------------------------------------------------- measurement */
 

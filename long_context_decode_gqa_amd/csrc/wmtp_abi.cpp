@@ -79,8 +79,8 @@ int check_paged(const wmtp_paged* kv, bool need_table) {
 
 int check_ring(const wmtp_ring* r) {
   if (!r || !r->k || !r->v || !r->slot_pos) return WMTP_EINVAL;
-  if (r->sink < 0 || r->window < 1) return WMTP_EINVAL;
-  if ((int64_t)r->sink + r->window > (int64_t)INT32_MAX / 2) return WMTP_EINVAL;
+  if (r->sink < 0 || r->window < 1 || r->headroom < 0) return WMTP_EINVAL;
+  if ((int64_t)r->sink + r->window + r->headroom > (int64_t)INT32_MAX / 2) return WMTP_EINVAL;
   if (!aligned(r->k, 16) || !aligned(r->v, 16) || !aligned(r->slot_pos, 4)) return WMTP_EALIGN;
   return WMTP_OK;
 }
@@ -113,18 +113,22 @@ int make_plan(const int64_t* vis, int batch, int chunk, int rows, int head_dim, 
 }
 
 int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, int32_t batch, int32_t chunk,
-               int32_t sink, int32_t window, Plan* p, int32_t* chunk_out) {
+               int32_t sink, int32_t window, int32_t headroom, Plan* p, int32_t* chunk_out) {
   int st = check_shape(shape);
   if (st) return st;
   const int base_mode = mode & 0xF;
   if (base_mode != WMTP_FULL && base_mode != WMTP_SINK_WINDOW) return WMTP_EINVAL;
   if ((mode & ~0xF) & ~WMTP_DRAFT_FAST_PV) return WMTP_EINVAL;
   if (!seq_lens || batch < 1 || batch > WMTP_MAX_BATCH) return WMTP_EINVAL;
-  if (base_mode == WMTP_SINK_WINDOW && (sink < 0 || window < 1)) return WMTP_EINVAL;
+  if (base_mode == WMTP_SINK_WINDOW &&
+      (sink < 0 || window < 1 || headroom < 0 || (int64_t)sink + window + headroom > (int64_t)INT32_MAX / 2))
+    return WMTP_EINVAL;
+  // window mode scans the ring's slots that can hold an entry: min(n, S+W+R)
+  const int64_t ring_slots = (int64_t)sink + window + headroom;
   int64_t vis[WMTP_MAX_BATCH];
   for (int b = 0; b < batch; ++b) {
     if (seq_lens[b] < 0) return WMTP_EINVAL;
-    vis[b] = base_mode == WMTP_FULL ? seq_lens[b] : std::min<int64_t>(seq_lens[b], (int64_t)sink + window);
+    vis[b] = base_mode == WMTP_FULL ? seq_lens[b] : std::min<int64_t>(seq_lens[b], ring_slots);
   }
   if (chunk == 0)
     chunk = base_mode == WMTP_FULL ? default_split(vis, batch, shape->num_kv_heads, kFullSlots, kFullMinSplit)
@@ -186,10 +190,10 @@ int launch_status(hipError_t e) { return e == hipSuccess ? WMTP_OK : WMTP_ELAUNC
 extern "C" {
 
 int64_t wmtp_draft_workspace_bytes(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens_host, int32_t batch,
-                                   int32_t chunk_tokens, int32_t sink, int32_t window) {
+                                   int32_t chunk_tokens, int32_t sink, int32_t window, int32_t headroom) {
   Plan p;
   int32_t chunk = 0;
-  const int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, &p, &chunk);
+  const int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, headroom, &p, &chunk);
   return st ? st : p.bytes;
 }
 
@@ -205,16 +209,17 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
                     const int32_t* seq_lens_host, int32_t batch, int32_t chunk_tokens, void* workspace,
                     size_t workspace_bytes, wmtp_partials* parts, void* stream) {
   const int base_mode = mode & 0xF;
-  int32_t sink = 0, window = 1;
+  int32_t sink = 0, window = 1, headroom = 0;
   if (base_mode == WMTP_SINK_WINDOW) {
     const int st = check_ring(ring);
     if (st) return st;
     sink = ring->sink;
     window = ring->window;
+    headroom = ring->headroom;
   }
   Plan p;
   int32_t chunk = 0;
-  int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, &p, &chunk);
+  int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, headroom, &p, &chunk);
   if (st) return st;
   if (!q || !parts) return WMTP_EINVAL;
   if (!aligned(q, 16)) return WMTP_EALIGN;
@@ -243,7 +248,7 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
     a.k = ring->k;
     a.v = ring->v;
     a.slot_pos = ring->slot_pos;
-    a.slots = ring->sink + ring->window;
+    a.slots = ring->sink + ring->window + ring->headroom;
     a.sink = ring->sink;
     a.window = ring->window;
   }
@@ -353,7 +358,25 @@ int wmtp_ring_append(const wmtp_shape* shape, const wmtp_ring* ring, const void*
   a.slot_pos = ring->slot_pos;
   a.sink = ring->sink;
   a.window = ring->window;
+  a.headroom = ring->headroom;
   return launch_status(launch_ring_append(a, batch, static_cast<hipStream_t>(stream)));
+}
+
+int wmtp_ring_rollback(const wmtp_ring* ring, const int32_t* seq_lens_host, int32_t batch, void* stream) {
+  int st = check_ring(ring);
+  if (st) return st;
+  if (!seq_lens_host || batch < 1 || batch > WMTP_MAX_BATCH) return WMTP_EINVAL;
+  AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens_host[b] < 0) return WMTP_EINVAL;
+    a.pos[b] = seq_lens_host[b];
+  }
+  a.slot_pos = ring->slot_pos;
+  a.sink = ring->sink;
+  a.window = ring->window;
+  a.headroom = ring->headroom;
+  return launch_status(launch_ring_rollback(a, batch, static_cast<hipStream_t>(stream)));
 }
 
 int wmtp_paged_append(const wmtp_shape* shape, const wmtp_paged* kv, const void* k_new, const void* v_new,
@@ -387,17 +410,20 @@ int wmtp_debug_resolve_paged(const wmtp_paged* kv, int32_t num_kv_heads, int32_t
                                                   static_cast<hipStream_t>(stream)));
 }
 
-int wmtp_debug_resolve_ring(int32_t sink, int32_t window, const int32_t* positions, int32_t n, int32_t* slots_out,
-                            void* stream) {
-  if (sink < 0 || window < 1 || n < 0 || (n > 0 && (!positions || !slots_out))) return WMTP_EINVAL;
-  return launch_status(
-      launch_debug_resolve_ring(sink, window, positions, n, slots_out, static_cast<hipStream_t>(stream)));
+int wmtp_debug_resolve_ring(int32_t sink, int32_t window, int32_t headroom, const int32_t* positions, int32_t n,
+                            int32_t* slots_out, void* stream) {
+  if (sink < 0 || window < 1 || headroom < 0 || n < 0 || (n > 0 && (!positions || !slots_out))) return WMTP_EINVAL;
+  if ((int64_t)sink + window + headroom > INT32_MAX / 2) return WMTP_EINVAL;
+  return launch_status(launch_debug_resolve_ring(sink, window + headroom, positions, n, slots_out,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
-int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t n, int32_t* out, void* stream) {
-  if (sink < 0 || window < 1 || n < 0 || !out) return WMTP_EINVAL;
-  if ((int64_t)sink + window > INT32_MAX / 2) return WMTP_EINVAL;
-  return launch_status(launch_debug_window_positions(sink, window, n, out, static_cast<hipStream_t>(stream)));
+int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t headroom, int32_t n, int32_t* out,
+                                void* stream) {
+  if (sink < 0 || window < 1 || headroom < 0 || n < 0 || !out) return WMTP_EINVAL;
+  if ((int64_t)sink + window + headroom > INT32_MAX / 2) return WMTP_EINVAL;
+  return launch_status(
+      launch_debug_window_positions(sink, window, headroom, n, out, static_cast<hipStream_t>(stream)));
 }
 
 int wmtp_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {

@@ -76,7 +76,7 @@ struct SplitArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t bt_stride;            // max_blocks_per_seq
-  int32_t slots;                // ring slots (sink + window)
+  int32_t slots;                // ring slots (sink + window + headroom)
   int32_t sink;
   int32_t window;
   int32_t chunk;                // entries per split
@@ -115,9 +115,10 @@ __device__ __forceinline__ int64_t paged_elem_offset(const int32_t* bt_row, int6
   return ((blk * num_kv_heads + h) * kBlock + (t % kBlock)) * (int64_t)head_dim;
 }
 
-// Compact ring: sinks keep slots 0..S-1, later positions cycle through S..S+W-1.
-__device__ __forceinline__ int32_t ring_slot(int32_t p, int32_t sink, int32_t window) {
-  return p < sink ? p : sink + (p - sink) % window;
+// Compact ring: sinks keep slots 0..S-1, later positions cycle through the
+// `cycle` = W + R slots S..S+cycle-1 (R headroom slots absorb rejected drafts).
+__device__ __forceinline__ int32_t ring_slot(int32_t p, int32_t sink, int32_t cycle) {
+  return p < sink ? p : sink + (p - sink) % cycle;
 }
 
 // Is absolute position p in the sink + window visible set of a query at length n?

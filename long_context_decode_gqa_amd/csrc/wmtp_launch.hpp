@@ -35,7 +35,8 @@ struct AppendArgs {
   int32_t bt_stride;
   int32_t sink;
   int32_t window;
-  int32_t pos[WMTP_MAX_BATCH];
+  int32_t headroom;
+  int32_t pos[WMTP_MAX_BATCH];  // first new position (appends) or kept length (rollback)
 };
 
 hipError_t launch_draft(int dtype, int head_dim, int group, bool window, bool pv_dot2, const SplitArgs& a,
@@ -46,12 +47,13 @@ hipError_t launch_verify(int head_dim, int group, bool single_query, const Split
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_ring_append(const AppendArgs& a, int batch, hipStream_t st);
 hipError_t launch_paged_append(const AppendArgs& a, int batch, hipStream_t st);
+hipError_t launch_ring_rollback(const AppendArgs& a, int batch, hipStream_t st);
 hipError_t launch_debug_resolve_paged(const int32_t* bt_row, int32_t row_len, int64_t max_block, int num_kv_heads,
                                       int head_dim, int h, const int32_t* positions, int n, int64_t* out,
                                       hipStream_t st);
-hipError_t launch_debug_resolve_ring(int sink, int window, const int32_t* positions, int n, int32_t* out,
+hipError_t launch_debug_resolve_ring(int sink, int cycle, const int32_t* positions, int n, int32_t* out,
                                      hipStream_t st);
-hipError_t launch_debug_window_positions(int sink, int window, int n, int32_t* out, hipStream_t st);
+hipError_t launch_debug_window_positions(int sink, int window, int headroom, int n, int32_t* out, hipStream_t st);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t st);
 
 }  // namespace wmtp

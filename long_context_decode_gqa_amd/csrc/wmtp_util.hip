@@ -105,9 +105,10 @@ __global__ __launch_bounds__(256) void ring_append_kernel(const AppendArgs a) {
   const int i = blockIdx.x % a.t_new;
   const int p = a.pos[b] + i;
   const int last = a.pos[b] + a.t_new - 1;
-  if (!(p < a.sink || p > last - a.window)) return;       // overwritten later in this append
-  const int slots = a.sink + a.window;
-  const int slot = ring_slot(p, a.sink, a.window);
+  const int cycle = a.window + a.headroom;
+  if (!(p < a.sink || p > last - cycle)) return;          // overwritten later in this append
+  const int slots = a.sink + cycle;
+  const int slot = ring_slot(p, a.sink, cycle);
   const int pieces = a.row_bytes / 16;                     // per head
   const int64_t src_tok = ((int64_t)b * a.t_new + i) * a.num_kv_heads * a.row_bytes;
   for (int j = threadIdx.x; j < 2 * a.num_kv_heads * pieces; j += blockDim.x) {
@@ -143,6 +144,22 @@ __global__ __launch_bounds__(256) void paged_append_kernel(const AppendArgs a) {
   }
 }
 
+// Rollback: one workgroup per sequence clears the tag of every slot holding a
+// position >= the kept length a.pos[b].
+__global__ __launch_bounds__(256) void ring_rollback_kernel(const AppendArgs a) {
+  const int b = blockIdx.x;
+  const int slots = a.sink + a.window + a.headroom;
+  int32_t* tags = a.slot_pos + (int64_t)b * slots;
+  for (int s = threadIdx.x; s < slots; s += blockDim.x)
+    if (tags[s] >= a.pos[b]) tags[s] = -1;
+}
+
+hipError_t launch_ring_rollback(const AppendArgs& a, int batch, hipStream_t st) {
+  if (batch <= 0) return hipSuccess;
+  ring_rollback_kernel<<<batch, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_ring_append(const AppendArgs& a, int batch, hipStream_t st) {
   const int grid = batch * a.t_new;
   if (grid <= 0) return hipSuccess;
@@ -168,16 +185,16 @@ __global__ void debug_resolve_paged_kernel(const int32_t* bt_row, int32_t row_le
                                              : paged_elem_offset(bt_row, p, h, num_kv_heads, head_dim, max_block);
 }
 
-__global__ void debug_resolve_ring_kernel(int sink, int window, const int32_t* positions, int n, int32_t* out) {
+__global__ void debug_resolve_ring_kernel(int sink, int cycle, const int32_t* positions, int n, int32_t* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = ring_slot(positions[i], sink, window);
+  if (i < n) out[i] = ring_slot(positions[i], sink, cycle);
 }
 
 // Slot -> visible position for a query at length n: slot s < S holds sink s;
 // ring slot s holds the most recent p < n with slot(p) = s, if it is visible.
-__global__ void debug_window_positions_kernel(int sink, int window, int n, int32_t* out) {
+__global__ void debug_window_positions_kernel(int sink, int window, int cycle, int n, int32_t* out) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s >= sink + window) return;
+  if (s >= sink + cycle) return;
   int32_t p;
   if (s < sink) {
     p = s < n ? s : -1;
@@ -185,8 +202,8 @@ __global__ void debug_window_positions_kernel(int sink, int window, int n, int32
     p = -1;
   } else {
     const int32_t last = n - 1;                          // newest position, last >= sink
-    const int32_t r = (last - sink) % window;            // its ring index
-    const int32_t d = ((r - (s - sink)) % window + window) % window;
+    const int32_t r = (last - sink) % cycle;             // its ring index
+    const int32_t d = ((r - (s - sink)) % cycle + cycle) % cycle;
     p = last - d;                                        // newest position mapped to slot s
     if (p < sink || !window_visible(p, n, sink, window)) p = -1;
   }
@@ -202,17 +219,17 @@ hipError_t launch_debug_resolve_paged(const int32_t* bt_row, int32_t row_len, in
   return hipGetLastError();
 }
 
-hipError_t launch_debug_resolve_ring(int sink, int window, const int32_t* positions, int n, int32_t* out,
+hipError_t launch_debug_resolve_ring(int sink, int cycle, const int32_t* positions, int n, int32_t* out,
                                      hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  debug_resolve_ring_kernel<<<(n + 255) / 256, 256, 0, st>>>(sink, window, positions, n, out);
+  debug_resolve_ring_kernel<<<(n + 255) / 256, 256, 0, st>>>(sink, cycle, positions, n, out);
   return hipGetLastError();
 }
 
-hipError_t launch_debug_window_positions(int sink, int window, int n, int32_t* out, hipStream_t st) {
-  const int slots = sink + window;
+hipError_t launch_debug_window_positions(int sink, int window, int headroom, int n, int32_t* out, hipStream_t st) {
+  const int slots = sink + window + headroom;
   if (slots <= 0) return hipSuccess;
-  debug_window_positions_kernel<<<(slots + 255) / 256, 256, 0, st>>>(sink, window, n, out);
+  debug_window_positions_kernel<<<(slots + 255) / 256, 256, 0, st>>>(sink, window, window + headroom, n, out);
   return hipGetLastError();
 }
 

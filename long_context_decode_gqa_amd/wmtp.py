@@ -47,7 +47,7 @@ class Paged(ctypes.Structure):
 
 class Ring(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slot_pos", ctypes.c_void_p),
-                ("sink", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("sink", ctypes.c_int32), ("window", ctypes.c_int32), ("headroom", ctypes.c_int32)]
 
 
 class Partials(ctypes.Structure):
@@ -58,7 +58,7 @@ class Partials(ctypes.Structure):
 
 EXPORTS = (
     "wmtp_draft_workspace_bytes", "wmtp_verify_workspace_bytes", "wmtp_draft_attn", "wmtp_verify_attn",
-    "wmtp_combine", "wmtp_ring_append", "wmtp_paged_append", "wmtp_debug_resolve_paged",
+    "wmtp_combine", "wmtp_ring_append", "wmtp_ring_rollback", "wmtp_paged_append", "wmtp_debug_resolve_paged",
     "wmtp_debug_resolve_ring", "wmtp_debug_window_positions", "wmtp_stream_read", "wmtp_status_str",
     "wmtp_version",
 )
@@ -77,7 +77,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sp, pp, rp, tp = ctypes.POINTER(Shape), ctypes.POINTER(Paged), ctypes.POINTER(Ring), ctypes.POINTER(Partials)
-    lib.wmtp_draft_workspace_bytes.argtypes = [I32, sp, P, I32, I32, I32, I32]
+    lib.wmtp_draft_workspace_bytes.argtypes = [I32, sp, P, I32, I32, I32, I32, I32]
     lib.wmtp_draft_workspace_bytes.restype = I64
     lib.wmtp_verify_workspace_bytes.argtypes = [sp, I32, P, I32, I32]
     lib.wmtp_verify_workspace_bytes.restype = I64
@@ -90,12 +90,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.wmtp_ring_append.argtypes = [sp, rp, P, P, P, I32, I32, P]
     lib.wmtp_ring_append.restype = ctypes.c_int
     lib.wmtp_paged_append.argtypes = [sp, pp, P, P, P, I32, I32, P]
+    lib.wmtp_ring_rollback.argtypes = [rp, P, I32, P]
+    lib.wmtp_ring_rollback.restype = ctypes.c_int
     lib.wmtp_paged_append.restype = ctypes.c_int
     lib.wmtp_debug_resolve_paged.argtypes = [pp, I32, I32, I32, I32, P, I32, P, P]
     lib.wmtp_debug_resolve_paged.restype = ctypes.c_int
-    lib.wmtp_debug_resolve_ring.argtypes = [I32, I32, P, I32, P, P]
+    lib.wmtp_debug_resolve_ring.argtypes = [I32, I32, I32, P, I32, P, P]
     lib.wmtp_debug_resolve_ring.restype = ctypes.c_int
-    lib.wmtp_debug_window_positions.argtypes = [I32, I32, I32, P, P]
+    lib.wmtp_debug_window_positions.argtypes = [I32, I32, I32, I32, P, P]
     lib.wmtp_debug_window_positions.restype = ctypes.c_int
     lib.wmtp_stream_read.argtypes = [P, I64, P, I32, P]
     lib.wmtp_stream_read.restype = ctypes.c_int
@@ -144,18 +146,19 @@ def make_paged(k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor) -> P
     return Paged(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), BLOCK_SIZE, block_table.shape[1], k.shape[0])
 
 
-def make_ring(k: torch.Tensor, v: torch.Tensor, slot_pos: torch.Tensor, sink: int, window: int) -> Ring:
-    """k, v: [batch][H_kv][sink+window][D]; slot_pos: int32 [batch][sink+window] (device)."""
+def make_ring(k: torch.Tensor, v: torch.Tensor, slot_pos: torch.Tensor, sink: int, window: int,
+              headroom: int = 0) -> Ring:
+    """k, v: [batch][H_kv][S+W+R][D]; slot_pos: int32 [batch][S+W+R] (device); R = headroom."""
     assert slot_pos.dtype == torch.int32
-    return Ring(k.data_ptr(), v.data_ptr(), slot_pos.data_ptr(), int(sink), int(window))
+    return Ring(k.data_ptr(), v.data_ptr(), slot_pos.data_ptr(), int(sink), int(window), int(headroom))
 
 
 # ---------------------------------------------------------------- planning
 def draft_workspace_bytes(mode: int, shape: Shape, seq_lens: Sequence[int], chunk_tokens: int = 0,
-                          sink: int = 0, window: int = 1) -> int:
+                          sink: int = 0, window: int = 1, headroom: int = 0) -> int:
     return _check("wmtp_draft_workspace_bytes", load().wmtp_draft_workspace_bytes(
         mode, ctypes.byref(shape), ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), chunk_tokens,
-        sink, window))
+        sink, window, headroom))
 
 
 def verify_workspace_bytes(shape: Shape, t_q: int, seq_lens: Sequence[int], split_tokens: int = 0) -> int:
@@ -204,6 +207,12 @@ def ring_append(shape: Shape, ring: Ring, k_new: torch.Tensor, v_new: torch.Tens
         ctypes.cast(_lens(pos), ctypes.c_void_p), len(pos), k_new.shape[1], _stream(stream)))
 
 
+def ring_rollback(ring: Ring, seq_lens: Sequence[int], stream=None) -> None:
+    """Forget ring entries at positions >= seq_lens[b] (drafted tokens verification rejected)."""
+    _check("wmtp_ring_rollback", load().wmtp_ring_rollback(
+        ctypes.byref(ring), ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), _stream(stream)))
+
+
 def paged_append(shape: Shape, paged: Paged, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
                  stream=None) -> None:
     _check("wmtp_paged_append", load().wmtp_paged_append(
@@ -221,17 +230,18 @@ def debug_resolve_paged(paged: Paged, num_kv_heads: int, head_dim: int, b: int, 
     return out
 
 
-def debug_resolve_ring(sink: int, window: int, positions: torch.Tensor, stream=None) -> torch.Tensor:
+def debug_resolve_ring(sink: int, window: int, positions: torch.Tensor, headroom: int = 0,
+                       stream=None) -> torch.Tensor:
     out = torch.empty(positions.numel(), dtype=torch.int32, device=positions.device)
     _check("wmtp_debug_resolve_ring", load().wmtp_debug_resolve_ring(
-        sink, window, positions.data_ptr(), positions.numel(), out.data_ptr(), _stream(stream)))
+        sink, window, headroom, positions.data_ptr(), positions.numel(), out.data_ptr(), _stream(stream)))
     return out
 
 
-def debug_window_positions(sink: int, window: int, n: int, device, stream=None) -> torch.Tensor:
-    out = torch.empty(sink + window, dtype=torch.int32, device=device)
+def debug_window_positions(sink: int, window: int, n: int, device, headroom: int = 0, stream=None) -> torch.Tensor:
+    out = torch.empty(sink + window + headroom, dtype=torch.int32, device=device)
     _check("wmtp_debug_window_positions", load().wmtp_debug_window_positions(
-        sink, window, n, out.data_ptr(), _stream(stream)))
+        sink, window, headroom, n, out.data_ptr(), _stream(stream)))
     return out
 
 

@@ -56,11 +56,12 @@ class PagedCache:
 
 
 class RingCache:
-    def __init__(self, batch, hk, d, sink, window, dtype):
-        self.k = torch.zeros((batch, hk, sink + window, d), dtype=dtype, device=DEV)
+    def __init__(self, batch, hk, d, sink, window, dtype, headroom=0):
+        slots = sink + window + headroom
+        self.k = torch.zeros((batch, hk, slots, d), dtype=dtype, device=DEV)
         self.v = torch.zeros_like(self.k)
-        self.tags = torch.full((batch, sink + window), -1, dtype=torch.int32, device=DEV)
-        self.desc = W.make_ring(self.k, self.v, self.tags, sink, window)
+        self.tags = torch.full((batch, slots), -1, dtype=torch.int32, device=DEV)
+        self.desc = W.make_ring(self.k, self.v, self.tags, sink, window, headroom)
 
 
 def max_err(gpu: torch.Tensor, ref: np.ndarray) -> float:

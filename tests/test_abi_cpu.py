@@ -54,8 +54,8 @@ def paged(k=FAKE, v=FAKE, bt=FAKE, bs=16, mb=100, nb=100):
     return W.Paged(k, v, bt, bs, mb, nb)
 
 
-def ring(k=FAKE, v=FAKE, tags=FAKE, s=4, w=64):
-    return W.Ring(k, v, tags, s, w)
+def ring(k=FAKE, v=FAKE, tags=FAKE, s=4, w=64, r=0):
+    return W.Ring(k, v, tags, s, w, r)
 
 
 def draft(mode=W.FULL, sh=None, q=FAKE, kv="default", rg="default", seq=(1000,), chunk=0, ws=FAKE, wsb=1 << 30,
@@ -96,13 +96,15 @@ def draft(mode=W.FULL, sh=None, q=FAKE, kv="default", rg="default", seq=(1000,),
     (dict(mode=W.SINK_WINDOW, rg=None), W.EINVAL),
     (dict(mode=W.SINK_WINDOW, rg=ring(w=0)), W.EINVAL),
     (dict(mode=W.SINK_WINDOW, rg=ring(s=-1)), W.EINVAL),
+    (dict(mode=W.SINK_WINDOW, rg=ring(r=-1)), W.EINVAL),
+    (dict(mode=W.SINK_WINDOW, rg=ring(w=1 << 30, r=1 << 30)), W.EINVAL),
     (dict(mode=W.SINK_WINDOW, rg=ring(k=FAKE_ODD)), W.EALIGN),
 ])
 def test_draft_argument_checks(kwargs, status):
     if status is None:
         # the valid call must pass every check; planning alone shows that without launching
         sh = shape()
-        n = W.load().wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(1000), 1, 0, 0, 1)
+        n = W.load().wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(1000), 1, 0, 0, 1, 0)
         assert n > 0
         return
     assert draft(**kwargs) == status
@@ -111,10 +113,10 @@ def test_draft_argument_checks(kwargs, status):
 def test_draft_batch_limits():
     lib = W.load()
     sh = shape()
-    assert lib.wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(1), 0, 0, 0, 1) == W.EINVAL
+    assert lib.wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(1), 0, 0, 0, 1, 0) == W.EINVAL
     big = (ctypes.c_int32 * 65)(*([10] * 65))
     assert lib.wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), ctypes.cast(big, ctypes.c_void_p), 65, 0, 0,
-                                          1) == W.EINVAL
+                                          1, 0) == W.EINVAL
 
 
 def _splits_of(ws_bytes, rows, d):
@@ -260,6 +262,29 @@ def test_append_checks():
     assert lib.wmtp_paged_append(ctypes.byref(sh), None, FAKE, FAKE, lens(0), 1, 1, None) == W.EINVAL
 
 
+def test_rollback_checks():
+    lib = W.load()
+    r = ring(r=2)
+    assert lib.wmtp_ring_rollback(None, lens(10), 1, None) == W.EINVAL
+    assert lib.wmtp_ring_rollback(ctypes.byref(r), None, 1, None) == W.EINVAL
+    assert lib.wmtp_ring_rollback(ctypes.byref(r), lens(-1), 1, None) == W.EINVAL
+    assert lib.wmtp_ring_rollback(ctypes.byref(r), lens(10), 0, None) == W.EINVAL
+    assert lib.wmtp_ring_rollback(ctypes.byref(r), lens(10), 65, None) == W.EINVAL
+    bad = ring(r=-1)
+    assert lib.wmtp_ring_rollback(ctypes.byref(bad), lens(10), 1, None) == W.EINVAL
+
+
+def test_window_workspace_covers_headroom_slots():
+    # the window draft scans min(n, S+W+R) slots: R extra entries in the plan
+    sh = shape()
+    assert W.draft_workspace_bytes(W.SINK_WINDOW, sh, [1 << 20], 64, 4, 4096, 2) == \
+        W.draft_workspace_bytes(W.FULL, sh, [4102], 64)
+    assert W.draft_workspace_bytes(W.SINK_WINDOW, sh, [100], 64, 4, 4096, 2) == \
+        W.draft_workspace_bytes(W.FULL, sh, [100], 64)
+    with pytest.raises(W.WmtpError):
+        W.draft_workspace_bytes(W.SINK_WINDOW, sh, [100], 64, 4, 4096, -1)
+
+
 def test_stream_read_checks():
     lib = W.load()
     assert lib.wmtp_stream_read(None, 1024, FAKE, 4, None) == W.EINVAL
@@ -274,6 +299,8 @@ def test_debug_hook_checks():
     kv = paged()
     assert lib.wmtp_debug_resolve_paged(ctypes.byref(kv), 2, 256, 0, 2, FAKE, 1, FAKE, None) == W.EINVAL   # h >= H_kv
     assert lib.wmtp_debug_resolve_paged(None, 2, 256, 0, 0, FAKE, 1, FAKE, None) == W.EINVAL
-    assert lib.wmtp_debug_resolve_ring(4, 0, FAKE, 1, FAKE, None) == W.EINVAL
-    assert lib.wmtp_debug_window_positions(-1, 4, 10, FAKE, None) == W.EINVAL
-    assert lib.wmtp_debug_window_positions(4, 4, 10, None, None) == W.EINVAL
+    assert lib.wmtp_debug_resolve_ring(4, 0, 0, FAKE, 1, FAKE, None) == W.EINVAL
+    assert lib.wmtp_debug_window_positions(-1, 4, 0, 10, FAKE, None) == W.EINVAL
+    assert lib.wmtp_debug_window_positions(4, 4, 0, 10, None, None) == W.EINVAL
+    assert lib.wmtp_debug_window_positions(4, 4, -1, 10, FAKE, None) == W.EINVAL
+    assert lib.wmtp_debug_resolve_ring(4, 4, -1, FAKE, 1, FAKE, None) == W.EINVAL

@@ -110,6 +110,115 @@ def test_paged_append_bit_exact():
     assert torch.equal(kf[untouched], before_k.reshape(-1)[untouched])
 
 
+# ============================================================== headroom and rollback
+@pytest.mark.parametrize("S,Wn,R", [(4, 4096, 2), (0, 7, 3), (1, 1, 5), (16, 1000, 7)])
+def test_resolve_ring_with_headroom_bit_exact(S, Wn, R):
+    rng = np.random.default_rng(S * 7 + Wn + R)
+    pos = np.concatenate([np.arange(0, 300), rng.integers(0, 1 << 24, size=3000)]).astype(np.int32)
+    got = W.debug_resolve_ring(S, Wn, torch.from_numpy(pos).to(DEV), headroom=R).cpu().numpy()
+    assert np.array_equal(got, np.array([O.ring_slot(int(p), S, Wn, R) for p in pos]))
+    for n in [0, 1, S, S + Wn, S + Wn + R, S + Wn + R + 1, 3 * Wn + 5, 1048579]:
+        g = W.debug_window_positions(S, Wn, n, DEV, headroom=R).cpu().numpy()
+        assert np.array_equal(g, O.window_slot_positions(n, S, Wn, R)), n
+
+
+def test_ring_append_with_headroom_bit_exact():
+    S, Wn, R, Hk, D, B = 4, 40, 3, 2, 64, 2
+    sh = W.make_shape(4, Hk, D, torch.bfloat16)
+    ring = RingCache(B, Hk, D, S, Wn, torch.bfloat16, headroom=R)
+    total = 300
+    k_all = synth.normal((B, total, Hk, D), 9, "rk", 1.0, "bf16")
+    v_all = synth.normal((B, total, Hk, D), 9, "rv", 1.0, "bf16")
+    tags = [np.full(S + Wn + R, -1, dtype=np.int64) for _ in range(B)]
+    at = 0
+    for t_new in [3, 1, 70, 1, 1, 45, 100, 1, 2, 50]:
+        if at + t_new > total:
+            break
+        W.ring_append(sh, ring.desc, k_all[:, at:at + t_new].contiguous().to(DEV),
+                      v_all[:, at:at + t_new].contiguous().to(DEV), [at] * B)
+        for b in range(B):
+            O.ring_append(tags[b], at, t_new, S, Wn, R)
+        at += t_new
+        torch.cuda.synchronize()
+        got = ring.tags.cpu().numpy()
+        kr, vr = ring.k.cpu(), ring.v.cpu()
+        for b in range(B):
+            assert np.array_equal(got[b], tags[b])
+            for s_, p in enumerate(tags[b]):
+                if p >= 0:
+                    assert torch.equal(kr[b, :, s_], k_all[b, p]) and torch.equal(vr[b, :, s_], v_all[b, p])
+
+
+@pytest.mark.parametrize("fast_pv", [False, True])
+def test_speculative_rollback_draft_parity(fast_pv):
+    """Draft cycles with partial acceptance on a ring with R = gamma - 1 headroom slots.
+
+    Prefill: one bulk append of n0 tokens.  Cycle c drafts gamma tokens (fresh K/V
+    per cycle) at positions n..n+gamma-1, each followed by a window draft query;
+    verification accepts the first a of them, wmtp_ring_rollback forgets the rest,
+    and the next cycle starts at n + a.  Every query is compared with the oracle
+    over the accepted sequence plus the current cycle's drafts; the ring's tags
+    with the oracle's ring model after every call, bit for bit.
+    """
+    S, Wn, gamma, Hq, Hk, D, B = 4, 64, 3, 8, 2, 128, 2
+    R = gamma - 1
+    scale = D ** -0.5
+    sh = W.make_shape(Hq, Hk, D, torch.bfloat16, scale)
+    n0 = [150, 97]
+    accepts = [[1, 3, 2, 1, 3, 1], [3, 1, 1, 2, 3, 2]]
+    ring = RingCache(B, Hk, D, S, Wn, torch.bfloat16, headroom=R)
+    cap = max(n0) + gamma * len(accepts[0]) + 1
+    k_pre = synth.normal((B, cap, Hk, D), 21, "pre_k", 0.5, "bf16")
+    v_pre = synth.normal((B, cap, Hk, D), 21, "pre_v", 0.5, "bf16")
+    truth_k = [synth.bf16_bits(k_pre[b]).copy() for b in range(B)]   # [cap][Hk][D] accepted content
+    truth_v = [synth.bf16_bits(v_pre[b]).copy() for b in range(B)]
+    tags = [np.full(S + Wn + R, -1, dtype=np.int64) for _ in range(B)]
+    for b in range(B):                                     # bulk init from the prefill
+        sub = W.Ring(ring.k[b].data_ptr(), ring.v[b].data_ptr(), ring.tags[b].data_ptr(), S, Wn, R)
+        W.ring_append(sh, sub, k_pre[b:b + 1, :n0[b]].contiguous().to(DEV),
+                      v_pre[b:b + 1, :n0[b]].contiguous().to(DEV), [0])
+        O.ring_append(tags[b], 0, n0[b], S, Wn, R)
+    flag = W.DRAFT_FAST_PV if fast_pv else 0
+    n = list(n0)
+    worst = 0.0
+    for c in range(len(accepts[0])):
+        kd = synth.normal((gamma, B, 1, Hk, D), 22, ("draft_k", c), 0.5, "bf16")
+        vd = synth.normal((gamma, B, 1, Hk, D), 22, ("draft_v", c), 0.5, "bf16")
+        q = synth.normal((gamma, B, Hq, D), 22, ("draft_q", c), 1.0, "bf16")
+        cur_k = [truth_k[b].copy() for b in range(B)]      # accepted prefix + this cycle's drafts
+        cur_v = [truth_v[b].copy() for b in range(B)]
+        for j in range(gamma):
+            pos = [n[b] + j for b in range(B)]
+            lens = [p + 1 for p in pos]
+            W.ring_append(sh, ring.desc, kd[j].contiguous().to(DEV), vd[j].contiguous().to(DEV), pos)
+            for b in range(B):
+                O.ring_append(tags[b], pos[b], 1, S, Wn, R)
+                cur_k[b][pos[b]] = synth.bf16_bits(kd[j, b, 0])
+                cur_v[b][pos[b]] = synth.bf16_bits(vd[j, b, 0])
+            ws = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW | flag, sh, lens, 0, S, Wn, R), DEV)
+            parts = W.draft_attn(W.SINK_WINDOW | flag, sh, q[j].contiguous().to(DEV), lens, ws, ring=ring.desc)
+            out, lse = run_combine(parts, Hq, D, B)
+            torch.cuda.synchronize()
+            assert np.array_equal(ring.tags.cpu().numpy(), np.stack(tags))
+            qf = O.to_f64(synth.bf16_bits(q[j]), "bf16")
+            for b in range(B):
+                o_ref, l_ref = O.draft_attention(qf[b], O.LogicalKV(cur_k[b], "bf16", lens[b]),
+                                                 O.LogicalKV(cur_v[b], "bf16", lens[b]), lens[b], O.SINK_WINDOW,
+                                                 S, Wn, scale)
+                worst = max(worst, max_err(out[b], o_ref), max_err(lse[b], l_ref))
+        for b in range(B):                                 # verification: accept the first a drafts
+            a = accepts[b][c]
+            truth_k[b][n[b]:n[b] + a] = cur_k[b][n[b]:n[b] + a]
+            truth_v[b][n[b]:n[b] + a] = cur_v[b][n[b]:n[b] + a]
+            n[b] += a
+            O.ring_rollback(tags[b], n[b])
+        W.ring_rollback(ring.desc, n)
+        torch.cuda.synchronize()
+        assert np.array_equal(ring.tags.cpu().numpy(), np.stack(tags))
+    say("speculative rollback worst", worst)
+    assert worst <= TOL["bf16"], worst
+
+
 # ============================================================== draft attention
 def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtype=torch.float32):
     """Run gamma draft steps on the GPU and the oracle; return the worst max-abs errors (o, lse)."""
