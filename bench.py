@@ -121,8 +121,13 @@ class Step:
         sink_v = synth.normal((1, S, Hk, D), wl.seed, "ring_sink_v", wl.kv_scale, "bf16", dev)
         tail_k = synth.normal((1, Wn, Hk, D), wl.seed, "ring_tail_k", wl.kv_scale, "bf16", dev)
         tail_v = synth.normal((1, Wn, Hk, D), wl.seed, "ring_tail_v", wl.kv_scale, "bf16", dev)
-        W.ring_append(self.sh, self.ring, sink_k, sink_v, [0])
-        W.ring_append(self.sh, self.ring, tail_k, tail_v, [n0 - Wn])
+        s_eff = min(S, n0)                        # contexts shorter than S + W fill what they have
+        t_eff = min(n0 - s_eff, Wn)
+        if s_eff:
+            W.ring_append(self.sh, self.ring, sink_k[:, :s_eff].contiguous(), sink_v[:, :s_eff].contiguous(), [0])
+        if t_eff:
+            W.ring_append(self.sh, self.ring, tail_k[:, Wn - t_eff:].contiguous(), tail_v[:, Wn - t_eff:].contiguous(),
+                          [n0 - t_eff])
         self.tail_k, self.tail_v = tail_k, tail_v
         # per-step inputs
         self.q_draft = synth.normal((g, 1, Hq, D), wl.seed, "q_draft", 1.0, "bf16", dev)
@@ -436,6 +441,43 @@ def cpu_baseline(wl, n0, budget_s=12.0):
     }
 
 
+def step_bytes(n0, wl, windowed):
+    """Algorithmic K/V bytes of one decode step (gamma draft steps + the target layers' verify)."""
+    g = wl.gamma
+    draft = sum(kv_bytes(min(n0 + j, wl.sink + wl.window) if windowed else n0 + j, wl) for j in range(1, g + 1))
+    return draft + wl.target_layers * kv_bytes(n0 + g + 1, wl)
+
+
+def sweep(flag, steps, warmup, dev, contexts, gammas):
+    """Decode steps across context length and draft depth, both draft modes, beside the
+    bytes model's native/windowed ratio (the wedge that grows with context)."""
+    rows = []
+    for n0 in contexts:
+        for g in gammas:
+            wl = synth.workload("step_1m_bf16", contexts=(n0,), gamma=g)
+            log(f"sweep n0={n0} gamma={g}")
+            step = Step(wl, n0, wl.target_layers, 0, 0, 0, dev)
+            win_ms, ver_ms, dwin_ms, _ = time_steps(step, W.SINK_WINDOW, flag, steps, warmup)
+            nat_ms, _, dnat_ms, _ = time_steps(step, W.FULL, flag, steps, warmup)
+            # the same steps replayed from a HIP graph: no host launch cost (small contexts are host-bound eagerly)
+            gw, okw = graph_step(step, W.SINK_WINDOW, flag, 5)
+            gn, okn = graph_step(step, W.FULL, flag, 5)
+            bw, bn = step_bytes(n0, wl, True), step_bytes(n0, wl, False)
+            rows.append({"context": n0, "gamma": g, "windowed_us": round(win_ms * 1e3, 1),
+                         "native_us": round(nat_ms * 1e3, 1), "ratio": round(nat_ms / win_ms, 4),
+                         "bytes_model_ratio": round(bn / bw, 4),
+                         "windowed_gbps": round(bw / (win_ms * 1e-3) / 1e9, 1),
+                         "native_gbps": round(bn / (nat_ms * 1e-3) / 1e9, 1),
+                         "draft_window_us": round(dwin_ms * 1e3, 2), "draft_native_us": round(dnat_ms * 1e3, 2),
+                         "verify_us": round(ver_ms * 1e3, 2),
+                         "graph_windowed_us": pct(gw)["median"], "graph_native_us": pct(gn)["median"],
+                         "graph_ratio": round(float(np.median(gn)) / float(np.median(gw)), 4),
+                         "graph_replays_match_eager": bool(okw and okn)})
+            del step
+            torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -449,6 +491,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-details", action="store_true",
                     help="skip the extra measurements (graph replay, cold window, split and batch variants)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step at --context: steps over contexts 2K..1M and gamma 3/5/8")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 256 MiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -470,9 +514,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    flag = 0 if args.exact_pv else W.DRAFT_FAST_PV
+    if args.sweep:
+        rows = sweep(flag, args.steps, args.warmup, dev, (2048, 8192, 32768, 131072, 524288, 1 << 20), (3, 5, 8))
+        print(json.dumps({"metric": "decode-step attention us across context and gamma", "unit": "us/decode-step",
+                          "data": "synthetic", "dtype": "bf16", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "rows": rows}), flush=True)
+        return
     wl = synth.workload("step_1m_bf16", contexts=(args.context,))
     n0 = args.context
-    flag = 0 if args.exact_pv else W.DRAFT_FAST_PV
     log("streaming-read ceiling")
     ceiling = stream_ceiling_gbps(dev)
     log(f"setup: {wl.target_layers} target layers + 1 draft layer at {n0} tokens")
@@ -501,9 +551,7 @@ def main():
         details["mixed_batch"] = mixed_batch(flag, reps, dev)
 
     g = wl.gamma
-    bytes_win = sum(kv_bytes(min(n0 + j, wl.sink + wl.window), wl) for j in range(1, g + 1)) + \
-        wl.target_layers * kv_bytes(n0 + g + 1, wl)
-    bytes_nat = sum(kv_bytes(n0 + j, wl) for j in range(1, g + 1)) + wl.target_layers * kv_bytes(n0 + g + 1, wl)
+    bytes_win, bytes_nat = step_bytes(n0, wl, True), step_bytes(n0, wl, False)
     ver_bytes = verify_launch_bytes(n0 + g + 1, wl, g + 1)
     ver_avg_ms = (ver_ms + ver_ms2) / 2
     achieved = ver_bytes / (ver_avg_ms * 1e-3) / 1e9

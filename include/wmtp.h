@@ -40,9 +40,9 @@
  * ------------------------------------------
  *  paged pool   k, v: [num_blocks][num_kv_heads][block_size][D], block_size 16
  *  block table  [batch][max_blocks_per_seq] int32 physical block ids
- *  ring         k, v: [batch][num_kv_heads][sink + window][D]
- *               slot_pos: [batch][sink + window] int32 (absolute position, -1 empty)
- *               slot(p) = p for p < sink, else sink + (p - sink) % window
+ *  ring         k, v: [batch][num_kv_heads][sink + window + headroom][D]
+ *               slot_pos: [batch][sink + window + headroom] int32 (absolute position, -1 empty)
+ *               slot(p) = p for p < sink, else sink + (p - sink) % (window + headroom)
  *  draft q      [batch][num_q_heads][D]
  *  verify q     [batch][t_q][num_q_heads][D]
  *  new k, v     [batch][t_new][num_kv_heads][D]
@@ -86,7 +86,7 @@ extern "C" {
 
 #define WMTP_MAX_BATCH   64     /* sequences per call                                         */
 #define WMTP_BLOCK_SIZE  16     /* tokens per paged block                                     */
-#define WMTP_MAX_VERIFY_ROWS 32 /* t_q * G per KV head in one verify call                     */
+#define WMTP_MAX_VERIFY_ROWS 96 /* t_q * G per KV head in one verify call (3 tiles of 32 rows) */
 
 /* ---------------------------------------------------------------- descriptors */
 typedef struct wmtp_shape {

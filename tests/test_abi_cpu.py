@@ -195,7 +195,7 @@ def test_workspace_sizes_follow_the_split_plan():
     (dict(sh=shape(dt=W.F32)), W.EUNSUPPORTED),
     (dict(sh=shape(d=128)), W.EUNSUPPORTED),
     (dict(t_q=0), W.EINVAL),
-    (dict(t_q=5), W.EUNSUPPORTED),                               # 5 x 8 rows > 32
+    (dict(t_q=13), W.EUNSUPPORTED),                              # 13 x 8 rows > 96
     (dict(seq=(3,)), W.EINVAL),                                  # fewer keys than queries
     (dict(split=48), W.EINVAL),
 ])

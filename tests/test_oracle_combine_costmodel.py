@@ -78,3 +78,39 @@ def test_one_draft_step_costs_a_tenth_of_the_target_read():
     ratio = per_draft_step / target
     assert abs(ratio - g["layers_draft"] / g["layers_target"]) < 1e-3
     assert abs(ratio - g["measured"]) < 0.015     # the case study measured 8.8%
+
+
+# ---------------------------------------------------------------- sweeps over context and gamma (row f2)
+def _ratio(n0, gamma, L=10, S=4, Wn=4096):
+    nat = O.step_kv_bytes(n0, gamma, L, 2, 256, 2, O.FULL)
+    win = O.step_kv_bytes(n0, gamma, L, 2, 256, 2, O.SINK_WINDOW, S, Wn)
+    return nat / win
+
+
+def test_wedge_widens_with_context():
+    """[P3 Abstract] the speedup grows with context: the bytes ratio never falls as n0 grows,
+    and it is exactly 1 while the window still covers the whole context."""
+    for gamma in (3, 5, 8):
+        ctx = [2048, 4096 - gamma, 8192, 32768, 131072, 524288, 1 << 20, 1 << 22]
+        r = [_ratio(n, gamma) for n in ctx]
+        assert r[0] == 1.0 and r[1] == 1.0                 # n0 + gamma <= S + W: same entries read
+        assert all(b >= a for a, b in zip(r, r[1:]))
+        assert r[-1] > r[2]
+
+
+def test_deeper_drafts_pay_more_at_long_context():
+    """More draft forwards per cycle multiply the native draft tax; the windowed draft's is constant."""
+    for n0 in (131072, 1 << 20):
+        r = [_ratio(n0, g) for g in (1, 3, 5, 8)]
+        assert all(b > a for a, b in zip(r, r[1:]))
+
+
+def test_ratio_tends_to_one_plus_gamma_over_layers():
+    """Closed form at long context: the draft steps read gamma full caches against L target layers,
+    so step_nat / step_win -> (L + gamma) / L as n0 -> infinity with S + W fixed."""
+    for gamma, L in ((3, 10), (5, 10), (8, 10), (3, 4)):
+        lim = (L + gamma) / L
+        gap1 = lim - _ratio(1 << 22, gamma, L)
+        gap2 = lim - _ratio(1 << 23, gamma, L)
+        assert 0 < gap2 < gap1 and gap2 < 2e-3
+        assert abs(gap1 / gap2 - 2.0) < 0.01             # the gap is O(1/n0): halves as the context doubles
