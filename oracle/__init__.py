@@ -8,4 +8,4 @@ from .wmtp_oracle import (FULL, SINK_WINDOW, decode_bf16, to_f64, visible_positi
                           draft_entries_read, ring_slot, ring_append, ring_rollback,
                           ring_expected_tags, window_slot_positions, ring_visible, paged_element_offset, LogicalKV, PagedKV,
                           ConcatKV, softmax_attention, attention_over, draft_attention,
-                          verify_attention, lse_combine, step_kv_bytes)
+                          verify_attention, lse_combine, step_kv_bytes, memory_plan)

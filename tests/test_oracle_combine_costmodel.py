@@ -114,3 +114,39 @@ def test_ratio_tends_to_one_plus_gamma_over_layers():
         gap2 = lim - _ratio(1 << 23, gamma, L)
         assert 0 < gap2 < gap1 and gap2 < 2e-3
         assert abs(gap1 / gap2 - 2.0) < 0.01             # the gap is O(1/n0): halves as the context doubles
+
+
+# ---------------------------------------------------------------- memory accounting (row f3)
+def test_ring_reclaims_the_dead_draft_pool_share_of_kv():
+    """[P3 Abstract] 7.7-11.1% of total KV at 1M: one draft layer among L target layers of equal
+    per-layer KV is 1/(L+1) of it (1/13, 1/11, 1/9 for L = 12, 10, 8), less the ring's 8 MB."""
+    g = _pages()["reclaimed_pool_fraction"]
+    fr = {}
+    for L in (8, 10, 12):
+        m = O.memory_plan(2, 256, 2, L, 1 << 20, 4, 4096, 2, 1 << 40)
+        fr[L] = m["reclaimed_fraction"]
+        assert abs(fr[L] - 1 / (L + 1)) < 1e-3
+    assert g["lo"] - 5e-4 <= min(fr.values()) and max(fr.values()) <= g["hi"] + 5e-4
+
+
+def test_hand_counted_bytes_at_1m():
+    m = O.memory_plan(2, 256, 2, 10, 1 << 20, 4, 4096, 2, 0)
+    assert m["layer_bytes"] == 65536 * 16 * 2 * 256 * 2 * 2 == 2 << 30          # 2 GiB per layer
+    assert m["ring_bytes"] == 4102 * (2048 + 4)
+    assert m["native_seq_bytes"] == 11 * (2 << 30) + 65536 * 4
+    assert m["windowed_seq_bytes"] == 10 * (2 << 30) + 4102 * 2052 + 65536 * 4
+
+
+def test_one_more_1m_request_fits():
+    """[P3 Abstract] the reclaimed pool made room for one additional concurrent 1M request: with a
+    budget that holds N native 1M sequences (N > L), the windowed draft admits at least N + 1 (at
+    N = L exactly, the ring and block table leave it just short)."""
+    for L in (8, 10, 12):
+        m = O.memory_plan(2, 256, 2, L, 1 << 20, 4, 4096, 2, 0)
+        p = O.memory_plan(2, 256, 2, L, 1 << 20, 4, 4096, 2, L * m["native_seq_bytes"])
+        assert p["windowed_sequences"] == L
+        for n in range(L + 1, 3 * L):
+            budget = n * m["native_seq_bytes"]
+            p = O.memory_plan(2, 256, 2, L, 1 << 20, 4, 4096, 2, budget)
+            assert p["native_sequences"] == n
+            assert p["windowed_sequences"] >= n + 1
