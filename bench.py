@@ -543,6 +543,10 @@ def main():
         log("window draft: warm, cold, across contexts")
         details["window_draft_step_us"] = window_measurements(
             step, flag, reps, dev, (32768, 131072, 524288, n0))
+        total_mem = torch.cuda.get_device_properties(0).total_memory
+        details["memory_plan"] = dict(W.plan_memory(step.sh, wl.target_layers, n0 + wl.gamma + 1, wl.sink, wl.window,
+                                                    step.R, total_mem),
+                                      budget="the GPU's whole memory", budget_bytes=int(total_mem))
         log("native draft launch: literal 256-key splits vs default")
         details["native_draft_launch_us"] = native_split_measurements(step, flag, 10, dev)
         del step

@@ -247,6 +247,34 @@ int wmtp_debug_resolve_ring(int32_t sink, int32_t window, int32_t headroom, cons
 int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t headroom, int32_t n, int32_t* out,
                                 void* stream);
 
+/* ---------------------------------------------------------------- memory accounting (host only) */
+
+/* KV memory of one sequence at `context` tokens with a native or a windowed
+ * draft, and the sequences an HBM budget admits (Windowed-MTP summary,
+ * Abstract: the ring reclaims the otherwise dead draft pool, 7.7-11.1% of
+ * total KV at 1M, room for one more concurrent 1M request).  Every
+ * full-attention layer (the `target_layers`, and the native draft) keeps a
+ * paged pool of ceil(context / 16) blocks of K and V; one int32 block table per
+ * sequence serves them all; the windowed draft keeps only its ring of
+ * S + W + R slots of K and V plus an int32 tag each. */
+typedef struct wmtp_memory_plan {
+  int64_t layer_bytes;          /* K+V of one paged full-attention layer        */
+  int64_t block_table_bytes;    /* the sequence's block table                   */
+  int64_t ring_bytes;           /* K+V+tags of the draft's ring                 */
+  int64_t native_seq_bytes;     /* target layers + draft pool + table           */
+  int64_t windowed_seq_bytes;   /* target layers + ring + table                 */
+  double  reclaimed_fraction;   /* 1 - windowed / native                        */
+  int64_t native_sequences;     /* floor(budget / native_seq_bytes)             */
+  int64_t windowed_sequences;   /* floor(budget / windowed_seq_bytes)           */
+} wmtp_memory_plan;
+
+/* Fill *out (host).  context >= 0, target_layers >= 0, budget_bytes >= 0,
+ * sink/window/headroom as in wmtp_ring.  A sequence that needs no bytes (no
+ * context and no target layer) gets fraction 0 and 0 sequences.  Makes no HIP
+ * call; WMTP_EINVAL on invalid arguments or int64 overflow. */
+int wmtp_plan_memory(const wmtp_shape* shape, int32_t target_layers, int64_t context, int32_t sink,
+                     int32_t window, int32_t headroom, int64_t budget_bytes, wmtp_memory_plan* out);
+
 /* ---------------------------------------------------------------- measurement */
 
 /* Streaming-read probe: `workgroups` workgroups of 256 threads each read one

@@ -426,6 +426,31 @@ int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t headroom, 
       launch_debug_window_positions(sink, window, headroom, n, out, static_cast<hipStream_t>(stream)));
 }
 
+int wmtp_plan_memory(const wmtp_shape* shape, int32_t target_layers, int64_t context, int32_t sink,
+                     int32_t window, int32_t headroom, int64_t budget_bytes, wmtp_memory_plan* out) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!out || target_layers < 0 || context < 0 || budget_bytes < 0) return WMTP_EINVAL;
+  if (sink < 0 || window < 1 || headroom < 0 || (int64_t)sink + window + headroom > (int64_t)INT32_MAX / 2)
+    return WMTP_EINVAL;
+  const int64_t row = (int64_t)shape->num_kv_heads * shape->head_dim * elem_bytes(shape->dtype) * 2;   // K+V
+  const int64_t blocks = (context + WMTP_BLOCK_SIZE - 1) / WMTP_BLOCK_SIZE;
+  if (blocks > INT64_MAX / (WMTP_BLOCK_SIZE * row) / (target_layers + 1)) return WMTP_EINVAL;
+  const int64_t layer = blocks * WMTP_BLOCK_SIZE * row;
+  const int64_t table = blocks * 4;
+  const int64_t ring = ((int64_t)sink + window + headroom) * (row + 4);
+  out->layer_bytes = layer;
+  out->block_table_bytes = table;
+  out->ring_bytes = ring;
+  out->native_seq_bytes = (int64_t)target_layers * layer + layer + table;
+  out->windowed_seq_bytes = (int64_t)target_layers * layer + ring + table;
+  out->reclaimed_fraction =
+      out->native_seq_bytes > 0 ? 1.0 - (double)out->windowed_seq_bytes / (double)out->native_seq_bytes : 0.0;
+  out->native_sequences = out->native_seq_bytes > 0 ? budget_bytes / out->native_seq_bytes : 0;
+  out->windowed_sequences = out->windowed_seq_bytes > 0 ? budget_bytes / out->windowed_seq_bytes : 0;
+  return WMTP_OK;
+}
+
 int wmtp_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
   if (!src || !sink || bytes < 16 || workgroups < 1 || workgroups > (1 << 20)) return WMTP_EINVAL;
   if (!aligned(src, 16) || !aligned(sink, 4) || bytes % 16 != 0) return WMTP_EALIGN;

@@ -50,6 +50,16 @@ class Ring(ctypes.Structure):
                 ("sink", ctypes.c_int32), ("window", ctypes.c_int32), ("headroom", ctypes.c_int32)]
 
 
+class MemoryPlan(ctypes.Structure):
+    _fields_ = [("layer_bytes", ctypes.c_int64), ("block_table_bytes", ctypes.c_int64),
+                ("ring_bytes", ctypes.c_int64), ("native_seq_bytes", ctypes.c_int64),
+                ("windowed_seq_bytes", ctypes.c_int64), ("reclaimed_fraction", ctypes.c_double),
+                ("native_sequences", ctypes.c_int64), ("windowed_sequences", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 class Partials(ctypes.Structure):
     _fields_ = [("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("batch", ctypes.c_int32),
                 ("rows_per_seq", ctypes.c_int32), ("head_dim", ctypes.c_int32),
@@ -59,7 +69,8 @@ class Partials(ctypes.Structure):
 EXPORTS = (
     "wmtp_draft_workspace_bytes", "wmtp_verify_workspace_bytes", "wmtp_draft_attn", "wmtp_verify_attn",
     "wmtp_combine", "wmtp_ring_append", "wmtp_ring_rollback", "wmtp_paged_append", "wmtp_debug_resolve_paged",
-    "wmtp_debug_resolve_ring", "wmtp_debug_window_positions", "wmtp_stream_read", "wmtp_status_str",
+    "wmtp_debug_resolve_ring", "wmtp_debug_window_positions", "wmtp_plan_memory", "wmtp_stream_read",
+    "wmtp_status_str",
     "wmtp_version",
 )
 
@@ -99,6 +110,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.wmtp_debug_resolve_ring.restype = ctypes.c_int
     lib.wmtp_debug_window_positions.argtypes = [I32, I32, I32, I32, P, P]
     lib.wmtp_debug_window_positions.restype = ctypes.c_int
+    lib.wmtp_plan_memory.argtypes = [sp, I32, I64, I32, I32, I32, I64, ctypes.POINTER(MemoryPlan)]
+    lib.wmtp_plan_memory.restype = ctypes.c_int
     lib.wmtp_stream_read.argtypes = [P, I64, P, I32, P]
     lib.wmtp_stream_read.restype = ctypes.c_int
     lib.wmtp_status_str.argtypes = [ctypes.c_int]
@@ -243,6 +256,15 @@ def debug_window_positions(sink: int, window: int, n: int, device, headroom: int
     _check("wmtp_debug_window_positions", load().wmtp_debug_window_positions(
         sink, window, headroom, n, out.data_ptr(), _stream(stream)))
     return out
+
+
+def plan_memory(shape: Shape, target_layers: int, context: int, sink: int, window: int, headroom: int,
+                budget_bytes: int) -> dict:
+    """KV bytes per sequence with a native or windowed draft, and sequences a budget admits (host only)."""
+    out = MemoryPlan()
+    _check("wmtp_plan_memory", load().wmtp_plan_memory(ctypes.byref(shape), target_layers, context, sink, window,
+                                                       headroom, budget_bytes, ctypes.byref(out)))
+    return out.as_dict()
 
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=None) -> None:

@@ -384,10 +384,12 @@ def memory_plan(num_kv_heads: int, head_dim: int, elem_bytes: int, target_layers
     target = target_layers * layer
     native = target + layer + table
     windowed = target + ring + table
+    # a sequence that needs no bytes (no context and no target layer) is reported as 0, not infinity
     return {
         "layer_bytes": layer, "block_table_bytes": table, "ring_bytes": ring,
         "native_seq_bytes": native, "windowed_seq_bytes": windowed,
-        "reclaimed_fraction": (native - windowed) / native,
-        "native_sequences": budget_bytes // native, "windowed_sequences": budget_bytes // windowed,
+        "reclaimed_fraction": (native - windowed) / native if native else 0.0,
+        "native_sequences": budget_bytes // native if native else 0,
+        "windowed_sequences": budget_bytes // windowed if windowed else 0,
     }
 

@@ -304,3 +304,35 @@ def test_debug_hook_checks():
     assert lib.wmtp_debug_window_positions(4, 4, 0, 10, None, None) == W.EINVAL
     assert lib.wmtp_debug_window_positions(4, 4, -1, 10, FAKE, None) == W.EINVAL
     assert lib.wmtp_debug_resolve_ring(4, 4, -1, FAKE, 1, FAKE, None) == W.EINVAL
+
+
+def test_memory_plan_matches_the_oracle():
+    """Host-only planner (row f3) against the oracle's independent count, exact integers."""
+    import oracle as O
+    for hq, hk, d, dt, eb in ((16, 2, 256, W.BF16, 2), (4, 1, 64, W.F32, 4), (8, 8, 128, W.BF16, 2)):
+        sh = shape(hq=hq, hk=hk, d=d, dt=dt)
+        for L in (0, 1, 10):
+            for ctx in (0, 1, 15, 16, 17, 131072, 1 << 20, 3_000_001):
+                for S, Wn, R in ((4, 4096, 2), (0, 1, 0), (16, 16384, 7)):
+                    budget = 288 * 10 ** 9
+                    got = W.plan_memory(sh, L, ctx, S, Wn, R, budget)
+                    want = O.memory_plan(hk, d, eb, L, ctx, S, Wn, R, budget)
+                    for key, val in want.items():
+                        if key == "reclaimed_fraction":
+                            assert abs(got[key] - val) < 1e-12, (key, got[key], val)
+                        else:
+                            assert got[key] == val, (key, got[key], val)
+
+
+def test_memory_plan_checks():
+    lib = W.load()
+    sh = shape()
+    out = W.MemoryPlan()
+    assert lib.wmtp_plan_memory(ctypes.byref(sh), -1, 10, 4, 64, 0, 0, ctypes.byref(out)) == W.EINVAL
+    assert lib.wmtp_plan_memory(ctypes.byref(sh), 10, -1, 4, 64, 0, 0, ctypes.byref(out)) == W.EINVAL
+    assert lib.wmtp_plan_memory(ctypes.byref(sh), 10, 10, 4, 0, 0, 0, ctypes.byref(out)) == W.EINVAL
+    assert lib.wmtp_plan_memory(ctypes.byref(sh), 10, 10, 4, 64, -1, 0, ctypes.byref(out)) == W.EINVAL
+    assert lib.wmtp_plan_memory(ctypes.byref(sh), 10, 10, 4, 64, 0, -5, ctypes.byref(out)) == W.EINVAL
+    assert lib.wmtp_plan_memory(ctypes.byref(sh), 10, 10, 4, 64, 0, 0, None) == W.EINVAL
+    assert lib.wmtp_plan_memory(ctypes.byref(sh), 1 << 30, 1 << 60, 4, 64, 0, 0, ctypes.byref(out)) == W.EINVAL
+    assert lib.wmtp_plan_memory(None, 10, 10, 4, 64, 0, 0, ctypes.byref(out)) == W.EINVAL
