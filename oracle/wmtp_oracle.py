@@ -33,6 +33,9 @@ design notes):
     rejects (R >= gamma - 1 keeps every entry a later window needs);
   * rejected drafted tokens are forgotten by clearing the tags of positions at
     or past the accepted length; a re-append at the same position overwrites;
+  * adaptive windows and dynamic sinks (named as future work) are per-sequence
+    S_b <= S and W_b <= W + R read from the ring laid out for (S, W, R), so a
+    sequence may change them between steps without moving any entry;
   * query head h reads KV head h // G (consecutive query heads share a KV head);
   * the softmax scale is 1/sqrt(D);
   * the paged pool is laid out [block][kv_head][block_offset][D].

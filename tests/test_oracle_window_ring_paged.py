@@ -139,7 +139,7 @@ def test_bulk_append_with_headroom_equals_sequential(S, W, R, pos, T):
     assert len(slots) == len(set(slots))
 
 
-def _speculate(S, W, R, gamma, n0, accepts, rollback):
+def _speculate(S, W, R, gamma, n0, accepts, rollback, vis=None):
     """Run draft cycles on a ring and return the first (cycle, step, missing position) a
     draft query fails to read with the right content, or None.
 
@@ -149,6 +149,7 @@ def _speculate(S, W, R, gamma, n0, accepts, rollback):
     the next cycle starts at n + a (its first token is the target's correction).
     """
     C = S + W + R
+    Sv, Wv = vis if vis is not None else (S, W)          # the queries' sinks and window (<= the layout's)
     tags = np.full(C, -1, dtype=np.int64)
     content = {}
     truth = {}                                           # position -> version of the accepted sequence
@@ -163,9 +164,9 @@ def _speculate(S, W, R, gamma, n0, accepts, rollback):
             (_, sl), = O.ring_append(tags, p, 1, S, W, R)
             content[sl] = (p, c)
             m = p + 1
-            want = {q: (truth[q] if q < n else c) for q in O.visible_positions(m, O.SINK_WINDOW, S, W)}
+            want = {q: (truth[q] if q < n else c) for q in O.visible_positions(m, O.SINK_WINDOW, Sv, Wv)}
             got = {}
-            for sl2, q in enumerate(O.ring_visible(tags, m, S, W)):
+            for sl2, q in enumerate(O.ring_visible(tags, m, Sv, Wv)):
                 if q >= 0:
                     got[int(q)] = content[sl2][1]
             for q, ver in want.items():
@@ -208,6 +209,32 @@ def test_ring_rollback_clears_exactly_the_rejected_positions():
     assert sorted(cleared) == sorted(O.ring_slot(p, S, W, R) for p in (17, 18, 19))
     assert sorted(t for t in tags if t >= 0) == [0, 1, 13, 14, 15, 16]
     assert O.ring_rollback(tags, 17) == []              # idempotent
+
+
+@settings(max_examples=200, deadline=None)
+@given(S=st.integers(0, 8), Wn=st.integers(1, 40), R=st.integers(0, 6), data=st.data())
+def test_per_sequence_sinks_and_windows_read_from_one_ring_layout(S, Wn, R, data):
+    """Adaptive windows / dynamic sinks: a ring laid out for (S, W, R) and appended in order
+    holds every position of the sink_window set of any S_b <= S and W_b <= W + R, and a query
+    reads exactly that set, so S_b and W_b may change from one step to the next."""
+    tags = np.full(S + Wn + R, -1, dtype=np.int64)
+    N = data.draw(st.integers(1, 3 * (S + Wn + R) + 5))
+    for p in range(N):
+        O.ring_append(tags, p, 1, S, Wn, R)
+        Sb = data.draw(st.integers(0, S))
+        Wb = data.draw(st.integers(1, Wn + R))
+        got = sorted(int(t) for t in O.ring_visible(tags, p + 1, Sb, Wb) if t >= 0)
+        assert got == _list_model_visible(p + 1, Sb, Wb)
+
+
+def test_per_sequence_windows_with_rollback():
+    """Per-sequence windows W_b with W_b + gamma - 1 <= W + R keep every needed entry through
+    draft cycles with partial acceptance (the ring layout stays (S, W, R))."""
+    S, Wn, R, gamma = 4, 16, 2, 3
+    for Sb, Wb in ((4, 16), (2, 10), (0, 16), (4, 1), (1, 16)):
+        assert _speculate(S, Wn, R, gamma, 100, [1, 3, 2, 1, 1, 3], rollback=True, vis=(Sb, Wb)) is None
+    # a window past the safe bound loses an entry after a partial acceptance
+    assert _speculate(S, Wn, R, gamma, 100, [1, 3], rollback=True, vis=(4, Wn + R)) is not None
 
 
 def _place_paged(logical, bt_row, bs, num_blocks):
