@@ -374,6 +374,17 @@ def mixed_batch(flag, reps, dev):
             W.combine(W.draft_attn(W.SINK_WINDOW | flag, sh, q, lens, wsw, ring=ring), out, lse)
         window()
         res["window_draft_step_us"][str(Wn)] = pct(_timed(window, reps))["median"]
+        if Wn == max(wl.windows):
+            # adaptive windows: every sequence its own W_b (and S_b) in one call on this ring layout
+            mix_w = [wl.windows[b % len(wl.windows)] for b in range(B)]
+            mix_s = [S if b % 2 == 0 else 0 for b in range(B)]
+            pol = W.with_policy(ring, mix_s, mix_w)
+
+            def mixed():
+                W.combine(W.draft_attn(W.SINK_WINDOW | flag, sh, q, lens, wsw, ring=pol), out, lse)
+            mixed()
+            res["per_sequence_policy"] = {"sinks": mix_s, "windows": mix_w,
+                                          "window_draft_step_us": pct(_timed(mixed, reps))["median"]}
         del rk, rv, tags, wsw
     del k, v
     torch.cuda.empty_cache()

@@ -121,6 +121,15 @@ typedef struct wmtp_ring {
   int32_t  sink;       /* S >= 0                                           */
   int32_t  window;     /* W >= 1                                           */
   int32_t  headroom;   /* R >= 0 extra slots in the cycle                  */
+  /* Optional per-sequence policy for the draft query (host, [batch], or
+   * NULL = S / W for every sequence): sequence b attends to positions
+   * {0..seq_sink[b]-1} and {n-seq_window[b]..n-1}, with
+   * 0 <= seq_sink[b] <= S and 1 <= seq_window[b] <= W + R.  The layout stays
+   * (S, W, R), so the values may change from one call to the next (adaptive
+   * windows, dynamic sinks).  Rolling back gamma drafted tokens needs
+   * seq_window[b] + gamma - 1 <= W + R. */
+  const int32_t* seq_sink;
+  const int32_t* seq_window;
 } wmtp_ring;
 
 /* Split-K partial results, written by wmtp_draft_attn / wmtp_verify_attn into
@@ -141,7 +150,9 @@ typedef struct wmtp_partials {
 
 /* Bytes of workspace wmtp_draft_attn needs.  Arguments as for wmtp_draft_attn
  * (sink/window/headroom, the ring's S/W/R, are read only in WMTP_SINK_WINDOW
- * mode).  Returns >= 0 bytes or a negative WMTP_E* code.  Makes no HIP call. */
+ * mode, where the size covers min(n, S + W + R) entries per sequence: enough
+ * for any per-sequence sinks and windows).  Returns >= 0 bytes or a negative
+ * WMTP_E* code.  Makes no HIP call. */
 int64_t wmtp_draft_workspace_bytes(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens_host,
                                    int32_t batch, int32_t chunk_tokens, int32_t sink, int32_t window,
                                    int32_t headroom);
@@ -159,8 +170,10 @@ int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const 
  *                            the paged pool `kv` (`ring` may be NULL).
  *  mode (low 4 bits) == WMTP_SINK_WINDOW: sequence b attends to positions {0..S-1} and
  *                            {n_b-W..n_b-1}, read from `ring` (`kv` may be NULL).
- *                            Ring slots whose slot_pos tag is not one of those
- *                            positions are ignored.
+ *                            Each visible position p is read from slot(p) when
+ *                            slot_pos holds p there (otherwise it is skipped);
+ *                            S and W may be per sequence (wmtp_ring.seq_sink /
+ *                            seq_window), and the cost follows min(n, S_b + W_b).
  *  n_b = seq_lens_host[b] (host) is the length after this step's own entry was
  *  appended, so the query attends to itself.  q: device [batch][H_q][D].
  *  chunk_tokens: entries per split (a multiple of 64).  0 = library default:

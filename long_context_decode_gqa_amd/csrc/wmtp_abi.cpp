@@ -112,8 +112,14 @@ int make_plan(const int64_t* vis, int batch, int chunk, int rows, int head_dim, 
   return WMTP_OK;
 }
 
+// Window mode: the launch plans each sequence's visible count min(n, S_b + W_b)
+// (S_b, W_b from the optional per-sequence arrays); the workspace size plans the
+// bound min(n, S + W + R) that any policy stays under.  The default chunk comes
+// from the bound in both, so a launch never needs more splits than the
+// workspace size allowed for.
 int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, int32_t batch, int32_t chunk,
-               int32_t sink, int32_t window, int32_t headroom, Plan* p, int32_t* chunk_out) {
+               int32_t sink, int32_t window, int32_t headroom, const int32_t* seq_sink, const int32_t* seq_window,
+               bool upper_bound, Plan* p, int32_t* chunk_out) {
   int st = check_shape(shape);
   if (st) return st;
   const int base_mode = mode & 0xF;
@@ -123,16 +129,23 @@ int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, i
   if (base_mode == WMTP_SINK_WINDOW &&
       (sink < 0 || window < 1 || headroom < 0 || (int64_t)sink + window + headroom > (int64_t)INT32_MAX / 2))
     return WMTP_EINVAL;
-  // window mode scans the ring's slots that can hold an entry: min(n, S+W+R)
   const int64_t ring_slots = (int64_t)sink + window + headroom;
-  int64_t vis[WMTP_MAX_BATCH];
+  int64_t vis[WMTP_MAX_BATCH], bound[WMTP_MAX_BATCH];
   for (int b = 0; b < batch; ++b) {
     if (seq_lens[b] < 0) return WMTP_EINVAL;
-    vis[b] = base_mode == WMTP_FULL ? seq_lens[b] : std::min<int64_t>(seq_lens[b], ring_slots);
+    if (base_mode == WMTP_FULL) {
+      vis[b] = bound[b] = seq_lens[b];
+      continue;
+    }
+    const int64_t sb = seq_sink ? seq_sink[b] : sink;
+    const int64_t wb = seq_window ? seq_window[b] : window;
+    if (sb < 0 || sb > sink || wb < 1 || wb > (int64_t)window + headroom) return WMTP_EINVAL;
+    bound[b] = std::min<int64_t>(seq_lens[b], ring_slots);
+    vis[b] = upper_bound ? bound[b] : std::min<int64_t>(seq_lens[b], sb + wb);
   }
   if (chunk == 0)
-    chunk = base_mode == WMTP_FULL ? default_split(vis, batch, shape->num_kv_heads, kFullSlots, kFullMinSplit)
-                                   : default_split(vis, batch, shape->num_kv_heads, kWindowSlots, kWindowMinSplit);
+    chunk = base_mode == WMTP_FULL ? default_split(bound, batch, shape->num_kv_heads, kFullSlots, kFullMinSplit)
+                                   : default_split(bound, batch, shape->num_kv_heads, kWindowSlots, kWindowMinSplit);
   if (chunk < kDraftTile || chunk % kDraftTile != 0) return WMTP_EINVAL;
   *chunk_out = chunk;
   return make_plan(vis, batch, chunk, shape->num_q_heads, shape->head_dim, shape->num_kv_heads, p);
@@ -193,7 +206,8 @@ int64_t wmtp_draft_workspace_bytes(int32_t mode, const wmtp_shape* shape, const 
                                    int32_t chunk_tokens, int32_t sink, int32_t window, int32_t headroom) {
   Plan p;
   int32_t chunk = 0;
-  const int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, headroom, &p, &chunk);
+  const int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, headroom, nullptr, nullptr,
+                            true, &p, &chunk);
   return st ? st : p.bytes;
 }
 
@@ -219,7 +233,9 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
   }
   Plan p;
   int32_t chunk = 0;
-  int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, headroom, &p, &chunk);
+  const bool win = base_mode == WMTP_SINK_WINDOW;
+  int st = draft_plan(mode, shape, seq_lens_host, batch, chunk_tokens, sink, window, headroom,
+                      win ? ring->seq_sink : nullptr, win ? ring->seq_window : nullptr, false, &p, &chunk);
   if (st) return st;
   if (!q || !parts) return WMTP_EINVAL;
   if (!aligned(q, 16)) return WMTP_EALIGN;
@@ -230,6 +246,10 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
       if ((int64_t)(seq_lens_host[b] + WMTP_BLOCK_SIZE - 1) / WMTP_BLOCK_SIZE > kv->max_blocks_per_seq)
         return WMTP_EINVAL;
   }
+  if (base_mode == WMTP_SINK_WINDOW &&
+      ((int64_t)ring->sink + ring->window + ring->headroom) * shape->head_dim * elem_bytes(shape->dtype) >
+          (int64_t)INT32_MAX)
+    return WMTP_EINVAL;   // lanes address the ring of one (sequence, head) with 32-bit offsets
   if (!workspace && p.bytes > 0) return WMTP_EINVAL;
   if (!aligned(workspace, 256)) return WMTP_EALIGN;
   if ((int64_t)workspace_bytes < p.bytes) return WMTP_EWORKSPACE;
@@ -251,6 +271,10 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
     a.slots = ring->sink + ring->window + ring->headroom;
     a.sink = ring->sink;
     a.window = ring->window;
+    for (int b = 0; b < batch; ++b) {
+      a.seq_sink[b] = ring->seq_sink ? ring->seq_sink[b] : ring->sink;
+      a.seq_window[b] = ring->seq_window ? ring->seq_window[b] : ring->window;
+    }
   }
   const int grid = p.total * shape->num_kv_heads;
   const bool fast_pv = (mode & WMTP_DRAFT_FAST_PV) != 0 && shape->dtype == WMTP_BF16;

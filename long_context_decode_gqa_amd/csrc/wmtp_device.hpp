@@ -85,6 +85,8 @@ struct SplitArgs {
   float scale_log2;             // scale * log2(e)
   int32_t split_base[WMTP_MAX_BATCH + 1];
   int32_t seq_len[WMTP_MAX_BATCH];
+  int32_t seq_sink[WMTP_MAX_BATCH];      // ring: per-sequence sinks and window of the query
+  int32_t seq_window[WMTP_MAX_BATCH];
 };
 
 // ----------------------------------------------------------------------------- resolvers

@@ -6,7 +6,9 @@
 // Removing the Full-Context Draft-KV Tax at Million-Token Context", arxivlens
 // summary, Abstract; readpriors.com post, What happened).  One kernel serves
 // both: the only difference is how a visible entry is located (block table vs
-// ring slot + tag check).
+// ring slot + tag check).  Window mode walks the visible positions (the
+// sequence's own sinks, then its window) and reads each from its ring slot, so
+// its cost follows the sequence's S_b + W_b, not the ring's size.
 //
 // Work item = (sequence b, KV head h, split of `chunk` visible entries); one
 // workgroup per item whose waves each own a 64-byte slice of every K/V row (8
@@ -96,7 +98,11 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
   const int sg = blockIdx.x / Hkv;
   const int b = seq_of_split(a, sg);
   const int n = a.seq_len[b];
-  const int nvis = WINDOW ? min(n, a.slots) : n;
+  // Window mode reads the visible set in position order: entry t < s_vis is sink
+  // t, entry t >= s_vis is position w_start + t - s_vis (the last W_b before n).
+  const int s_vis = min(a.seq_sink[b], n);
+  const int w_start = max(s_vis, n - a.seq_window[b]);
+  const int nvis = WINDOW ? s_vis + (n - w_start) : n;
   const int t_begin = (sg - a.split_base[b]) * a.chunk;
   const int t_end = min(t_begin + a.chunk, nvis);
   const int ntiles = (t_end - t_begin + S::TILE - 1) / S::TILE;
@@ -106,6 +112,20 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
   const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
   const int64_t ring_seq = ((int64_t)b * Hkv + h) * a.slots * (int64_t)ROWB;
   const int32_t* tags = a.slot_pos + (int64_t)b * a.slots;
+  // Ring slot of visible entry t (clamped to the split): positions below the
+  // layout's S sit in their own slot, later ones cycle through C = slots - S.
+  // The window spans at most C positions, so its cycle index wraps at most once
+  // from ws_mod, the cycle index of w_start: no per-lane division.
+  const int cyc = a.slots - a.sink;
+  const int ws_mod = w_start >= a.sink ? (w_start - a.sink) % cyc : 0;
+  auto entry_pos = [&](int t) -> int { return t < s_vis ? t : w_start + (t - s_vis); };
+  auto entry_slot = [&](int t) -> int {
+    const int p = entry_pos(t);
+    if (p < a.sink) return p;
+    int c = w_start >= a.sink ? ws_mod + (p - w_start) : p - a.sink;
+    c = c >= cyc ? c - cyc : c;
+    return a.sink + c;
+  };
   const int last_blk_idx = (t_end - 1) >> 4;
 
   // query rows of this KV head, this wave's slice of D (wave-uniform -> SGPRs)
@@ -114,14 +134,15 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
 
   uint8_t* my_k = k_lds + wave * S::KSTAGE;
 
-  // ---- addressing.  A tile's entries live in up to 4 runs of 16 rows (paged) or
-  // one run of 64 rows (ring).  run[j] is the uniform byte offset of run j; a lane
-  // adds a 32-bit offset.  Entries past the split end are clamped to a valid row.
+  // ---- addressing.  A tile's entries live in up to 4 runs of 16 rows (paged);
+  // in the ring every lane adds its entry's slot offset to the ring's base.
+  // run[j] is the uniform byte offset of run j; a lane adds a 32-bit offset.
+  // Entries past the split end are clamped to a valid row.
   auto tile_runs = [&](int t0, int64_t (&run)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (WINDOW) {
-        run[j] = ring_seq + (int64_t)t0 * ROWB;
+        run[j] = ring_seq;
       } else {
         const int bi = min((t0 >> 4) + j, last_blk_idx);
         run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, ROWB);
@@ -129,7 +150,7 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
     }
   };
   auto lane_off = [&](int t0, int tt) -> uint32_t {
-    if constexpr (WINDOW) return (uint32_t)min(tt, a.slots - 1 - t0) * ROWB;
+    if constexpr (WINDOW) return (uint32_t)entry_slot(min(t0 + tt, t_end - 1)) * ROWB;
     return (uint32_t)(tt & 15) * ROWB;
   };
   auto run_base = [&](const uint8_t* base, const int64_t (&run)[4], int first, int span, int tt) -> const uint8_t* {
@@ -180,7 +201,7 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
         vreg[slot][k] = load_at<uint2>(run_base(vbase, run, k * TPV, TPV, tt), lane_off(t0, tt) + v_d * 8);
       }
     }
-    if constexpr (WINDOW) tag[slot] = tags[min(t0 + ln, a.slots - 1)];
+    if constexpr (WINDOW) tag[slot] = tags[entry_slot(min(t0 + ln, t_end - 1))];
   };
 
   float o[G][EV];
@@ -257,7 +278,8 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
 
     // ---- online softmax (log2 domain, lazy maximum)
     bool valid = t0 + ln < t_end;
-    if constexpr (WINDOW) valid = valid && window_visible(tag[slot], n, a.sink, a.window);
+    // the slot must hold exactly the entry's position (a hole or a stale entry is masked)
+    if constexpr (WINDOW) valid = valid && tag[slot] == entry_pos(t0 + ln);
     bool exceed = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {

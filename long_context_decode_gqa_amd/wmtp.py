@@ -47,7 +47,8 @@ class Paged(ctypes.Structure):
 
 class Ring(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slot_pos", ctypes.c_void_p),
-                ("sink", ctypes.c_int32), ("window", ctypes.c_int32), ("headroom", ctypes.c_int32)]
+                ("sink", ctypes.c_int32), ("window", ctypes.c_int32), ("headroom", ctypes.c_int32),
+                ("seq_sink", ctypes.c_void_p), ("seq_window", ctypes.c_void_p)]
 
 
 class MemoryPlan(ctypes.Structure):
@@ -163,7 +164,20 @@ def make_ring(k: torch.Tensor, v: torch.Tensor, slot_pos: torch.Tensor, sink: in
               headroom: int = 0) -> Ring:
     """k, v: [batch][H_kv][S+W+R][D]; slot_pos: int32 [batch][S+W+R] (device); R = headroom."""
     assert slot_pos.dtype == torch.int32
-    return Ring(k.data_ptr(), v.data_ptr(), slot_pos.data_ptr(), int(sink), int(window), int(headroom))
+    return Ring(k.data_ptr(), v.data_ptr(), slot_pos.data_ptr(), int(sink), int(window), int(headroom), None, None)
+
+
+def with_policy(ring: Ring, seq_sink: Optional[Sequence[int]] = None,
+                seq_window: Optional[Sequence[int]] = None) -> Ring:
+    """A copy of `ring` whose draft queries use per-sequence sinks / windows (host arrays kept alive)."""
+    r = Ring(ring.k, ring.v, ring.slot_pos, ring.sink, ring.window, ring.headroom, None, None)
+    if seq_sink is not None:
+        r._seq_sink = _lens(seq_sink)
+        r.seq_sink = ctypes.cast(r._seq_sink, ctypes.c_void_p)
+    if seq_window is not None:
+        r._seq_window = _lens(seq_window)
+        r.seq_window = ctypes.cast(r._seq_window, ctypes.c_void_p)
+    return r
 
 
 # ---------------------------------------------------------------- planning

@@ -262,6 +262,23 @@ def test_append_checks():
     assert lib.wmtp_paged_append(ctypes.byref(sh), None, FAKE, FAKE, lens(0), 1, 1, None) == W.EINVAL
 
 
+def test_per_sequence_policy_checks():
+    """Per-sequence sinks <= S and windows in [1, W + R] (window mode only)."""
+    lib = W.load()
+    sh = shape()
+    base = ring(s=4, w=64, r=2)
+    for sinks, wins, want in (([4], [66], W.OK), ([5], [64], W.EINVAL), ([-1], [64], W.EINVAL),
+                              ([0], [0], W.EINVAL), ([0], [67], W.EINVAL), (None, [66], W.OK), ([2], None, W.OK)):
+        r = W.with_policy(base, sinks, wins)
+        p = W.Partials()
+        st = lib.wmtp_draft_attn(W.SINK_WINDOW, ctypes.byref(sh), FAKE, None, ctypes.byref(r), lens(1000), 1, 0,
+                                 FAKE, 1 << 30, ctypes.byref(p), None)
+        if want == W.OK:
+            assert st != W.EINVAL      # passes validation (no GPU here: the launch itself reports ELAUNCH)
+        else:
+            assert st == want, (sinks, wins, st)
+
+
 def test_rollback_checks():
     lib = W.load()
     r = ring(r=2)

@@ -219,6 +219,50 @@ def test_speculative_rollback_draft_parity(fast_pv):
     assert worst <= TOL["bf16"], worst
 
 
+@pytest.mark.parametrize("fast_pv", [False, True])
+def test_per_sequence_sinks_and_windows_parity(fast_pv):
+    """Adaptive windows / dynamic sinks: one batched window-mode call where every sequence has
+    its own S_b <= S and W_b <= W + R, changing from step to step, on one ring layout."""
+    S, Wn, R, Hq, Hk, D, B = 8, 96, 2, 16, 2, 256, 4
+    scale = D ** -0.5
+    sh = W.make_shape(Hq, Hk, D, torch.bfloat16, scale)
+    n0 = [40, 200, 1000, 7]
+    steps = 4
+    policies = [([8, 0, 4, 2], [98, 1, 50, 96]), ([1, 8, 8, 0], [10, 98, 97, 5]),
+                ([0, 3, 8, 8], [96, 64, 2, 98]), ([8, 8, 0, 5], [1, 33, 98, 40])]
+    ring = RingCache(B, Hk, D, S, Wn, torch.bfloat16, headroom=R)
+    cap = max(n0) + steps
+    kc = synth.normal((B, cap, Hk, D), 31, "pol_k", 0.5, "bf16")
+    vc = synth.normal((B, cap, Hk, D), 31, "pol_v", 0.5, "bf16")
+    for b in range(B):
+        sub = W.Ring(ring.k[b].data_ptr(), ring.v[b].data_ptr(), ring.tags[b].data_ptr(), S, Wn, R)
+        W.ring_append(sh, sub, kc[b:b + 1, :n0[b]].contiguous().to(DEV), vc[b:b + 1, :n0[b]].contiguous().to(DEV), [0])
+    kb = [synth.bf16_bits(kc[b]) for b in range(B)]
+    vb = [synth.bf16_bits(vc[b]) for b in range(B)]
+    flag = W.DRAFT_FAST_PV if fast_pv else 0
+    worst = 0.0
+    for j in range(steps):
+        pos = [n + j for n in n0]
+        lens = [p + 1 for p in pos]
+        W.ring_append(sh, ring.desc, torch.stack([kc[b, pos[b]] for b in range(B)])[:, None].contiguous().to(DEV),
+                      torch.stack([vc[b, pos[b]] for b in range(B)])[:, None].contiguous().to(DEV), pos)
+        sinks, wins = policies[j]
+        pol = W.with_policy(ring.desc, sinks, wins)
+        q = synth.normal((B, Hq, D), 31, ("pol_q", j), 1.0, "bf16")
+        ws = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW | flag, sh, lens, 64, S, Wn, R), DEV)
+        parts = W.draft_attn(W.SINK_WINDOW | flag, sh, q.to(DEV), lens, ws, ring=pol, chunk_tokens=64)
+        out, lse = run_combine(parts, Hq, D, B)
+        torch.cuda.synchronize()
+        qf = O.to_f64(synth.bf16_bits(q), "bf16")
+        for b in range(B):
+            o_ref, l_ref = O.draft_attention(qf[b], O.LogicalKV(kb[b], "bf16", lens[b]),
+                                             O.LogicalKV(vb[b], "bf16", lens[b]), lens[b], O.SINK_WINDOW,
+                                             sinks[b], wins[b], scale)
+            worst = max(worst, max_err(out[b], o_ref), max_err(lse[b], l_ref))
+    say("per-sequence policy worst", worst)
+    assert worst <= TOL["bf16"], worst
+
+
 # ============================================================== draft attention
 def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtype=torch.float32):
     """Run gamma draft steps on the GPU and the oracle; return the worst max-abs errors (o, lse)."""
