@@ -41,8 +41,8 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "61e0a2dff6375097725b39de31783f90854e1a44864be1f0bb44f04b4b6da762",
-                  "fetch_kib": 1053702.05, "write_kib": 8224.0, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_TRAFFIC = {"sources_sha256": "fb16e35e476d97761b8eca3c70169784163a0e3d06f96991946978b457933514",
+                  "fetch_kib": 1053754.55, "write_kib": 8224.00, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
 
@@ -85,6 +85,33 @@ def stream_ceiling_gbps(dev, nbytes=2 << 30):
         best = max(best, nbytes / (a.elapsed_time(b) / 10 * 1e-3) / 1e9)
     del src
     torch.cuda.empty_cache()
+    return best
+
+
+def paged_ceiling_gbps(step):
+    """Best rate of the paged streaming-read probe over one verify layer's pools, read in
+    the block table's order: (block, head) runs of 8 KiB, one head's blocks after another."""
+    wl, n = step.wl, step.n0 + step.wl.gamma + 1
+    k, v, _ = step.layers[1]
+    nb = synth.blocks_for(n, 16)
+    Hk = wl.num_kv_heads
+    bt = step.bt[0, :nb].to(torch.int64)
+    runs = torch.cat([bt * Hk + h for h in range(Hk)]).to(torch.int32).contiguous()
+    run_bytes = 16 * wl.head_dim * 2
+    nbytes = 2 * runs.numel() * run_bytes
+    best = 0.0
+    for wgs in (256, 512):
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device=k.device)
+        for _ in range(3):
+            W.stream_read_paged(k, v, runs, run_bytes, sink, wgs)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(10):
+            W.stream_read_paged(k, v, runs, run_bytes, sink, wgs)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) / 10 * 1e-3) / 1e9)
     return best
 
 
@@ -540,6 +567,8 @@ def main():
     step = Step(wl, n0, wl.target_layers, args.chunk_full, args.chunk_window,
                 args.split, dev)
 
+    log("paged streaming-read ceiling")
+    paged_ceiling = paged_ceiling_gbps(step)
     log("timing windowed step")
     win_ms, ver_ms, dwin_ms, win_steps = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup)
     log("timing native step")
@@ -604,7 +633,7 @@ def main():
             "draft_native_per_step": round(dnat_ms * 1e3, 2),
         },
         "roofline": {
-            "kernel": "mfma_attn_kernel<8, false> (verify, 10 launches per step)",
+            "kernel": "mfma_attn_kernel<8, 1, false> (verify, 10 launches per step)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -614,6 +643,8 @@ def main():
             "algorithmic_bytes": ver_bytes,
             "measured_read_ceiling": round(ceiling, 1),
             "frac_of_measured_ceiling": round(achieved / ceiling, 4),
+            "measured_paged_read_ceiling": round(paged_ceiling, 1),
+            "frac_of_paged_ceiling": round(achieved / paged_ceiling, 4),
         },
     }
     native_draft_bytes = draft_launch_bytes(n0 + 1, wl, True)

@@ -297,6 +297,16 @@ int wmtp_plan_memory(const wmtp_shape* shape, int32_t target_layers, int64_t con
  * bytes must be a positive multiple of 16; src 16-byte aligned. */
 int wmtp_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
 
+/* Paged streaming-read probe: reads the runs runs[0..nruns) (device int32, run
+ * ids clamped to [0, pool_bytes / run_bytes)) of both k and v (device, each
+ * pool_bytes), run_bytes per run (a power of two, 4 KiB .. 1 MiB), in that order,
+ * split over `workgroups` workgroups of 256 threads; one word per thread goes
+ * to sink (device, workgroups * 256 uint32).  With the runs of a paged cache in
+ * table order it is the attention kernels' access pattern without their
+ * arithmetic: the practical ceiling for reading that cache. */
+int wmtp_stream_read_paged(const void* k, const void* v, int64_t pool_bytes, const int32_t* runs, int32_t nruns,
+                           int32_t run_bytes, uint32_t* sink, int32_t workgroups, void* stream);
+
 /* ---------------------------------------------------------------- misc */
 const char* wmtp_status_str(int status);
 const char* wmtp_version(void);

@@ -481,6 +481,17 @@ int wmtp_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t wor
   return launch_status(launch_stream_read(src, bytes, sink, workgroups, static_cast<hipStream_t>(stream)));
 }
 
+int wmtp_stream_read_paged(const void* k, const void* v, int64_t pool_bytes, const int32_t* runs, int32_t nruns,
+                           int32_t run_bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+  if (!k || !v || !runs || !sink || nruns < 1 || workgroups < 1 || workgroups > (1 << 20)) return WMTP_EINVAL;
+  if (run_bytes < 4096 || run_bytes > (1 << 20) || (run_bytes & (run_bytes - 1)) != 0) return WMTP_EINVAL;
+  if (pool_bytes < run_bytes) return WMTP_EINVAL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(runs, 4) || !aligned(sink, 4)) return WMTP_EALIGN;
+  const int run_shift = __builtin_ctz((unsigned)run_bytes);
+  return launch_status(launch_stream_read_paged(k, v, runs, nruns, pool_bytes / run_bytes, run_shift, sink, workgroups,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 const char* wmtp_status_str(int status) {
   switch (status) {
     case WMTP_OK: return "ok";

@@ -55,5 +55,8 @@ hipError_t launch_debug_resolve_ring(int sink, int cycle, const int32_t* positio
                                      hipStream_t st);
 hipError_t launch_debug_window_positions(int sink, int window, int headroom, int n, int32_t* out, hipStream_t st);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t st);
+hipError_t launch_stream_read_paged(const void* k, const void* v, const int32_t* runs, int32_t nruns,
+                                    int64_t pool_runs, int run_shift, uint32_t* sink, int workgroups,
+                                    hipStream_t st);
 
 }  // namespace wmtp

@@ -71,7 +71,7 @@ EXPORTS = (
     "wmtp_draft_workspace_bytes", "wmtp_verify_workspace_bytes", "wmtp_draft_attn", "wmtp_verify_attn",
     "wmtp_combine", "wmtp_ring_append", "wmtp_ring_rollback", "wmtp_paged_append", "wmtp_debug_resolve_paged",
     "wmtp_debug_resolve_ring", "wmtp_debug_window_positions", "wmtp_plan_memory", "wmtp_stream_read",
-    "wmtp_status_str",
+    "wmtp_stream_read_paged", "wmtp_status_str",
     "wmtp_version",
 )
 
@@ -114,6 +114,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.wmtp_plan_memory.argtypes = [sp, I32, I64, I32, I32, I32, I64, ctypes.POINTER(MemoryPlan)]
     lib.wmtp_plan_memory.restype = ctypes.c_int
     lib.wmtp_stream_read.argtypes = [P, I64, P, I32, P]
+    lib.wmtp_stream_read_paged.argtypes = [P, P, I64, P, I32, I32, P, I32, P]
+    lib.wmtp_stream_read_paged.restype = ctypes.c_int
     lib.wmtp_stream_read.restype = ctypes.c_int
     lib.wmtp_status_str.argtypes = [ctypes.c_int]
     lib.wmtp_status_str.restype = ctypes.c_char_p
@@ -285,6 +287,14 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=N
     """Read all of `src` once (bandwidth probe); sink: int32/uint32 [workgroups * 256]."""
     _check("wmtp_stream_read", load().wmtp_stream_read(
         src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), workgroups, _stream(stream)))
+
+
+def stream_read_paged(k: torch.Tensor, v: torch.Tensor, runs: torch.Tensor, run_bytes: int, sink: torch.Tensor,
+                      workgroups: int, stream=None) -> None:
+    """Read the listed runs of k and v in order (paged bandwidth probe); runs: device int32."""
+    _check("wmtp_stream_read_paged", load().wmtp_stream_read_paged(
+        k.data_ptr(), v.data_ptr(), k.numel() * k.element_size(), runs.data_ptr(), runs.numel(), run_bytes,
+        sink.data_ptr(), workgroups, _stream(stream)))
 
 
 def version() -> str:

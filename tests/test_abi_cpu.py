@@ -311,6 +311,19 @@ def test_stream_read_checks():
     assert lib.wmtp_stream_read(FAKE, 1000, FAKE, 4, None) == W.EALIGN
 
 
+def test_stream_read_paged_checks():
+    lib = W.load()
+    f = lib.wmtp_stream_read_paged
+    assert f(FAKE, FAKE, 1 << 20, FAKE, 4, 8192, FAKE, 4, None) not in (W.EINVAL, W.EALIGN)   # valid: passes the checks
+    assert f(None, FAKE, 1 << 20, FAKE, 4, 8192, FAKE, 4, None) == W.EINVAL
+    assert f(FAKE, FAKE, 1 << 20, None, 4, 8192, FAKE, 4, None) == W.EINVAL
+    assert f(FAKE, FAKE, 1 << 20, FAKE, 0, 8192, FAKE, 4, None) == W.EINVAL
+    assert f(FAKE, FAKE, 1 << 20, FAKE, 4, 6000, FAKE, 4, None) == W.EINVAL          # not a power of two
+    assert f(FAKE, FAKE, 1 << 20, FAKE, 4, 2048, FAKE, 4, None) == W.EINVAL          # below 4 KiB
+    assert f(FAKE, FAKE, 4096, FAKE, 4, 8192, FAKE, 4, None) == W.EINVAL              # pool smaller than a run
+    assert f(FAKE_ODD, FAKE, 1 << 20, FAKE, 4, 8192, FAKE, 4, None) == W.EALIGN
+
+
 def test_debug_hook_checks():
     lib = W.load()
     kv = paged()
