@@ -458,7 +458,8 @@ def test_draft_full_1m_paged_sampled_head():
 
 @pytest.mark.slow
 def test_verify_1m_paged_sampled_head():
-    """C4's verify layer at its real size: 4 causal queries over 1,048,580 keys, 2048-key splits."""
+    """C4's verify layer at its real size and in the benchmark's launch configuration (default
+    splits): 4 causal queries over 1,048,580 keys, two query tokens checked on one KV head."""
     say("verify 1M")
     n0, bt, k, v, btd = _paged_1m(3)
     sh = W.make_shape(16, 2, 256, torch.bfloat16, 1 / 16)
@@ -483,3 +484,161 @@ def test_verify_1m_paged_sampled_head():
         eo = max_err(out[0, rows], o_ref)
         el = max_err(lse[0, rows], l_ref)
         assert eo <= TOL["bf16"] and el <= TOL["bf16"], (i, eo, el)
+
+
+# ============================================================== full sizes, benchmark launch configuration
+def _gather(pool, bt_row, positions):
+    """Tokens [T][H_kv][D] of a paged pool at `positions` (device gather through the block table)."""
+    return pool[bt_row[positions // 16].long(), :, positions % 16, :]
+
+
+def _fill_ring(sh, ring, k, v, bt_row, n0, S, Wn, R):
+    """Ring of one sequence at length n0: sinks 0..S-1 and the last W + R context tokens, gathered from the pool."""
+    pos_s = torch.arange(0, S, device=DEV)
+    pos_t = torch.arange(n0 - (Wn + R), n0, device=DEV)
+    W.ring_append(sh, ring, _gather(k, bt_row, pos_s)[None].contiguous(), _gather(v, bt_row, pos_s)[None].contiguous(), [0])
+    W.ring_append(sh, ring, _gather(k, bt_row, pos_t)[None].contiguous(), _gather(v, bt_row, pos_t)[None].contiguous(),
+                  [n0 - (Wn + R)])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+def test_draft_1m_benchmark_launch_config(mode):
+    """C3 at its real size in the benchmark's configuration: bf16 PV weights, default splits
+    (the native step runs on the matrix-core kernel), ring with gamma - 1 headroom; one KV head checked."""
+    S, Wn, R = 4, 4096, 2
+    say("draft 1M bench config", mode)
+    n0, bt, k, v, btd = _paged_1m(6)
+    sh = W.make_shape(16, 2, 256, torch.bfloat16, 1 / 16)
+    desc = W.make_paged(k, v, btd)
+    kn = synth.normal((1, 1, 2, 256), 6, "kn", 0.5, "bf16", DEV)
+    vn = synth.normal((1, 1, 2, 256), 6, "vn", 0.5, "bf16", DEV)
+    q = synth.normal((1, 16, 256), 6, "q", 1.0, "bf16", DEV)
+    n = n0 + 1
+    if mode == O.FULL:
+        W.paged_append(sh, desc, kn, vn, [n0])
+        ws = W.workspace(W.draft_workspace_bytes(W.FULL, sh, [n], 0), DEV)
+        parts = W.draft_attn(W.FULL | W.DRAFT_FAST_PV, sh, q, [n], ws, paged=desc)
+    else:
+        ring = RingCache(1, 2, 256, S, Wn, torch.bfloat16, headroom=R)
+        _fill_ring(sh, ring.desc, k, v, btd[0], n0, S, Wn, R)
+        W.ring_append(sh, ring.desc, kn, vn, [n0])
+        ws = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, [n], 0, S, Wn, R), DEV)
+        parts = W.draft_attn(W.SINK_WINDOW | W.DRAFT_FAST_PV, sh, q, [n], ws, ring=ring.desc)
+    out, lse = run_combine(parts, 16, 256, 1)
+    torch.cuda.synchronize()
+    kh, vh = synth.bf16_bits(k), synth.bf16_bits(v)
+    h = 1
+    sk = O.ConcatKV(O.PagedKV(kh, bt[0], 16, "bf16", n0), O.LogicalKV(synth.bf16_bits(kn[0]), "bf16"))
+    sv = O.ConcatKV(O.PagedKV(vh, bt[0], 16, "bf16", n0), O.LogicalKV(synth.bf16_bits(vn[0]), "bf16"))
+    qf = O.to_f64(synth.bf16_bits(q[0]), "bf16")
+    rows = slice(h * 8, h * 8 + 8)
+    o_ref, l_ref = O.attention_over(qf[rows], sk, sv, O.visible_positions(n, mode, S, Wn), h, 1 / 16)
+    eo, el = max_err(out[0, rows], o_ref), max_err(lse[0, rows], l_ref)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+def test_draft_131k_three_steps_full_size(mode):
+    """C2 at its real size: 131,072-token context (identity block table), gamma = 3 draft steps,
+    ring of S + W slots, benchmark launch configuration; one KV head checked at every step."""
+    wl = synth.workload("draft_131k_bf16")
+    S, Wn = wl.sink, wl.window
+    say("draft 131K full size", mode)
+    n0 = wl.contexts[0]
+    nb = synth.blocks_for(n0 + wl.gamma, 16)
+    bt, total = synth.block_table(wl.seed, [nb], permuted=False)
+    btd = torch.from_numpy(bt).to(DEV)
+    k = synth.normal((total, 2, 16, 256), wl.seed, "c2k", wl.kv_scale, "bf16", DEV)
+    v = synth.normal((total, 2, 16, 256), wl.seed, "c2v", wl.kv_scale, "bf16", DEV)
+    kh, vh = synth.bf16_bits(k), synth.bf16_bits(v)                 # the context as generated (before appends)
+    sh = W.make_shape(16, 2, 256, torch.bfloat16, wl.scale)
+    desc = W.make_paged(k, v, btd)
+    if mode == O.SINK_WINDOW:
+        ring = RingCache(1, 2, 256, S, Wn, torch.bfloat16)
+        _fill_ring(sh, ring.desc, k, v, btd[0], n0, S, Wn, 0)
+    kn = synth.normal((wl.gamma, 1, 1, 2, 256), wl.seed, "c2kn", wl.kv_scale, "bf16", DEV)
+    vn = synth.normal((wl.gamma, 1, 1, 2, 256), wl.seed, "c2vn", wl.kv_scale, "bf16", DEV)
+    q = synth.normal((wl.gamma, 1, 16, 256), wl.seed, "c2q", 1.0, "bf16", DEV)
+    h = 0
+    for j in range(wl.gamma):
+        n = n0 + j + 1
+        if mode == O.FULL:
+            W.paged_append(sh, desc, kn[j], vn[j], [n - 1])
+            ws = W.workspace(W.draft_workspace_bytes(W.FULL, sh, [n], 0), DEV)
+            parts = W.draft_attn(W.FULL | W.DRAFT_FAST_PV, sh, q[j], [n], ws, paged=desc)
+        else:
+            W.ring_append(sh, ring.desc, kn[j], vn[j], [n - 1])
+            ws = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, [n], 0, S, Wn), DEV)
+            parts = W.draft_attn(W.SINK_WINDOW | W.DRAFT_FAST_PV, sh, q[j], [n], ws, ring=ring.desc)
+        out, lse = run_combine(parts, 16, 256, 1)
+        torch.cuda.synchronize()
+        new_k = synth.bf16_bits(kn[:j + 1, 0, 0])                   # [j+1][H_kv][D]
+        new_v = synth.bf16_bits(vn[:j + 1, 0, 0])
+        sk = O.ConcatKV(O.PagedKV(kh, bt[0], 16, "bf16", n0), O.LogicalKV(new_k, "bf16"))
+        sv = O.ConcatKV(O.PagedKV(vh, bt[0], 16, "bf16", n0), O.LogicalKV(new_v, "bf16"))
+        qf = O.to_f64(synth.bf16_bits(q[j, 0]), "bf16")
+        rows = slice(h * 8, h * 8 + 8)
+        o_ref, l_ref = O.attention_over(qf[rows], sk, sv, O.visible_positions(n, mode, S, Wn), h, wl.scale)
+        eo, el = max_err(out[0, rows], o_ref), max_err(lse[0, rows], l_ref)
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"], (j, eo, el)
+
+
+@pytest.mark.slow
+def test_mixed_batch_full_sizes():
+    """C5 at its real sizes: 4 sequences of 32K / 131K / 512K / 1M tokens in one call, one block
+    table permutation split over them; full mode and window mode with W in {1,024, 4,096, 16,384}
+    (default splits, bf16 PV weights); checked on one KV head (full mode: the shortest and the
+    longest sequence; window mode: all four)."""
+    wl = synth.workload("mixed_4seq_bf16")
+    S, R = wl.sink, wl.gamma - 1
+    say("mixed batch full sizes")
+    lens0 = list(wl.contexts)
+    B = len(lens0)
+    bt, total = synth.block_table(wl.seed, [synth.blocks_for(n + 1, 16) for n in lens0], permuted=True)
+    btd = torch.from_numpy(bt).to(DEV)
+    k = synth.normal((total, 2, 16, 256), wl.seed, "c5k", wl.kv_scale, "bf16", DEV)
+    v = synth.normal((total, 2, 16, 256), wl.seed, "c5v", wl.kv_scale, "bf16", DEV)
+    kh, vh = synth.bf16_bits(k), synth.bf16_bits(v)
+    sh = W.make_shape(16, 2, 256, torch.bfloat16, wl.scale)
+    desc = W.make_paged(k, v, btd)
+    kn = synth.normal((B, 1, 2, 256), wl.seed, "c5kn", wl.kv_scale, "bf16", DEV)
+    vn = synth.normal((B, 1, 2, 256), wl.seed, "c5vn", wl.kv_scale, "bf16", DEV)
+    q = synth.normal((B, 16, 256), wl.seed, "c5q", 1.0, "bf16", DEV)
+    qf = O.to_f64(synth.bf16_bits(q), "bf16")
+    lens = [n + 1 for n in lens0]
+    h = 1
+    rows = slice(h * 8, h * 8 + 8)
+
+    def ref(b, mode, Wn):
+        sk = O.ConcatKV(O.PagedKV(kh, bt[b], 16, "bf16", lens0[b]), O.LogicalKV(synth.bf16_bits(kn[b]), "bf16"))
+        sv = O.ConcatKV(O.PagedKV(vh, bt[b], 16, "bf16", lens0[b]), O.LogicalKV(synth.bf16_bits(vn[b]), "bf16"))
+        return O.attention_over(qf[b, rows], sk, sv, O.visible_positions(lens[b], mode, S, Wn), h, wl.scale)
+
+    # window mode first (the pool is left as generated), one ring per W
+    for Wn in wl.windows:
+        ring = RingCache(B, 2, 256, S, Wn, torch.bfloat16, headroom=R)
+        for b in range(B):
+            sub = W.Ring(ring.k[b].data_ptr(), ring.v[b].data_ptr(), ring.tags[b].data_ptr(), S, Wn, R)
+            _fill_ring(sh, sub, k, v, btd[b], lens0[b], S, Wn, R)
+        W.ring_append(sh, ring.desc, kn, vn, lens0)
+        ws = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, lens, 0, S, Wn, R), DEV)
+        parts = W.draft_attn(W.SINK_WINDOW | W.DRAFT_FAST_PV, sh, q, lens, ws, ring=ring.desc)
+        out, lse = run_combine(parts, 16, 256, B)
+        torch.cuda.synchronize()
+        for b in range(B):
+            o_ref, l_ref = ref(b, O.SINK_WINDOW, Wn)
+            eo, el = max_err(out[b, rows], o_ref), max_err(lse[b, rows], l_ref)
+            assert eo <= TOL["bf16"] and el <= TOL["bf16"], (Wn, b, eo, el)
+    # full mode over the paged pool
+    W.paged_append(sh, desc, kn, vn, lens0)
+    ws = W.workspace(W.draft_workspace_bytes(W.FULL, sh, lens, 0), DEV)
+    parts = W.draft_attn(W.FULL | W.DRAFT_FAST_PV, sh, q, lens, ws, paged=desc)
+    out, lse = run_combine(parts, 16, 256, B)
+    torch.cuda.synchronize()
+    for b in (0, 3):
+        o_ref, l_ref = ref(b, O.FULL, 1)
+        eo, el = max_err(out[b, rows], o_ref), max_err(lse[b, rows], l_ref)
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"], ("full", b, eo, el)
+
