@@ -156,16 +156,27 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // ----------------------------------------------------------------------------- wave reductions
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
+// All cross-lane steps are VALU: DPP permutes inside 16-lane rows and gfx950's
+// v_permlane16_swap / v_permlane32_swap across rows, so a reduction costs six
+// dependent VALU operations and no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i inside each 8 lanes
+constexpr int kDppMirror = 0x140;       // lane i <-> 15 - i inside each 16-lane row
+constexpr int kDppRowRor = 0x120;       // + s: rotate by s inside each 16-lane row
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
+// value of the partner row (rows of 16 lanes paired 0-1, 2-3), combined
+__device__ __forceinline__ float rows16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rows16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // max / sum of lane l and lane l ^ 32 (gfx950 v_permlane32_swap: a VALU swap
@@ -177,6 +188,55 @@ __device__ __forceinline__ float halves_max(float x) {
 __device__ __forceinline__ float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// max / sum over all 64 lanes, returned in every lane (the sum's rounding
+// order may differ between lanes)
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f32<kDppXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppMirror>(x));
+  return halves_max(rows16_max(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f32<kDppXor1>(x);
+  x += dpp_f32<kDppXor2>(x);
+  x += dpp_f32<kDppHalfMirror>(x);
+  x += dpp_f32<kDppMirror>(x);
+  return halves_sum(rows16_sum(x));
+}
+
+// The value of lane (this lane ^ M) for M = 8, 16, 32: a rotation by 8 inside
+// the 16-lane row, or the row / half swaps (which hand each lane both its own
+// and its partner's value; the lane's row parity picks the partner's).
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+  static_assert(M == 8 || M == 16 || M == 32, "partner distance 8, 16 or 32");
+  const int lane = __lane_id();
+  if constexpr (M == 8) {
+    return dpp_f32<kDppRowRor + 8>(x);
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(((lane >> 4) & 1) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(((lane >> 5) & 1) ? r[0] : r[1]);
+  }
+}
+
+// Sum over the lanes congruent to this lane modulo STRIDE (a power of two):
+// rotations by STRIDE, 2 STRIDE, ... inside the 16-lane rows, then the row swaps.
+template <int STRIDE>
+__device__ __forceinline__ float strided_lane_sum(float x) {
+  static_assert(STRIDE >= 1 && STRIDE <= 64 && (STRIDE & (STRIDE - 1)) == 0, "power-of-two stride");
+  if constexpr (STRIDE <= 1) x += dpp_f32<kDppXor1>(x);
+  if constexpr (STRIDE <= 2) x += dpp_f32<kDppRowRor + 2>(x);
+  if constexpr (STRIDE <= 4) x += dpp_f32<kDppRowRor + 4>(x);
+  if constexpr (STRIDE <= 8) x += dpp_f32<kDppRowRor + 8>(x);
+  if constexpr (STRIDE <= 16) x = rows16_sum(x);
+  if constexpr (STRIDE <= 32) x = halves_sum(x);
+  return x;
 }
 
 // 2^x on the hardware exponential (v_exp_f32): exp2(-inf) = 0; results below

@@ -169,11 +169,13 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
   // (which the matrix-core kernel uses) measured 10% slower here.
   // Register ring: the K and V of tile i arrive in slot i % kRing, issued
   // kRing - 1 tiles ahead, so two tiles per wave are in flight while one is
-  // computed.
-  constexpr int kRing = 3;
+  // computed.  Window mode reads one or a few tiles per work item (its splits
+  // are short so that many work items cover the ring at once): a single slot,
+  // a third of the code on that latency-bound path.
+  constexpr int kRing = WINDOW ? 1 : 3;
   u32x4 kreg[kRing][NCH];
   uint2 vreg[kRing][NV];
-  int tag[kRing] = {0, 0, 0};
+  int tag[kRing] = {};
 
   // Loads of tile `it`, clamped to the last tile so every body issues the same
   // number of loads.  `ln` is this lane's index.
@@ -371,19 +373,24 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
     }
   };
 
-  // Three bodies per trip over fixed slots; leaving early exits the loop, so the
-  // latch is only reached after all three and its pending loads always match.
+  // One body per tile with a single slot; otherwise three bodies per trip over
+  // fixed slots, where leaving early exits the loop, so the latch is only
+  // reached after all three and its pending loads always match.
   if (ntiles > 0) {
+    if constexpr (kRing == 1) {
+      for (int it = 0; it < ntiles; ++it) body(it, 0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kRing - 1; ++i) issue(i, i, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int it = 0;; it += kRing) {
-      body(it, 0);
-      if (it + 1 >= ntiles) break;
-      body(it + 1, 1);
-      if (it + 2 >= ntiles) break;
-      body(it + 2, 2);
-      if (it + 3 >= ntiles) break;
+      for (int i = 0; i < kRing - 1; ++i) issue(i, i, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int it = 0;; it += kRing) {
+        body(it, 0);
+        if (it + 1 >= ntiles) break;
+        body(it + 1, 1);
+        if (it + 2 >= ntiles) break;
+        body(it + 2, 2);
+        if (it + 3 >= ntiles) break;
+      }
     }
   }
 
@@ -392,11 +399,9 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
 #pragma unroll
   for (int g = 0; g < G; ++g) l[g] = wave_sum(l_lane[g]);
 #pragma unroll
-  for (int m = LPR; m < 64; m <<= 1)
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < EV; ++e) o[g][e] += __shfl_xor(o[g][e], m);
+    for (int e = 0; e < EV; ++e) o[g][e] = strided_lane_sum<LPR>(o[g][e]);
 
   const int rows = a.num_q_heads;
   const int pv_tok = lane / LPR, pv_d = lane % LPR;

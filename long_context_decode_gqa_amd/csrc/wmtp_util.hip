@@ -59,16 +59,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
       st.w += e;
     }
   }
-  // shuffle tree over the 16 split lanes of this wave (lane = 4 sl + dl)
-#pragma unroll
-  for (int m = kCombineDL; m < 64; m <<= 1) {
+  // merge tree over the split lanes of this wave (lane = kCombineDL sl + dl):
+  // partners 8, 16 and 32 lanes away, exchanged without LDS
+  auto merge_with = [&](auto partner) {
     MergeState o;
-    o.m = __shfl_xor(st.m, m);
-    o.w = __shfl_xor(st.w, m);
+    o.m = partner(st.m);
+    o.w = partner(st.w);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.acc[e] = __shfl_xor(st.acc[e], m);
+    for (int e = 0; e < 4; ++e) o.acc[e] = partner(st.acc[e]);
     st = merge_state(st, o);
-  }
+  };
+  static_assert(kCombineDL == 8, "the merge tree starts 8 lanes apart");
+  merge_with([](float x) { return lane_xor<8>(x); });
+  merge_with([](float x) { return lane_xor<16>(x); });
+  merge_with([](float x) { return lane_xor<32>(x); });
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) < kCombineDL) sm[wave][dl] = st;
   __syncthreads();
