@@ -488,7 +488,7 @@ def step_bytes(n0, wl, windowed):
 
 def sweep(flag, steps, warmup, dev, contexts, gammas):
     """Decode steps across context length and draft depth, both draft modes, beside the
-    bytes model's native/windowed ratio (the wedge that grows with context)."""
+    bytes model's native/windowed ratio (which widens as the context grows)."""
     rows = []
     for n0 in contexts:
         for g in gammas:
@@ -537,7 +537,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():

@@ -264,7 +264,7 @@ int wmtp_debug_window_positions(int32_t sink, int32_t window, int32_t headroom, 
 
 /* KV memory of one sequence at `context` tokens with a native or a windowed
  * draft, and the sequences an HBM budget admits (Windowed-MTP summary,
- * Abstract: the ring reclaims the otherwise dead draft pool, 7.7-11.1% of
+ * Abstract: the ring frees the draft pool the window no longer reads, 7.7-11.1% of
  * total KV at 1M, room for one more concurrent 1M request).  Every
  * full-attention layer (the `target_layers`, and the native draft) keeps a
  * paged pool of ceil(context / 16) blocks of K and V; one int32 block table per

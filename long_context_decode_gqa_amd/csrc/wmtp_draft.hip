@@ -1,7 +1,7 @@
 // Split-K flash-decoding for the MTP draft head on gfx950.
 //
 // The native MTP draft attends over the whole KV cache at every draft step, so
-// its read grows with context; Windowed-MTP attends over attention-sink tokens
+// its read scales with the context length; Windowed-MTP attends over sink tokens
 // plus a window of recent tokens held in a compact ring ("Windowed-MTP:
 // Removing the Full-Context Draft-KV Tax at Million-Token Context", arxivlens
 // summary, Abstract; readpriors.com post, What happened).  One kernel serves

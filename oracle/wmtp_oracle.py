@@ -12,12 +12,12 @@ it follows and the reading taken where the text is silent):
   [P1] "Does speculative decode still pay at 128K context?" (howtospark.com case
        study): Method (verify cycle = three draft forwards plus one batched
        verify), Findings (1 draft layer against 10 full-attention target layers,
-       the draft tax of about 0.5 ms per draft step), Limitations (the technique
+       about 0.5 ms of draft cost per draft step), Limitations (the technique
        is a sliding window plus attention sink on the draft's attention).
   [P2] "Your Million-Token Pipeline Is Bleeding Speed You Don't Know You're
        Losing" (readpriors.com): What happened (the native draft reads the whole
        cache at every draft step; the windowed draft keeps a constant working
-       set, dropping roughly 99% of entries at 1M; Figure 3's cost-side ratio).
+       set that leaves out about 99% of entries at 1M; Figure 3's cost-side ratio).
   [P3] "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token
        Context" (arxivlens.com summary): Abstract (gamma draft forwards per
        decode step, window plus sink on the draft only, full-context target
@@ -105,8 +105,8 @@ def draft_entries_read(n: int, mode: int, sink: int = 0, window: int = 0) -> int
 def ring_slot(p: int, sink: int, window: int, headroom: int = 0) -> int:
     """Slot of absolute position p in the compact ring of S + W + R slots.
 
-    [P3 Abstract] names a compact ring buffer holding the draft's window; the
-    layout is this build's reading: sinks occupy slots 0..S-1 in place, every
+    [P3 Abstract] names a compact ring buffer holding the draft's window but
+    gives no layout; the one taken here: sinks occupy slots 0..S-1 in place, every
     later position cycles through the C = W + R slots S..S+C-1.  R >= 0 extra
     slots ("headroom") let drafted tokens that verification rejects be written
     without overwriting an entry that a later window still needs.
@@ -373,8 +373,9 @@ def memory_plan(num_kv_heads: int, head_dim: int, elem_bytes: int, target_layers
     """KV memory of one sequence with a native or a windowed draft, and how many fit a budget.
 
     [P3 Abstract] the window leaves most of the draft's KV unread and a compact
-    ring buffer turns that into capacity: it reclaims the otherwise dead draft
-    pool (7.7-11.1% of total KV at 1M), room for one more concurrent 1M request.
+    ring buffer turns that into capacity: the draft's full pool, which nothing
+    reads any more, is freed (7.7-11.1% of total KV at 1M), room for one more
+    concurrent 1M request.
     Reading: every full-attention layer, target or native draft, keeps a paged
     pool of ceil(context / block_size) blocks of K and V; one int32 block table
     per sequence serves all of them; the windowed draft keeps only its ring

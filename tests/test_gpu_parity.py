@@ -430,7 +430,8 @@ def _paged_1m(seed, hk=2, d=256, extra=8):
 
 @pytest.mark.slow
 def test_draft_full_1m_paged_sampled_head():
-    """C3 shape at its real size: 1,048,576-token permuted paged pool, 256-token splits."""
+    """Native draft step over a 1,048,576-token paged pool (random block permutation), fp32 PV
+    weights and 256-token splits (the dot-product kernel); one KV head checked."""
     say("draft 1M")
     n0, bt, k, v, btd = _paged_1m(2)
     sh = W.make_shape(16, 2, 256, torch.bfloat16, 1 / 16)
@@ -458,7 +459,7 @@ def test_draft_full_1m_paged_sampled_head():
 
 @pytest.mark.slow
 def test_verify_1m_paged_sampled_head():
-    """C4's verify layer at its real size and in the benchmark's launch configuration (default
+    """One target layer's verify at 1M context in the benchmark's launch configuration (default
     splits): 4 causal queries over 1,048,580 keys, two query tokens checked on one KV head."""
     say("verify 1M")
     n0, bt, k, v, btd = _paged_1m(3)
@@ -504,8 +505,9 @@ def _fill_ring(sh, ring, k, v, bt_row, n0, S, Wn, R):
 @pytest.mark.slow
 @pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
 def test_draft_1m_benchmark_launch_config(mode):
-    """C3 at its real size in the benchmark's configuration: bf16 PV weights, default splits
-    (the native step runs on the matrix-core kernel), ring with gamma - 1 headroom; one KV head checked."""
+    """Draft step at 1,048,576 tokens (permuted paged pool) in the benchmark's configuration: bf16 PV
+    weights, default splits (the native step runs on the matrix-core kernel), ring with gamma - 1
+    headroom; one KV head checked."""
     S, Wn, R = 4, 4096, 2
     say("draft 1M bench config", mode)
     n0, bt, k, v, btd = _paged_1m(6)
@@ -541,7 +543,7 @@ def test_draft_1m_benchmark_launch_config(mode):
 @pytest.mark.slow
 @pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
 def test_draft_131k_three_steps_full_size(mode):
-    """C2 at its real size: 131,072-token context (identity block table), gamma = 3 draft steps,
+    """Single draft layer at 131,072 tokens (identity block table), gamma = 3 draft steps,
     ring of S + W slots, benchmark launch configuration; one KV head checked at every step."""
     wl = synth.workload("draft_131k_bf16")
     S, Wn = wl.sink, wl.window
@@ -587,7 +589,7 @@ def test_draft_131k_three_steps_full_size(mode):
 
 @pytest.mark.slow
 def test_mixed_batch_full_sizes():
-    """C5 at its real sizes: 4 sequences of 32K / 131K / 512K / 1M tokens in one call, one block
+    """Mixed batch: 4 sequences of 32K / 131K / 512K / 1M tokens in one call, one block
     table permutation split over them; full mode and window mode with W in {1,024, 4,096, 16,384}
     (default splits, bf16 PV weights); checked on one KV head (full mode: the shortest and the
     longest sequence; window mode: all four)."""

@@ -88,7 +88,7 @@ def _ratio(n0, gamma, L=10, S=4, Wn=4096):
 
 
 def test_wedge_widens_with_context():
-    """[P3 Abstract] the speedup grows with context: the bytes ratio never falls as n0 grows,
+    """[P3 Abstract] the speedup increases with the context length: the bytes ratio never falls as n0 grows,
     and it is exactly 1 while the window still covers the whole context."""
     for gamma in (3, 5, 8):
         ctx = [2048, 4096 - gamma, 8192, 32768, 131072, 524288, 1 << 20, 1 << 22]
@@ -99,7 +99,7 @@ def test_wedge_widens_with_context():
 
 
 def test_deeper_drafts_pay_more_at_long_context():
-    """More draft forwards per cycle multiply the native draft tax; the windowed draft's is constant."""
+    """More draft forwards per cycle multiply the native draft's cost; the windowed draft's stays constant."""
     for n0 in (131072, 1 << 20):
         r = [_ratio(n0, g) for g in (1, 3, 5, 8)]
         assert all(b > a for a, b in zip(r, r[1:]))
