@@ -369,6 +369,270 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
   }
 }
 
+// Two row tiles (33..64 packed rows) on two teams of 4 waves, 512 threads.
+// With both row tiles in one wave the per-tile chain of LDS stages, barriers,
+// MFMA and softmax has nothing to hide behind at one wave per SIMD; here team 0
+// loads K and V exactly as the one-row-tile kernel, stages both in LDS and
+// computes row tile 0 of tile t, while team 1 computes row tile 1 of tile t - 1
+// from those stages: every SIMD runs one wave of each team, and HBM is read
+// once.  Stages are double-buffered by tile parity; every tile step has two
+// barriers, so team 0 overwrites a stage only after team 1 has read it.
+template <int G>
+__global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs a) {
+  constexpr int ROWB = kVD * 2;
+  constexpr float TAU = 8.0f;
+
+  __shared__ __attribute__((aligned(16))) uint8_t k_stage[2][4 * kVStage];    // [parity][wave quarter]
+  __shared__ __attribute__((aligned(16))) u32x4 v_stage[2][4][4][64];         // [parity][wave][piece][lane]
+  __shared__ __attribute__((aligned(16))) float sc_lds[2][4 * 4 * 64 * 4];    // [team][(wave*4+q)*64+lane][4]
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int team = wid >> 2, wave = wid & 3;
+  const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, tq = a.t_q;
+  const int rows = tq * G;
+  const int h = blockIdx.x % Hkv;
+  const int sg = blockIdx.x / Hkv;
+  const int b = seq_of_split(a, sg);
+  const int n = a.seq_len[b];
+  const int t_begin = (sg - a.split_base[b]) * a.chunk;
+  const int t_end = min(t_begin + a.chunk, n);
+  const int ntiles = (t_end - t_begin + kVTile - 1) / kVTile;
+  const int last_blk_idx = (t_end - 1) >> 4;
+  const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + wave * (kVQ * 2);
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + wave * (kVQ * 2);
+
+  const int c32 = lane & 31;
+  const int kh = lane >> 5;
+  const int row0 = 32 * team;    // this team's first packed row
+
+  u32x4 qreg[kVKS];
+  {
+    const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
+    const int j = row0 + c32;
+    const int i = j / G, g = j % G;
+    const int64_t qrow = ((int64_t)b * tq + i) * Hq + (int64_t)h * G + g;
+#pragma unroll
+    for (int s = 0; s < kVKS; ++s) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (j < rows) x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + wave * (kVQ * 2) + (2 * s + kh) * 16);
+      qreg[s] = x;
+    }
+#pragma unroll
+    for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(qreg[s]));
+  }
+
+  const float c = a.scale_log2;
+  const int row_last = min(n - tq + (row0 + c32) / G, t_end - 1);
+  const int all_last = min(n - tq, t_end - 1);
+
+  f32x16 O[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) O[e][x] = 0.f;
+  float M = kNegInf, l_lane = 0.f;
+  float* sc = sc_lds[team];
+
+  // partial S^T of this wave's quarter of D for the team's row tile, into the team's exchange
+  auto qk_exchange = [&](const uint8_t* kst) {
+    f32x16 sacc;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kVKS; ++s) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + vpiece(c32, 2 * s + kh) * 16);
+      sacc = mfma32(ka, qreg[s], sacc);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 w4 = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+      *reinterpret_cast<f32x4*>(sc + ((wave * 4 + q) * 64 + lane) * 4) = w4;
+    }
+  };
+  auto read_scores = [&](float (&s2)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(sc + (q * 64 + lane) * 4);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) x += *reinterpret_cast<const f32x4*>(sc + ((w * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s2[4 * q + e] = x[e];
+    }
+  };
+  // mask, lazy maximum, bf16 weights and O += P V for the tile starting at key t0
+  auto softmax_pv = [&](int t0, float (&s2)[16], const uint32_t (&vv)[2][8]) {
+    if (t0 + kVTile - 1 > all_last) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int key = t0 + 8 * (x >> 2) + 4 * kh + (x & 3);
+        s2[x] = key <= row_last ? s2[x] : kNegInf;
+      }
+    }
+    float mx = s2[0];
+#pragma unroll
+    for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s2[x]);
+    mx = halves_max(mx) * c;
+    if (__ballot(mx > M + TAU) != 0) {
+      const float mn = fmaxf(M, mx);
+      const float alpha = (M == kNegInf) ? 0.f : fast_exp2(M - mn);
+      M = mn;
+      l_lane *= alpha;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const float ar = __shfl(alpha, 8 * (x >> 2) + 4 * kh + (x & 3));
+        O[0][x] *= ar;
+        O[1][x] *= ar;
+      }
+    }
+    const float negM = M == kNegInf ? 0.f : -M;
+    uint32_t pk[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float p0 = fast_exp2(fmaf(s2[2 * q], c, negM));
+      const float p1 = fast_exp2(fmaf(s2[2 * q + 1], c, negM));
+      pk[q] = pack_bf16x2(p0, p1);
+      l_lane = dot2_bf16(pk[q], kBf16One2, l_lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 pa = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        u32x4 vb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          vb[q] = __builtin_amdgcn_perm(vv[ks][2 * q + 1], vv[ks][2 * q], e ? 0x07060302u : 0x05040100u);
+        O[e] = mfma32(pa, vb, O[e]);
+      }
+    }
+  };
+
+  if (team == 0) {
+    // ---- loader team: the one-row-tile kernel's loads and ring, plus the stages for team 1
+    auto tile_runs = [&](int it, int64_t (&run)[2]) {
+      const int t0 = t_begin + min(it, ntiles - 1) * kVTile;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int bi = min((t0 >> 4) + j, last_blk_idx);
+        run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, ROWB);
+      }
+    };
+    constexpr int kRing = 3;
+    u32x4 kreg[kRing][kVLoads];
+    uint32_t vreg[kRing][2][8];
+    int64_t run_next[2];
+    const uint32_t k_off0 = (uint32_t)((lane >> 3) * ROWB + (lane & 7) * 16);
+    const uint8_t* kbase_hi = kbase + 8 * ROWB;
+    const uint32_t v_off0 = (uint32_t)(4 * kh * ROWB + c32 * 4);
+    auto issue = [&](int slot, const int64_t (&run)[2], uint32_t k_off, uint32_t v_off) {
+#pragma unroll
+      for (int l = 0; l < kVLoads; ++l)
+        kreg[slot][l] = load_nt<u32x4>(((l & 1) ? kbase_hi : kbase) + run[l >> 1], k_off);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          vreg[slot][ks][jj] =
+              load_nt<uint32_t>(vbase + run[ks] + (8 * (jj >> 2)) * ROWB, v_off + (jj & 3) * ROWB);
+    };
+    auto body = [&](int it, int slot) {
+      uint32_t k_off = k_off0, v_off = v_off0;
+      asm volatile("" : "+v"(k_off), "+v"(v_off));
+      const int t0 = t_begin + it * kVTile;
+      issue((slot + kRing - 1) % kRing, run_next, k_off, v_off);
+      __builtin_amdgcn_sched_barrier(0);
+      uint8_t* kst = k_stage[it & 1] + wave * kVStage;
+#pragma unroll
+      for (int l = 0; l < kVLoads; ++l) {
+        const int P = 64 * l + lane;
+        *reinterpret_cast<u32x4*>(kst + vpiece(P / kVNQ, P % kVNQ) * 16) = kreg[slot][l];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 w = {vreg[slot][q >> 1][4 * (q & 1)], vreg[slot][q >> 1][4 * (q & 1) + 1],
+                         vreg[slot][q >> 1][4 * (q & 1) + 2], vreg[slot][q >> 1][4 * (q & 1) + 3]};
+        v_stage[it & 1][wave][q][lane] = w;
+      }
+      qk_exchange(kst);
+      __syncthreads();
+      float s2[16];
+      read_scores(s2);
+      __builtin_amdgcn_sched_barrier(0);
+      tile_runs(it + kRing, run_next);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_pv(t0, s2, vreg[slot]);
+      __syncthreads();
+    };
+    if (ntiles > 0) {
+#pragma unroll
+      for (int i = 0; i < kRing - 1; ++i) {
+        tile_runs(i, run_next);
+        issue(i, run_next, k_off0, v_off0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      tile_runs(kRing - 1, run_next);
+      __builtin_amdgcn_sched_barrier(0);
+      int it = 0;
+      for (; it + 3 <= ntiles; it += 3) {
+        body(it, 0);
+        body(it + 1, 1);
+        body(it + 2, 2);
+      }
+      if (it < ntiles) body(it, 0);
+      if (it + 1 < ntiles) body(it + 1, 1);
+    }
+    // team 1 still computes the last tile: its two barriers
+    __syncthreads();
+    __syncthreads();
+  } else {
+    // ---- team 1: row tile 1 of tile it - 1, from team 0's stages
+    for (int it = 0; it <= ntiles; ++it) {
+      const int t = it - 1;
+      if (t >= 0) qk_exchange(k_stage[t & 1] + wave * kVStage);
+      __syncthreads();
+      if (t >= 0) {
+        float s2[16];
+        read_scores(s2);
+        uint32_t vv[2][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 w = v_stage[t & 1][wave][q][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[q >> 1][4 * (q & 1) + e] = w[e];
+        }
+        softmax_pv(t_begin + t * kVTile, s2, vv);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- normalise and write this wave's quarter of the team's live rows
+  const float l_row = halves_sum(l_lane);
+  const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const int rl = 8 * (x >> 2) + 4 * kh + (x & 3);
+    const float inv = __shfl(inv_row, rl);
+    const int row = row0 + rl;
+    if (row < rows) {
+      const int i = row / G, g = row % G;
+      const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
+      float2 w2;
+      w2.x = O[0][x] * inv;
+      w2.y = O[1][x] * inv;
+      *reinterpret_cast<float2*>(a.part_o + orow * kVD + wave * kVQ + 2 * c32) = w2;
+    }
+  }
+  if (wave == 0 && lane < 32 && row0 + lane < rows) {
+    const int row = row0 + lane;
+    const int i = row / G, g = row % G;
+    const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
+    a.part_lse[orow] = l_row > 0.f ? (M + __log2f(l_row)) * kLn2 : kNegInf;
+  }
+}
+
 template <int G>
 static hipError_t launch_rt(int rt, bool single, const SplitArgs& a, int grid, hipStream_t st) {
   if (single) {
@@ -376,7 +640,7 @@ static hipError_t launch_rt(int rt, bool single, const SplitArgs& a, int grid, h
   } else {
     switch (rt) {
       case 1: mfma_attn_kernel<G, 1, false><<<grid, 256, 0, st>>>(a); break;
-      case 2: mfma_attn_kernel<G, 2, false><<<grid, 256, 0, st>>>(a); break;
+      case 2: mfma_attn_teams_kernel<G><<<grid, 512, 0, st>>>(a); break;
       case 3: mfma_attn_kernel<G, 3, false><<<grid, 256, 0, st>>>(a); break;
       default: return hipErrorInvalidValue;
     }
