@@ -375,16 +375,18 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
 // loads K and V exactly as the one-row-tile kernel, stages both in LDS and
 // computes row tile 0 of tile t, while team 1 computes row tile 1 of tile t - 1
 // from those stages: every SIMD runs one wave of each team, and HBM is read
-// once.  Stages are double-buffered by tile parity; every tile step has two
-// barriers, so team 0 overwrites a stage only after team 1 has read it.
+// once.  One barrier per tile step: the K/V stages rotate over three buffers
+// and each team's score exchange over two, and since neither team can pass a
+// step's barrier before the other reaches it, team 0 rewrites a stage only
+// after team 1 has finished with it (160 KiB of LDS, the per-workgroup limit).
 template <int G>
 __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs a) {
   constexpr int ROWB = kVD * 2;
   constexpr float TAU = 8.0f;
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_stage[2][4 * kVStage];    // [parity][wave quarter]
-  __shared__ __attribute__((aligned(16))) u32x4 v_stage[2][4][4][64];         // [parity][wave][piece][lane]
-  __shared__ __attribute__((aligned(16))) float sc_lds[2][4 * 4 * 64 * 4];    // [team][(wave*4+q)*64+lane][4]
+  __shared__ __attribute__((aligned(16))) uint8_t k_stage[3][4 * kVStage];    // [tile % 3][wave quarter]
+  __shared__ __attribute__((aligned(16))) u32x4 v_stage[3][4][4][64];         // [tile % 3][wave][piece][lane]
+  __shared__ __attribute__((aligned(16))) float sc_lds[2][2][4 * 4 * 64 * 4]; // [team][tile & 1][(wave*4+q)*64+lane][4]
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -433,10 +435,9 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
 #pragma unroll
     for (int x = 0; x < 16; ++x) O[e][x] = 0.f;
   float M = kNegInf, l_lane = 0.f;
-  float* sc = sc_lds[team];
 
   // partial S^T of this wave's quarter of D for the team's row tile, into the team's exchange
-  auto qk_exchange = [&](const uint8_t* kst) {
+  auto qk_exchange = [&](const uint8_t* kst, float* sc) {
     f32x16 sacc;
 #pragma unroll
     for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       *reinterpret_cast<f32x4*>(sc + ((wave * 4 + q) * 64 + lane) * 4) = w4;
     }
   };
-  auto read_scores = [&](float (&s2)[16]) {
+  auto read_scores = [&](const float* sc, float (&s2)[16]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       f32x4 x = *reinterpret_cast<const f32x4*>(sc + (q * 64 + lane) * 4);
@@ -543,7 +544,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       const int t0 = t_begin + it * kVTile;
       issue((slot + kRing - 1) % kRing, run_next, k_off, v_off);
       __builtin_amdgcn_sched_barrier(0);
-      uint8_t* kst = k_stage[it & 1] + wave * kVStage;
+      uint8_t* kst = k_stage[it % 3] + wave * kVStage;
 #pragma unroll
       for (int l = 0; l < kVLoads; ++l) {
         const int P = 64 * l + lane;
@@ -553,17 +554,17 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       for (int q = 0; q < 4; ++q) {
         const u32x4 w = {vreg[slot][q >> 1][4 * (q & 1)], vreg[slot][q >> 1][4 * (q & 1) + 1],
                          vreg[slot][q >> 1][4 * (q & 1) + 2], vreg[slot][q >> 1][4 * (q & 1) + 3]};
-        v_stage[it & 1][wave][q][lane] = w;
+        v_stage[it % 3][wave][q][lane] = w;
       }
-      qk_exchange(kst);
+      float* sc = sc_lds[0][it & 1];
+      qk_exchange(kst, sc);
       __syncthreads();
       float s2[16];
-      read_scores(s2);
+      read_scores(sc, s2);
       __builtin_amdgcn_sched_barrier(0);
       tile_runs(it + kRing, run_next);
       __builtin_amdgcn_sched_barrier(0);
       softmax_pv(t0, s2, vreg[slot]);
-      __syncthreads();
     };
     if (ntiles > 0) {
 #pragma unroll
@@ -583,28 +584,27 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       if (it < ntiles) body(it, 0);
       if (it + 1 < ntiles) body(it + 1, 1);
     }
-    // team 1 still computes the last tile: its two barriers
-    __syncthreads();
+    // team 1 still computes the last tile: its barrier
     __syncthreads();
   } else {
     // ---- team 1: row tile 1 of tile it - 1, from team 0's stages
     for (int it = 0; it <= ntiles; ++it) {
       const int t = it - 1;
-      if (t >= 0) qk_exchange(k_stage[t & 1] + wave * kVStage);
+      float* sc = sc_lds[1][it & 1];
+      if (t >= 0) qk_exchange(k_stage[t % 3] + wave * kVStage, sc);
       __syncthreads();
       if (t >= 0) {
         float s2[16];
-        read_scores(s2);
+        read_scores(sc, s2);
         uint32_t vv[2][8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const u32x4 w = v_stage[t & 1][wave][q][lane];
+          const u32x4 w = v_stage[t % 3][wave][q][lane];
 #pragma unroll
           for (int e = 0; e < 4; ++e) vv[q >> 1][4 * (q & 1) + e] = w[e];
         }
         softmax_pv(t_begin + t * kVTile, s2, vv);
       }
-      __syncthreads();
     }
   }
 
