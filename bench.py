@@ -41,8 +41,8 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "fb16e35e476d97761b8eca3c70169784163a0e3d06f96991946978b457933514",
-                  "fetch_kib": 1053754.55, "write_kib": 8224.00, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_TRAFFIC = {"sources_sha256": "c002ebc5fd579120415e84d5d494ea05762f389a8731b7282b8f8562be370d00",
+                  "fetch_kib": 1053760.10, "write_kib": 8224.00, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
 
@@ -279,9 +279,11 @@ def _timed(fn, reps, before=_hold):
 def graph_step(step, mode, flag, reps):
     """One whole decode step captured in a HIP graph and replayed.
 
-    Eager work (clearing the outputs) runs between replays, and every replay's
-    outputs are compared with an eager step's, bit for bit (the kernels are
-    deterministic).  Returns (per-replay ms, all replays matched).
+    Eager work (clearing the outputs, snapshotting them) runs between replays,
+    and every replay's outputs are compared with an eager step's, bit for bit
+    (the kernels are deterministic).  Replays are queued back to back after an
+    untimed one, as the eager steps are, so that no replay starts from an idle
+    GPU.  Returns (per-replay ms, all replays matched).
     """
     cur = torch.cuda.current_stream()
     side = torch.cuda.Stream()
@@ -297,12 +299,21 @@ def graph_step(step, mode, flag, reps):
         step.draft(mode, flag)
         step.verify()
     torch.cuda.synchronize()
-    ok, times = True, []
+    gr.replay()
+    _hold()
+    evs, outs = [], []
     for _ in range(reps):
         step.out_d.zero_()
         step.out_v.zero_()
-        times += _timed(gr.replay, 1)
-        ok = ok and torch.equal(step.out_d, ref_d) and torch.equal(step.out_v, ref_v)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        gr.replay()
+        b.record()
+        evs.append((a, b))
+        outs.append((step.out_d.clone(), step.out_v.clone()))
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in evs]
+    ok = all(torch.equal(d, ref_d) and torch.equal(v, ref_v) for d, v in outs)
     del gr
     torch.cuda.synchronize()
     return times, ok
