@@ -41,8 +41,8 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "c002ebc5fd579120415e84d5d494ea05762f389a8731b7282b8f8562be370d00",
-                  "fetch_kib": 1053760.10, "write_kib": 8224.00, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_TRAFFIC = {"sources_sha256": "367c22f49888306f13292dfbe85a27737aea94d3e2664b492a95466fa7a21816",
+                  "fetch_kib": 1053696.33, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
 
@@ -67,13 +67,18 @@ def verify_traffic_bytes():
     return int(round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024))
 
 
+# Untimed launches (~0.3 ms each over 2 GiB) before a probe's timed ones: the device's
+# rate settles only after ~20 ms of sustained load.
+SETTLE_LAUNCHES = 60
+
+
 def stream_ceiling_gbps(dev, nbytes=2 << 30):
     """Best rate of the library's streaming-read probe over a 2 GiB buffer."""
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
     best = 0.0
     for wgs in (256, 512, 1024, 2048):
         sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
-        for _ in range(3):
+        for _ in range(SETTLE_LAUNCHES):
             W.stream_read(src, sink, wgs)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -102,7 +107,7 @@ def paged_ceiling_gbps(step):
     best = 0.0
     for wgs in (256, 512):
         sink = torch.empty(wgs * 256, dtype=torch.int32, device=k.device)
-        for _ in range(3):
+        for _ in range(SETTLE_LAUNCHES):
             W.stream_read_paged(k, v, runs, run_bytes, sink, wgs)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -174,35 +179,47 @@ class Step:
         self.out_v = torch.empty((1, (g + 1) * Hq, D), dtype=torch.float32, device=dev)
         self.lse_v = torch.empty((1, (g + 1) * Hq), dtype=torch.float32, device=dev)
 
-    def draft(self, mode, flag, ev=None):
+    def draft(self, mode, flag, ev=None, fused=True):
+        """gamma draft steps.  fused: each step's append runs inside its attention launch
+        (wmtp_draft_attn_append); else an append call precedes wmtp_draft_attn.  ev brackets
+        the first step's attention launch (with the fused append, that launch includes it)."""
         g, n0 = self.wl.gamma, self.n0
         for j in range(g):
             pos, n = n0 + j, n0 + j + 1
-            if mode == W.FULL:
-                W.paged_append(self.sh, self.layers[0][2], self.k_draft[j], self.v_draft[j], [pos])
-                if ev is not None:
-                    ev[0].record()
-                parts = W.draft_attn(W.FULL | flag, self.sh, self.q_draft[j], [n], self.ws_full,
-                                     paged=self.layers[0][2], chunk_tokens=self.chunk_full)
+            kw = dict(paged=self.layers[0][2], chunk_tokens=self.chunk_full) if mode == W.FULL else \
+                dict(ring=self.ring, chunk_tokens=self.chunk_win)
+            ws = self.ws_full if mode == W.FULL else self.ws_win
+            if not fused:
+                if mode == W.FULL:
+                    W.paged_append(self.sh, self.layers[0][2], self.k_draft[j], self.v_draft[j], [pos])
+                else:
+                    W.ring_append(self.sh, self.ring, self.k_draft[j], self.v_draft[j], [pos])
+            if ev is not None:
+                ev[0].record()
+            if fused:
+                parts = W.draft_attn_append(mode | flag, self.sh, self.q_draft[j], self.k_draft[j], self.v_draft[j],
+                                            [n], ws, **kw)
             else:
-                W.ring_append(self.sh, self.ring, self.k_draft[j], self.v_draft[j], [pos])
-                if ev is not None:
-                    ev[0].record()
-                parts = W.draft_attn(W.SINK_WINDOW | flag, self.sh, self.q_draft[j], [n], self.ws_win,
-                                     ring=self.ring, chunk_tokens=self.chunk_win)
+                parts = W.draft_attn(mode | flag, self.sh, self.q_draft[j], [n], ws, **kw)
             if ev is not None:
                 ev[1].record()
                 ev = None
             W.combine(parts, self.out_d, self.lse_d)
 
-    def verify(self, ev_list=None):
+    def verify(self, ev_list=None, fused=True):
+        """The target layers' verify; fused: each layer's append runs inside its verify launch."""
         g, n0 = self.wl.gamma, self.n0
         for l in range(len(self.layers) - 1):
             desc = self.layers[l + 1][2]
-            W.paged_append(self.sh, desc, self.k_ver, self.v_ver, [n0])
+            if not fused:
+                W.paged_append(self.sh, desc, self.k_ver, self.v_ver, [n0])
             if ev_list is not None:
                 ev_list[l][0].record()
-            parts = W.verify_attn(self.sh, self.q_ver[l], g + 1, desc, [n0 + g + 1], self.ws_ver, self.split)
+            if fused:
+                parts = W.verify_attn_append(self.sh, self.q_ver[l], g + 1, desc, self.k_ver, self.v_ver,
+                                             [n0 + g + 1], self.ws_ver, self.split)
+            else:
+                parts = W.verify_attn(self.sh, self.q_ver[l], g + 1, desc, [n0 + g + 1], self.ws_ver, self.split)
             if ev_list is not None:
                 ev_list[l][1].record()
             W.combine(parts, self.out_v, self.lse_v)
@@ -213,21 +230,24 @@ def kv_bytes(tokens, wl):
 
 
 def verify_launch_bytes(n, wl, t_q):
-    """Algorithmic bytes of one verify launch: visible K/V, queries, block-table entries."""
-    return kv_bytes(n, wl) + t_q * wl.num_q_heads * wl.head_dim * 2 + synth.blocks_for(n, 16) * 4
+    """Algorithmic bytes of one verify launch: visible K/V, queries, block-table entries, and the
+    t_q new tokens' K/V written into the cache (the append runs inside the launch)."""
+    return kv_bytes(n, wl) + t_q * wl.num_q_heads * wl.head_dim * 2 + synth.blocks_for(n, 16) * 4 + kv_bytes(t_q, wl)
 
 
 def draft_launch_bytes(entries, wl, paged):
-    b = kv_bytes(entries, wl) + wl.num_q_heads * wl.head_dim * 2
+    """Algorithmic bytes of one draft launch: visible K/V, the query, block-table entries (or ring
+    tags), and the step's new token's K/V written into the cache (the append runs inside the launch)."""
+    b = kv_bytes(entries, wl) + wl.num_q_heads * wl.head_dim * 2 + kv_bytes(1, wl)
     return b + (synth.blocks_for(entries, 16) * 4 if paged else entries * 4)
 
 
-def time_steps(step, mode, flag, steps, warmup):
+def time_steps(step, mode, flag, steps, warmup, fused=True):
     """Warmup, then time `steps` decode steps; per-launch events on the dominant kernels."""
     torch.cuda.synchronize()
     for _ in range(warmup):
-        step.draft(mode, flag)
-        step.verify()
+        step.draft(mode, flag, fused=fused)
+        step.verify(fused=fused)
     torch.cuda.synchronize()
     L = len(step.layers) - 1
     ev_v = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
@@ -237,8 +257,8 @@ def time_steps(step, mode, flag, steps, warmup):
     torch.cuda.synchronize()
     ev_s[0].record()
     for s in range(steps):
-        step.draft(mode, flag, ev_d[s])
-        step.verify(ev_v[s])
+        step.draft(mode, flag, ev_d[s], fused=fused)
+        step.verify(ev_v[s], fused=fused)
         ev_s[s + 1].record()
     torch.cuda.synchronize()
     total_ms = ev_s[0].elapsed_time(ev_s[-1])
@@ -299,7 +319,8 @@ def graph_step(step, mode, flag, reps):
         step.draft(mode, flag)
         step.verify()
     torch.cuda.synchronize()
-    gr.replay()
+    for _ in range(5):          # settle under sustained load, as the eager warmup does
+        gr.replay()
     _hold()
     evs, outs = [], []
     for _ in range(reps):
@@ -320,13 +341,12 @@ def graph_step(step, mode, flag, reps):
 
 
 def window_step_fn(step, flag, n):
-    """One windowed draft step at length n (append at n - 1, attend, combine)."""
+    """One windowed draft step at length n (append at n - 1 and attend in one launch, combine)."""
     g0 = 0
 
     def run():
-        W.ring_append(step.sh, step.ring, step.k_draft[g0], step.v_draft[g0], [n - 1])
-        parts = W.draft_attn(W.SINK_WINDOW | flag, step.sh, step.q_draft[g0], [n], step.ws_win, ring=step.ring,
-                             chunk_tokens=step.chunk_win)
+        parts = W.draft_attn_append(W.SINK_WINDOW | flag, step.sh, step.q_draft[g0], step.k_draft[g0],
+                                    step.v_draft[g0], [n], step.ws_win, ring=step.ring, chunk_tokens=step.chunk_win)
         W.combine(parts, step.out_d, step.lse_d)
     return run
 
@@ -339,7 +359,8 @@ def window_measurements(step, flag, reps, dev, contexts):
     run()
     torch.cuda.synchronize()
     res = {"warm": pct(_timed(run, reps)), "cold_after_1GiB_write": pct(_timed(run, reps, lambda: flush.fill_(1)))}
-    res["launches"] = "ring append + draft attention + combine; host launches queued behind a spin or the flush"
+    res["launches"] = ("draft attention with the ring append inside + combine; host launches queued behind a "
+                       "spin or the flush")
     by_ctx = {}
     for n in contexts:
         # the ring of a sequence at length n: sinks at 0..S-1, the last W context tokens before n
@@ -531,7 +552,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    # ~35 ms of sustained load at 1M: after an idle spell the first launches run fast, then
+    # slow for a few ms, and settle after ~20 ms of load; the warmup absorbs that
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--context", type=int, default=1 << 20)
     ap.add_argument("--chunk-full", type=int, default=0, help="draft split size, native mode (0 = library default)")
     ap.add_argument("--chunk-window", type=int, default=0, help="draft split size, window mode (0 = default)")
@@ -587,6 +610,10 @@ def main():
     details = {"step_us": {"windowed": pct(win_steps), "native": pct(nat_steps)}}
     if not args.no_details:
         reps = 20
+        log("unfused steps (append calls before the attention calls)")
+        uw = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup, fused=False)
+        un = time_steps(step, W.FULL, flag, args.steps, args.warmup, fused=False)
+        details["unfused_step_us"] = {"windowed": pct(uw[3]), "native": pct(un[3])}
         log("graph-captured steps")
         gw, okw = graph_step(step, W.SINK_WINDOW, flag, 5)
         gn, okn = graph_step(step, W.FULL, flag, 5)

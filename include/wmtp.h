@@ -203,6 +203,37 @@ int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const 
                      const int32_t* seq_lens_host, int32_t batch, int32_t split_tokens,
                      void* workspace, size_t workspace_bytes, wmtp_partials* parts, void* stream);
 
+/* A draft step's append and attention in one launch (Windowed-MTP summary,
+ * Abstract, and readpriors.com post, What happened: each draft step adds one
+ * entry and then attends).  Equal, in the cache it leaves and in *parts, to
+ * wmtp_paged_append (WMTP_FULL, into `kv`) or wmtp_ring_append
+ * (WMTP_SINK_WINDOW, into `ring`, with its slot tag) of one token at position
+ * n_b - 1, followed by wmtp_draft_attn with the same arguments.
+ *  k_new, v_new: device [batch][1][H_kv][D], 16-byte aligned, caller-owned;
+ *  the work item whose keys include position n_b - 1 writes it before reading.
+ *  Every n_b must be >= 1.  Other arguments, workspace and errors as for
+ *  wmtp_draft_attn; NULL k_new or v_new gives WMTP_EINVAL.  Nothing is written
+ *  when the call returns an error. */
+int wmtp_draft_attn_append(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv,
+                           const wmtp_ring* ring, const void* k_new, const void* v_new,
+                           const int32_t* seq_lens_host, int32_t batch, int32_t chunk_tokens, void* workspace,
+                           size_t workspace_bytes, wmtp_partials* parts, void* stream);
+
+/* A target layer's append of the t_q query tokens' own K/V and its verify in
+ * one launch (Windowed-MTP summary, Abstract; howtospark case study, Method:
+ * the verify pass covers the drafted tokens).  Equal to wmtp_paged_append of
+ * t_q tokens at positions n_b - t_q .. n_b - 1 into `kv`, followed by
+ * wmtp_verify_attn with the same arguments.
+ *  k_new, v_new: device [batch][t_q][H_kv][D], 16-byte aligned, caller-owned;
+ *  each work item writes the new positions inside its own key range before
+ *  reading.  Other arguments, workspace and errors as for wmtp_verify_attn;
+ *  NULL k_new or v_new gives WMTP_EINVAL.  Nothing is written when the call
+ *  returns an error. */
+int wmtp_verify_attn_append(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv,
+                            const void* k_new, const void* v_new, const int32_t* seq_lens_host, int32_t batch,
+                            int32_t split_tokens, void* workspace, size_t workspace_bytes, wmtp_partials* parts,
+                            void* stream);
+
 /* Log-sum-exp merge of split partials (flash-decoding combine):
  *  L = log sum_i exp(lse_i),  out = sum_i exp(lse_i - L) * o_i  per row.
  *  Splits with lse = -inf carry no keys and are skipped; a row with no live

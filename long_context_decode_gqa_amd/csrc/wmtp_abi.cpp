@@ -219,9 +219,23 @@ int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const 
   return st ? st : p.bytes;
 }
 
-int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv, const wmtp_ring* ring,
-                    const int32_t* seq_lens_host, int32_t batch, int32_t chunk_tokens, void* workspace,
-                    size_t workspace_bytes, wmtp_partials* parts, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// New tokens a fused call appends: none (t_new = 0), or t_new per sequence.
+int check_new_tokens(const void* k_new, const void* v_new, int32_t t_new, const int32_t* seq_lens, int32_t batch) {
+  if (t_new == 0) return WMTP_OK;
+  if (!k_new || !v_new) return WMTP_EINVAL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return WMTP_EALIGN;
+  for (int b = 0; b < batch; ++b)
+    if (seq_lens[b] < t_new) return WMTP_EINVAL;
+  return WMTP_OK;
+}
+
+int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv, const wmtp_ring* ring,
+               const void* k_new, const void* v_new, int32_t t_new, const int32_t* seq_lens_host, int32_t batch,
+               int32_t chunk_tokens, void* workspace, size_t workspace_bytes, wmtp_partials* parts, void* stream) {
   const int base_mode = mode & 0xF;
   int32_t sink = 0, window = 1, headroom = 0;
   if (base_mode == WMTP_SINK_WINDOW) {
@@ -253,11 +267,16 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
   if (!workspace && p.bytes > 0) return WMTP_EINVAL;
   if (!aligned(workspace, 256)) return WMTP_EALIGN;
   if ((int64_t)workspace_bytes < p.bytes) return WMTP_EWORKSPACE;
+  st = check_new_tokens(k_new, v_new, t_new, seq_lens_host, batch);
+  if (st) return st;
 
   fill_parts(p, workspace, batch, shape->head_dim, parts);
   SplitArgs a;
   fill_split_args(a, shape, p, seq_lens_host, batch, chunk, parts);
   a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.t_new = t_new;
   if (base_mode == WMTP_FULL) {
     a.k = kv->k;
     a.v = kv->v;
@@ -292,9 +311,9 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
                                     static_cast<hipStream_t>(stream)));
 }
 
-int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv,
-                     const int32_t* seq_lens_host, int32_t batch, int32_t split_tokens, void* workspace,
-                     size_t workspace_bytes, wmtp_partials* parts, void* stream) {
+int verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv, const void* k_new,
+                const void* v_new, int32_t t_new, const int32_t* seq_lens_host, int32_t batch, int32_t split_tokens,
+                void* workspace, size_t workspace_bytes, wmtp_partials* parts, void* stream) {
   Plan p;
   int32_t split = 0;
   int st = verify_plan(shape, t_q, seq_lens_host, batch, split_tokens, &p, &split);
@@ -309,11 +328,16 @@ int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const 
   if (!workspace && p.bytes > 0) return WMTP_EINVAL;
   if (!aligned(workspace, 256)) return WMTP_EALIGN;
   if ((int64_t)workspace_bytes < p.bytes) return WMTP_EWORKSPACE;
+  st = check_new_tokens(k_new, v_new, t_new, seq_lens_host, batch);
+  if (st) return st;
 
   fill_parts(p, workspace, batch, shape->head_dim, parts);
   SplitArgs a;
   fill_split_args(a, shape, p, seq_lens_host, batch, split, parts);
   a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.t_new = t_new;
   a.k = kv->k;
   a.v = kv->v;
   a.block_table = kv->block_table;
@@ -323,6 +347,42 @@ int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const 
   const int grid = p.total * shape->num_kv_heads;
   return launch_status(launch_verify(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, false, a, grid,
                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv, const wmtp_ring* ring,
+                    const int32_t* seq_lens_host, int32_t batch, int32_t chunk_tokens, void* workspace,
+                    size_t workspace_bytes, wmtp_partials* parts, void* stream) {
+  return draft_attn(mode, shape, q, kv, ring, nullptr, nullptr, 0, seq_lens_host, batch, chunk_tokens, workspace,
+                    workspace_bytes, parts, stream);
+}
+
+int wmtp_draft_attn_append(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv,
+                           const wmtp_ring* ring, const void* k_new, const void* v_new, const int32_t* seq_lens_host,
+                           int32_t batch, int32_t chunk_tokens, void* workspace, size_t workspace_bytes,
+                           wmtp_partials* parts, void* stream) {
+  if (!k_new || !v_new) return WMTP_EINVAL;
+  return draft_attn(mode, shape, q, kv, ring, k_new, v_new, 1, seq_lens_host, batch, chunk_tokens, workspace,
+                    workspace_bytes, parts, stream);
+}
+
+int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv,
+                     const int32_t* seq_lens_host, int32_t batch, int32_t split_tokens, void* workspace,
+                     size_t workspace_bytes, wmtp_partials* parts, void* stream) {
+  return verify_attn(shape, q, t_q, kv, nullptr, nullptr, 0, seq_lens_host, batch, split_tokens, workspace,
+                     workspace_bytes, parts, stream);
+}
+
+int wmtp_verify_attn_append(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv,
+                            const void* k_new, const void* v_new, const int32_t* seq_lens_host, int32_t batch,
+                            int32_t split_tokens, void* workspace, size_t workspace_bytes, wmtp_partials* parts,
+                            void* stream) {
+  if (!k_new || !v_new) return WMTP_EINVAL;
+  return verify_attn(shape, q, t_q, kv, k_new, v_new, t_q, seq_lens_host, batch, split_tokens, workspace,
+                     workspace_bytes, parts, stream);
 }
 
 int wmtp_combine(const wmtp_partials* parts, void* out, int32_t out_dtype, float* lse_out, void* stream) {

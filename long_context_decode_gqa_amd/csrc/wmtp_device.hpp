@@ -87,6 +87,12 @@ struct SplitArgs {
   int32_t seq_len[WMTP_MAX_BATCH];
   int32_t seq_sink[WMTP_MAX_BATCH];      // ring: per-sequence sinks and window of the query
   int32_t seq_window[WMTP_MAX_BATCH];
+  // Fused append: the step's t_new new tokens per sequence (positions n - t_new
+  // .. n - 1), [batch][t_new][H_kv][D], written into k / v (and, for the ring,
+  // their slot tags into slot_pos) before they are read.  t_new = 0: none.
+  const void* k_new;
+  const void* v_new;
+  int32_t t_new;
 };
 
 // ----------------------------------------------------------------------------- resolvers
@@ -133,6 +139,47 @@ __device__ __forceinline__ int seq_of_split(const SplitArgs& a, int sg) {
   int b = 0;
   while (b + 1 < a.batch && a.split_base[b + 1] <= sg) ++b;
   return b;
+}
+
+// Fused append: write the step's new tokens at positions [lo, hi) of sequence
+// b, KV head h, into the cache (paged through the block table, or the ring
+// with the slot tag), then make them visible to the whole workgroup before
+// any of its loads.  Callers pass the positions that fall in the work item's
+// own key range, so each (position, head) row has one writer and no other
+// work item of the launch reads it; a ring tag is shared by the heads, and
+// each head's writer stores the same value before reading it.  lo >= hi (no
+// new token here) must hold for the whole workgroup or for none of it.
+template <bool RING>
+__device__ __forceinline__ void append_own_rows(const SplitArgs& a, int b, int h, int n, int lo, int hi,
+                                                int row_bytes) {
+  if (lo >= hi) return;
+  const int Hkv = a.num_kv_heads;
+  const int pieces = row_bytes / 16;
+  const int cnt = hi - lo;
+  const int first = n - a.t_new;                 // position of new token 0
+  uint8_t* const k = static_cast<uint8_t*>(const_cast<void*>(a.k));
+  uint8_t* const v = static_cast<uint8_t*>(const_cast<void*>(a.v));
+  const int cycle = a.slots - a.sink;
+  for (int j = threadIdx.x; j < 2 * cnt * pieces; j += blockDim.x) {
+    const int which = j / (cnt * pieces);        // 0 = K, 1 = V
+    const int r = j % (cnt * pieces);
+    const int p = lo + r / pieces, pc = r % pieces;
+    const int64_t src = (((int64_t)b * a.t_new + (p - first)) * Hkv + h) * row_bytes + pc * 16;
+    int64_t dst;
+    if constexpr (RING) {
+      dst = (((int64_t)b * Hkv + h) * a.slots + ring_slot(p, a.sink, cycle)) * row_bytes;
+    } else {
+      const int64_t blk = paged_block_of(a.block_table + (int64_t)b * a.bt_stride, p, a.max_block);
+      dst = paged_block_run(blk, h, Hkv, row_bytes) + (int64_t)(p % kBlock) * row_bytes;
+    }
+    const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(which ? a.v_new : a.k_new) + src);
+    *reinterpret_cast<u32x4*>((which ? v : k) + dst + pc * 16) = x;
+  }
+  if constexpr (RING) {
+    int32_t* tags = const_cast<int32_t*>(a.slot_pos) + (int64_t)b * a.slots;
+    for (int p = lo + (int)threadIdx.x; p < hi; p += blockDim.x) tags[ring_slot(p, a.sink, cycle)] = p;
+  }
+  __syncthreads();   // workgroup-scope release/acquire: the rows are visible to every wave's loads
 }
 
 // ----------------------------------------------------------------------------- numbers

@@ -106,6 +106,14 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
   const int t_begin = (sg - a.split_base[b]) * a.chunk;
   const int t_end = min(t_begin + a.chunk, nvis);
   const int ntiles = (t_end - t_begin + S::TILE - 1) / S::TILE;
+  if (a.t_new > 0) {
+    if constexpr (WINDOW) {
+      // one new token at n - 1: the last visible entry, in the sequence's last split
+      if (t_end == nvis) append_own_rows<true>(a, b, h, n, n - 1, n, ROWB);
+    } else {
+      append_own_rows<false>(a, b, h, n, max(t_begin, n - a.t_new), t_end, ROWB);
+    }
+  }
 
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + wave * QB;
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + wave * QB;

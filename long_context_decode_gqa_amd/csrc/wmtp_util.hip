@@ -41,22 +41,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int s0 = a.split_base[b], s1 = a.split_base[b + 1];
   const int d0 = slice * 4 * kCombineDL + dl * 4;
 
-  // Two passes over this thread's splits with independent loads: first the
-  // maximum lse, then the weighted sum.  Empty splits carry lse = -inf and
-  // o = 0, so they add exactly nothing.
+  // One pass over this thread's splits, merging each (lse, o) into a running
+  // (m, w, acc) in log2 units: the lse and o loads of all the thread's splits
+  // are independent, so they are in flight together.  An empty split carries
+  // lse = -inf and o = 0 and is skipped.
   MergeState st;
   st.m = kNegInf;
-#pragma unroll 8
-  for (int s = s0 + sl; s < s1; s += kCombineSL) st.m = fmaxf(st.m, a.part_lse[(int64_t)s * a.rows + r] * kLog2e);
   st.w = 0.f;
   st.acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (st.m != kNegInf) {
 #pragma unroll 4
-    for (int s = s0 + sl; s < s1; s += kCombineSL) {
-      const float e = exp2f(a.part_lse[(int64_t)s * a.rows + r] * kLog2e - st.m);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)s * a.rows + r) * a.head_dim + d0);
-      st.acc += e * x;
-      st.w += e;
+  for (int s = s0 + sl; s < s1; s += kCombineSL) {
+    const float l = a.part_lse[(int64_t)s * a.rows + r] * kLog2e;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)s * a.rows + r) * a.head_dim + d0);
+    if (l != kNegInf) {
+      const float mn = fmaxf(st.m, l);
+      const float fa = exp2f(st.m - mn), fb = exp2f(l - mn);   // st.m = -inf gives fa = 0
+      st.acc = st.acc * fa + fb * x;
+      st.w = st.w * fa + fb;
+      st.m = mn;
     }
   }
   // merge tree over the split lanes of this wave (lane = kCombineDL sl + dl):

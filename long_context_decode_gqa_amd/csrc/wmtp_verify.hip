@@ -84,6 +84,7 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
   const int t_end = min(t_begin + a.chunk, n);
   const int ntiles = (t_end - t_begin + kVTile - 1) / kVTile;
   const int last_blk_idx = (t_end - 1) >> 4;
+  if (a.t_new > 0) append_own_rows<false>(a, b, h, n, max(t_begin, n - a.t_new), t_end, kVD * 2);
   const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + wave * (kVQ * 2);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + wave * (kVQ * 2);
@@ -401,6 +402,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
   const int t_end = min(t_begin + a.chunk, n);
   const int ntiles = (t_end - t_begin + kVTile - 1) / kVTile;
   const int last_blk_idx = (t_end - 1) >> 4;
+  if (a.t_new > 0) append_own_rows<false>(a, b, h, n, max(t_begin, n - a.t_new), t_end, kVD * 2);
   const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + wave * (kVQ * 2);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + wave * (kVQ * 2);

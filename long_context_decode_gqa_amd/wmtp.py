@@ -69,7 +69,7 @@ class Partials(ctypes.Structure):
 
 EXPORTS = (
     "wmtp_draft_workspace_bytes", "wmtp_verify_workspace_bytes", "wmtp_draft_attn", "wmtp_verify_attn",
-    "wmtp_combine", "wmtp_ring_append", "wmtp_ring_rollback", "wmtp_paged_append", "wmtp_debug_resolve_paged",
+    "wmtp_draft_attn_append", "wmtp_verify_attn_append", "wmtp_combine", "wmtp_ring_append", "wmtp_ring_rollback", "wmtp_paged_append", "wmtp_debug_resolve_paged",
     "wmtp_debug_resolve_ring", "wmtp_debug_window_positions", "wmtp_plan_memory", "wmtp_stream_read",
     "wmtp_stream_read_paged", "wmtp_status_str",
     "wmtp_version",
@@ -97,6 +97,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.wmtp_draft_attn.restype = ctypes.c_int
     lib.wmtp_verify_attn.argtypes = [sp, P, I32, pp, P, I32, I32, P, SZ, tp, P]
     lib.wmtp_verify_attn.restype = ctypes.c_int
+    lib.wmtp_draft_attn_append.argtypes = [I32, sp, P, pp, rp, P, P, P, I32, I32, P, SZ, tp, P]
+    lib.wmtp_draft_attn_append.restype = ctypes.c_int
+    lib.wmtp_verify_attn_append.argtypes = [sp, P, I32, pp, P, P, P, I32, I32, P, SZ, tp, P]
+    lib.wmtp_verify_attn_append.restype = ctypes.c_int
     lib.wmtp_combine.argtypes = [tp, P, I32, P, P]
     lib.wmtp_combine.restype = ctypes.c_int
     lib.wmtp_ring_append.argtypes = [sp, rp, P, P, P, I32, I32, P]
@@ -220,6 +224,42 @@ def verify_attn(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, seq_lens:
         ctypes.byref(shape), q.data_ptr(), t_q, ctypes.byref(paged), ctypes.cast(_lens(seq_lens), ctypes.c_void_p),
         len(seq_lens), split_tokens, ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(parts),
         _stream(stream)))
+    return parts
+
+
+def _new_tokens(shape: Shape, k_new: torch.Tensor, v_new: torch.Tensor, batch: int, t_new: int) -> None:
+    """The fused calls read [batch][t_new][H_kv][D] from k_new and v_new: check that much is there."""
+    want = batch * t_new * shape.num_kv_heads * shape.head_dim
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        if x.numel() != want or dtype_code(x.dtype) != shape.dtype or not x.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous [{batch}][{t_new}][{shape.num_kv_heads}]"
+                             f"[{shape.head_dim}] tensor of the cache dtype, got {tuple(x.shape)} {x.dtype}")
+
+
+def draft_attn_append(mode: int, shape: Shape, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      seq_lens: Sequence[int], ws: torch.Tensor, paged: Optional[Paged] = None,
+                      ring: Optional[Ring] = None, chunk_tokens: int = 0, stream=None) -> Partials:
+    """Append one token per sequence at position seq_lens[b] - 1 (paged or ring) and attend, in one launch."""
+    _new_tokens(shape, k_new, v_new, len(seq_lens), 1)
+    parts = Partials()
+    _check("wmtp_draft_attn_append", load().wmtp_draft_attn_append(
+        mode, ctypes.byref(shape), q.data_ptr(), ctypes.byref(paged) if paged is not None else None,
+        ctypes.byref(ring) if ring is not None else None, k_new.data_ptr(), v_new.data_ptr(),
+        ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), chunk_tokens, ws.data_ptr(),
+        ws.numel() * ws.element_size(), ctypes.byref(parts), _stream(stream)))
+    return parts
+
+
+def verify_attn_append(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, k_new: torch.Tensor,
+                       v_new: torch.Tensor, seq_lens: Sequence[int], ws: torch.Tensor, split_tokens: int = 0,
+                       stream=None) -> Partials:
+    """Append the t_q query tokens' K/V at positions seq_lens[b] - t_q .. seq_lens[b] - 1 and verify, in one launch."""
+    _new_tokens(shape, k_new, v_new, len(seq_lens), t_q)
+    parts = Partials()
+    _check("wmtp_verify_attn_append", load().wmtp_verify_attn_append(
+        ctypes.byref(shape), q.data_ptr(), t_q, ctypes.byref(paged), k_new.data_ptr(), v_new.data_ptr(),
+        ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), split_tokens, ws.data_ptr(),
+        ws.numel() * ws.element_size(), ctypes.byref(parts), _stream(stream)))
     return parts
 
 

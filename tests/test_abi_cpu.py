@@ -262,6 +262,47 @@ def test_append_checks():
     assert lib.wmtp_paged_append(ctypes.byref(sh), None, FAKE, FAKE, lens(0), 1, 1, None) == W.EINVAL
 
 
+def test_fused_append_checks():
+    lib = W.load()
+    sh = shape()
+    kv = paged()
+    r = ring()
+    p = W.Partials()
+
+    def draft(mode=W.FULL, k_new=FAKE, v_new=FAKE, seq=(1000,), rg=r, wsb=1 << 30):
+        return lib.wmtp_draft_attn_append(mode, ctypes.byref(sh), FAKE, ctypes.byref(kv),
+                                          ctypes.byref(rg) if rg is not None else None, k_new, v_new, lens(*seq),
+                                          len(seq), 0, FAKE, wsb, ctypes.byref(p), None)
+
+    def verify(t_q=4, k_new=FAKE, v_new=FAKE, seq=(1000,)):
+        return lib.wmtp_verify_attn_append(ctypes.byref(sh), FAKE, t_q, ctypes.byref(kv), k_new, v_new, lens(*seq),
+                                           len(seq), 0, FAKE, 1 << 30, ctypes.byref(p), None)
+
+    for mode in (W.FULL, W.SINK_WINDOW):
+        assert draft(mode, k_new=None) == W.EINVAL
+        assert draft(mode, v_new=None) == W.EINVAL
+        assert draft(mode, k_new=FAKE_ODD) == W.EALIGN
+        assert draft(mode, v_new=FAKE_ODD) == W.EALIGN
+        assert draft(mode, seq=(5, 0)) == W.EINVAL          # the new token needs a position: n >= 1
+        assert draft(mode, wsb=16) == W.EWORKSPACE
+    assert draft(W.SINK_WINDOW, rg=None) == W.EINVAL
+    assert verify(k_new=None) == W.EINVAL
+    assert verify(v_new=FAKE_ODD) == W.EALIGN
+    assert verify(seq=(3,)) == W.EINVAL                      # fewer keys than new tokens
+    assert verify(t_q=13) == W.EUNSUPPORTED
+    # the binding checks that k_new / v_new hold [batch][t_new][H_kv][D] of the cache dtype
+    pyshape = W.make_shape(16, 2, 256, torch.bfloat16)
+    q = torch.zeros((1, 16, 256), dtype=torch.bfloat16)
+    ws = torch.zeros(256, dtype=torch.uint8)
+    good = torch.zeros((1, 1, 2, 256), dtype=torch.bfloat16)
+    for bad in (torch.zeros((1, 2, 2, 256), dtype=torch.bfloat16), torch.zeros((1, 1, 2, 256)),
+                torch.zeros((1, 1, 2, 512), dtype=torch.bfloat16)[..., ::2]):
+        with pytest.raises(ValueError):
+            W.draft_attn_append(W.FULL, pyshape, q, bad, good, [10], ws, paged=kv)
+        with pytest.raises(ValueError):
+            W.verify_attn_append(pyshape, q, 3, kv, bad, bad, [10], ws)
+
+
 def test_per_sequence_policy_checks():
     """Per-sequence sinks <= S and windows in [1, W + R] (window mode only)."""
     lib = W.load()

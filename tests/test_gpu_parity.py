@@ -264,8 +264,13 @@ def test_per_sequence_sinks_and_windows_parity(fast_pv):
 
 
 # ============================================================== draft attention
-def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtype=torch.float32):
-    """Run gamma draft steps on the GPU and the oracle; return the worst max-abs errors (o, lse)."""
+def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtype=torch.float32, fused=False,
+                headroom=0, record=None):
+    """Run gamma draft steps on the GPU and the oracle; return the worst max-abs errors (o, lse).
+
+    fused: append and attend in one call (wmtp_draft_attn_append) instead of an
+    append call followed by wmtp_draft_attn.  record: a list that receives each
+    step's (out, lse) and, last, the cache tensors the steps leave."""
     case = synth.draft_case(wl, contexts)
     B, Hq, Hk, D = len(case.n0), wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     dt = wl.dtype
@@ -278,11 +283,12 @@ def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtyp
     if mode == O.FULL:
         cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=steps, seed=wl.seed, permuted=wl.permuted)
     else:
-        ring = RingCache(B, Hk, D, wl.sink, wl.window, TDT[dt])
+        ring = RingCache(B, Hk, D, wl.sink, wl.window, TDT[dt], headroom)
         for b in range(B):                   # bulk-fill each sequence's ring with its context
             if case.n0[b] == 0:
                 continue
-            sub = W.Ring(ring.k[b].data_ptr(), ring.v[b].data_ptr(), ring.tags[b].data_ptr(), wl.sink, wl.window)
+            sub = W.Ring(ring.k[b].data_ptr(), ring.v[b].data_ptr(), ring.tags[b].data_ptr(), wl.sink, wl.window,
+                         headroom)
             W.ring_append(sh, sub, case.k_ctx[b:b + 1, :case.n0[b]].contiguous().to(DEV),
                           case.v_ctx[b:b + 1, :case.n0[b]].contiguous().to(DEV), [0])
     flag = W.DRAFT_FAST_PV if fast_pv else 0
@@ -292,19 +298,28 @@ def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtyp
         vn = case.v_new[j].contiguous().to(DEV)
         pos = [n + j for n in case.n0]
         lens = [n + j + 1 for n in case.n0]
+        qj = case.q[j].contiguous().to(DEV)
         if mode == O.FULL:
-            W.paged_append(sh, cache.desc, kn, vn, pos)
             nbytes = W.draft_workspace_bytes(mode | flag, sh, lens, chunk)
             ws = W.workspace(nbytes, DEV)
-            parts = W.draft_attn(mode | flag, sh, case.q[j].contiguous().to(DEV), lens, ws, paged=cache.desc,
-                                 chunk_tokens=chunk)
+            if fused:
+                parts = W.draft_attn_append(mode | flag, sh, qj, kn, vn, lens, ws, paged=cache.desc,
+                                            chunk_tokens=chunk)
+            else:
+                W.paged_append(sh, cache.desc, kn, vn, pos)
+                parts = W.draft_attn(mode | flag, sh, qj, lens, ws, paged=cache.desc, chunk_tokens=chunk)
         else:
-            W.ring_append(sh, ring.desc, kn, vn, pos)
-            nbytes = W.draft_workspace_bytes(mode | flag, sh, lens, chunk, wl.sink, wl.window)
+            nbytes = W.draft_workspace_bytes(mode | flag, sh, lens, chunk, wl.sink, wl.window, headroom)
             ws = W.workspace(nbytes, DEV)
-            parts = W.draft_attn(mode | flag, sh, case.q[j].contiguous().to(DEV), lens, ws, ring=ring.desc,
-                                 chunk_tokens=chunk)
+            if fused:
+                parts = W.draft_attn_append(mode | flag, sh, qj, kn, vn, lens, ws, ring=ring.desc,
+                                            chunk_tokens=chunk)
+            else:
+                W.ring_append(sh, ring.desc, kn, vn, pos)
+                parts = W.draft_attn(mode | flag, sh, qj, lens, ws, ring=ring.desc, chunk_tokens=chunk)
         out, lse = run_combine(parts, Hq, D, B, out_dtype)
+        if record is not None:
+            record.append((out, lse))
         torch.cuda.synchronize()
         qf = O.to_f64(host_array(case.q[j], dt), dt)
         for b in range(B):
@@ -313,6 +328,8 @@ def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtyp
             o_ref, l_ref = O.draft_attention(qf[b], src_k, src_v, lens[b], mode, wl.sink, wl.window, wl.scale)
             worst_o = max(worst_o, max_err(out[b], o_ref))
             worst_l = max(worst_l, max_err(lse[b], l_ref))
+    if record is not None:
+        record.append((cache.k, cache.v) if mode == O.FULL else (ring.k, ring.v, ring.tags))
     return worst_o, worst_l
 
 
@@ -367,17 +384,25 @@ def test_window_covering_context_equals_full_on_gpu():
 
 
 # ============================================================== verify attention
-def verify_run(wl, contexts, t_q, split=0, layer=0):
+def verify_run(wl, contexts, t_q, split=0, layer=0, fused=False, record=None):
+    """Verify on the GPU (append + verify, or the fused call) against the oracle: worst (o, lse) errors.
+    record: a list that receives (out, lse, k pool, v pool)."""
     case = synth.verify_case(wl, contexts, t_q, layer=layer)
     B, Hq, Hk, D = len(case.n0), wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     dt = wl.dtype
     sh = W.make_shape(Hq, Hk, D, TDT[dt], wl.scale)
     cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=t_q, seed=wl.seed + 100 + layer)
-    W.paged_append(sh, cache.desc, case.k_new.to(DEV), case.v_new.to(DEV), list(case.n0))
+    kn, vn = case.k_new.contiguous().to(DEV), case.v_new.contiguous().to(DEV)
     lens = [n + t_q for n in case.n0]
     ws = W.workspace(W.verify_workspace_bytes(sh, t_q, lens, split), DEV)
-    parts = W.verify_attn(sh, case.q.to(DEV), t_q, cache.desc, lens, ws, split)
+    if fused:
+        parts = W.verify_attn_append(sh, case.q.to(DEV), t_q, cache.desc, kn, vn, lens, ws, split)
+    else:
+        W.paged_append(sh, cache.desc, kn, vn, list(case.n0))
+        parts = W.verify_attn(sh, case.q.to(DEV), t_q, cache.desc, lens, ws, split)
     out, lse = run_combine(parts, t_q * Hq, D, B)
+    if record is not None:
+        record.append((out, lse, cache.k, cache.v))
     torch.cuda.synchronize()
     qf = O.to_f64(host_array(case.q, dt), dt)
     ck, cv = host_array(case.k_ctx, dt), host_array(case.v_ctx, dt)
@@ -415,6 +440,70 @@ def test_verify_mixed_batch():
     say("verify mixed")
     eo, el = verify_run(wl, (100, 3000, 17, 6000), 4, 256)
     assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
+# ============================================================== fused append + attention
+# One launch that appends the step's new tokens and attends must leave the
+# same cache and produce the same partials, bit for bit, as the append call
+# followed by the attention call; and it must match the oracle.  The cases put
+# the new tokens across a split boundary, at position 0, in a sink slot, in a
+# ring that has wrapped (with headroom), and on every kernel that serves them.
+@pytest.mark.parametrize("contexts,t_q,split,hq,hk", [
+    ((62, 99), 4, 64, 16, 2),       # 62..65 straddle the split at 64
+    ((0, 1234), 4, 32, 16, 2),      # first tokens of an empty sequence
+    ((29, 300), 6, 32, 16, 2),      # two row tiles (two wave teams), straddling 32
+    ((2044, 17), 9, 256, 16, 2),    # three row tiles, straddling 2048
+    ((1000, 4000), 4, 0, 16, 2),    # library default split
+    ((33, 500), 4, 32, 8, 1),       # G = 8 on one KV head
+])
+def test_verify_fused_append_equals_separate_calls(contexts, t_q, split, hq, hk):
+    wl = synth.workload("step_1m_bf16", num_q_heads=hq, num_kv_heads=hk)
+    say("verify fused append", contexts, t_q, split, hq, hk)
+    fused, sep = [], []
+    eo, el = verify_run(wl, contexts, t_q, split, fused=True, record=fused)
+    verify_run(wl, contexts, t_q, split, fused=False, record=sep)
+    for a, b in zip(fused[0], sep[0]):
+        assert torch.equal(a, b)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+@pytest.mark.parametrize("fast_pv", [False, True])
+@pytest.mark.parametrize("contexts,chunk,window,headroom", [
+    ((63, 0, 2000), 64, 1024, 0),       # step tokens at 63..65 cross the split at 64; an empty sequence
+    ((1, 5000), 128, 1024, 2),          # a sink slot; a wrapped ring with headroom
+    ((700, 4096), 0, 256, 3),           # library default split
+])
+def test_draft_fused_append_equals_separate_calls(mode, fast_pv, contexts, chunk, window, headroom):
+    wl = synth.workload("draft_131k_bf16", window=window)
+    say("draft fused append", mode, fast_pv, contexts, chunk, window, headroom)
+    fused, sep = [], []
+    eo, el = draft_steps(wl, contexts, mode, chunk=chunk, fast_pv=fast_pv, fused=True, headroom=headroom,
+                         record=fused)
+    draft_steps(wl, contexts, mode, chunk=chunk, fast_pv=fast_pv, fused=False, headroom=headroom, record=sep)
+    assert len(fused) == len(sep) == wl.gamma + 1
+    for got, want in zip(fused, sep):
+        for a, b in zip(got, want):
+            assert torch.equal(a, b)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+def test_draft_fused_append_fp32_and_other_shapes(mode):
+    cases = [(synth.workload("tiny_fp32_4k"), None, TOL["f32"]),
+             (synth.workload("draft_131k_bf16", num_q_heads=4, num_kv_heads=2, head_dim=128, window=300), (1500,),
+              TOL["bf16"]),
+             (synth.workload("draft_131k_bf16", num_q_heads=8, num_kv_heads=8, head_dim=64, window=300), (777,),
+              TOL["bf16"])]
+    for wl, contexts, tol in cases:
+        say("draft fused append shapes", mode, wl.num_q_heads, wl.num_kv_heads, wl.head_dim)
+        fused, sep = [], []
+        eo, el = draft_steps(wl, contexts, mode, chunk=192 if contexts else 0, fused=True, record=fused)
+        draft_steps(wl, contexts, mode, chunk=192 if contexts else 0, fused=False, record=sep)
+        for got, want in zip(fused, sep):
+            for a, b in zip(got, want):
+                assert torch.equal(a, b)
+        assert eo <= tol and el <= tol, (eo, el)
 
 
 # ============================================================== 1M-token cases (sampled)
