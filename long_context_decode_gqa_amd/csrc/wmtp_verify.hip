@@ -370,24 +370,34 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
   }
 }
 
-// Two row tiles (33..64 packed rows) on two teams of 4 waves, 512 threads.
-// With both row tiles in one wave the per-tile chain of LDS stages, barriers,
-// MFMA and softmax has nothing to hide behind at one wave per SIMD; here team 0
-// loads K and V exactly as the one-row-tile kernel, stages both in LDS and
-// computes row tile 0 of tile t, while team 1 computes row tile 1 of tile t - 1
-// from those stages: every SIMD runs one wave of each team, and HBM is read
-// once.  One barrier per tile step: the K/V stages rotate over three buffers
-// and each team's score exchange over two, and since neither team can pass a
-// step's barrier before the other reaches it, team 0 rewrites a stage only
-// after team 1 has finished with it (160 KiB of LDS, the per-workgroup limit).
-template <int G>
+// Two or three row tiles (33..96 packed rows) on two teams of 4 waves, 512
+// threads.  With all row tiles in one wave the per-tile chain of LDS stages,
+// barriers, MFMA and softmax has nothing to hide behind at one wave per SIMD;
+// here team 0 loads K and V exactly as the one-row-tile kernel, stages both in
+// LDS and computes row tile 0 of tile t, while team 1 computes the other R1
+// row tiles (1, or 2 and 3) of tile t - 1 from those stages: every SIMD runs
+// one wave of each team, and HBM is read once.
+//   R1 = 1: one barrier per tile step.  The K/V stages rotate over three
+//   buffers and each team's score exchange over two; neither team can pass a
+//   step's barrier before the other reaches it, so team 0 rewrites a stage only
+//   after team 1 has passed the barrier that follows its last read of it
+//   (160 KiB of LDS, the per-workgroup limit).
+//   R1 = 2: team 1's exchange is twice as large, so the stages use two buffers
+//   and the exchanges one, with a second barrier per tile step after the
+//   softmax and PV (112 KiB of LDS).
+template <int G, int R1>
 __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs a) {
+  static_assert(R1 == 1 || R1 == 2, "team 1 computes one or two row tiles");
   constexpr int ROWB = kVD * 2;
   constexpr float TAU = 8.0f;
+  constexpr int NB = R1 == 1 ? 3 : 2;          // K/V stage buffers
+  constexpr int NP = R1 == 1 ? 2 : 1;          // score-exchange buffers per team
+  constexpr int kExch = 4 * 4 * 64 * 4;        // floats of one row tile's exchange
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_stage[3][4 * kVStage];    // [tile % 3][wave quarter]
-  __shared__ __attribute__((aligned(16))) u32x4 v_stage[3][4][4][64];         // [tile % 3][wave][piece][lane]
-  __shared__ __attribute__((aligned(16))) float sc_lds[2][2][4 * 4 * 64 * 4]; // [team][tile & 1][(wave*4+q)*64+lane][4]
+  __shared__ __attribute__((aligned(16))) uint8_t k_stage[NB][4 * kVStage];   // [tile % NB][wave quarter]
+  __shared__ __attribute__((aligned(16))) u32x4 v_stage[NB][4][4][64];        // [tile % NB][wave][piece][lane]
+  __shared__ __attribute__((aligned(16))) float sc0_lds[NP][kExch];           // team 0: [tile % NP]
+  __shared__ __attribute__((aligned(16))) float sc1_lds[NP][R1 * kExch];      // team 1: [tile % NP][row tile]
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -409,44 +419,48 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
 
   const int c32 = lane & 31;
   const int kh = lane >> 5;
-  const int row0 = 32 * team;    // this team's first packed row
+  const float c = a.scale_log2;
+  const int all_last = min(n - tq, t_end - 1);
 
-  u32x4 qreg[kVKS];
-  {
+  // One row tile's queries (this wave's quarter of D), softmax state and accumulators.
+  struct RowTile {
+    u32x4 q[kVKS];
+    f32x16 O[2];
+    float M, l;
+    int row0, row_last;
+  };
+  auto init_tile = [&](RowTile& rt, int r) {
+    rt.row0 = 32 * r;
     const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
-    const int j = row0 + c32;
+    const int j = rt.row0 + c32;
     const int i = j / G, g = j % G;
     const int64_t qrow = ((int64_t)b * tq + i) * Hq + (int64_t)h * G + g;
 #pragma unroll
     for (int s = 0; s < kVKS; ++s) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (j < rows) x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + wave * (kVQ * 2) + (2 * s + kh) * 16);
-      qreg[s] = x;
+      rt.q[s] = x;
     }
 #pragma unroll
-    for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(qreg[s]));
-  }
-
-  const float c = a.scale_log2;
-  const int row_last = min(n - tq + (row0 + c32) / G, t_end - 1);
-  const int all_last = min(n - tq, t_end - 1);
-
-  f32x16 O[2];
+    for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(rt.q[s]));
+    rt.row_last = min(n - tq + j / G, t_end - 1);
 #pragma unroll
-  for (int e = 0; e < 2; ++e)
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) O[e][x] = 0.f;
-  float M = kNegInf, l_lane = 0.f;
+      for (int x = 0; x < 16; ++x) rt.O[e][x] = 0.f;
+    rt.M = kNegInf;
+    rt.l = 0.f;
+  };
 
-  // partial S^T of this wave's quarter of D for the team's row tile, into the team's exchange
-  auto qk_exchange = [&](const uint8_t* kst, float* sc) {
+  // partial S^T of this wave's quarter of D for one row tile, into an exchange buffer
+  auto qk_exchange = [&](const uint8_t* kst, const RowTile& rt, float* sc) {
     f32x16 sacc;
 #pragma unroll
     for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
 #pragma unroll
     for (int s = 0; s < kVKS; ++s) {
       const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + vpiece(c32, 2 * s + kh) * 16);
-      sacc = mfma32(ka, qreg[s], sacc);
+      sacc = mfma32(ka, rt.q[s], sacc);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -465,38 +479,38 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
     }
   };
   // mask, lazy maximum, bf16 weights and O += P V for the tile starting at key t0
-  auto softmax_pv = [&](int t0, float (&s2)[16], const uint32_t (&vv)[2][8]) {
+  auto softmax_pv = [&](int t0, float (&s2)[16], const uint32_t (&vv)[2][8], RowTile& rt) {
     if (t0 + kVTile - 1 > all_last) {
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int key = t0 + 8 * (x >> 2) + 4 * kh + (x & 3);
-        s2[x] = key <= row_last ? s2[x] : kNegInf;
+        s2[x] = key <= rt.row_last ? s2[x] : kNegInf;
       }
     }
     float mx = s2[0];
 #pragma unroll
     for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s2[x]);
     mx = halves_max(mx) * c;
-    if (__ballot(mx > M + TAU) != 0) {
-      const float mn = fmaxf(M, mx);
-      const float alpha = (M == kNegInf) ? 0.f : fast_exp2(M - mn);
-      M = mn;
-      l_lane *= alpha;
+    if (__ballot(mx > rt.M + TAU) != 0) {
+      const float mn = fmaxf(rt.M, mx);
+      const float alpha = (rt.M == kNegInf) ? 0.f : fast_exp2(rt.M - mn);
+      rt.M = mn;
+      rt.l *= alpha;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const float ar = __shfl(alpha, 8 * (x >> 2) + 4 * kh + (x & 3));
-        O[0][x] *= ar;
-        O[1][x] *= ar;
+        rt.O[0][x] *= ar;
+        rt.O[1][x] *= ar;
       }
     }
-    const float negM = M == kNegInf ? 0.f : -M;
+    const float negM = rt.M == kNegInf ? 0.f : -rt.M;
     uint32_t pk[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const float p0 = fast_exp2(fmaf(s2[2 * q], c, negM));
       const float p1 = fast_exp2(fmaf(s2[2 * q + 1], c, negM));
       pk[q] = pack_bf16x2(p0, p1);
-      l_lane = dot2_bf16(pk[q], kBf16One2, l_lane);
+      rt.l = dot2_bf16(pk[q], kBf16One2, rt.l);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -507,13 +521,40 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           vb[q] = __builtin_amdgcn_perm(vv[ks][2 * q + 1], vv[ks][2 * q], e ? 0x07060302u : 0x05040100u);
-        O[e] = mfma32(pa, vb, O[e]);
+        rt.O[e] = mfma32(pa, vb, rt.O[e]);
       }
+    }
+  };
+  // normalise and write this wave's quarter of the row tile's live rows
+  auto finish = [&](const RowTile& rt) {
+    const float l_row = halves_sum(rt.l);
+    const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int rl = 8 * (x >> 2) + 4 * kh + (x & 3);
+      const float inv = __shfl(inv_row, rl);
+      const int row = rt.row0 + rl;
+      if (row < rows) {
+        const int i = row / G, g = row % G;
+        const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
+        float2 w2;
+        w2.x = rt.O[0][x] * inv;
+        w2.y = rt.O[1][x] * inv;
+        *reinterpret_cast<float2*>(a.part_o + orow * kVD + wave * kVQ + 2 * c32) = w2;
+      }
+    }
+    if (wave == 0 && lane < 32 && rt.row0 + lane < rows) {
+      const int row = rt.row0 + lane;
+      const int i = row / G, g = row % G;
+      const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
+      a.part_lse[orow] = l_row > 0.f ? (rt.M + __log2f(l_row)) * kLn2 : kNegInf;
     }
   };
 
   if (team == 0) {
     // ---- loader team: the one-row-tile kernel's loads and ring, plus the stages for team 1
+    RowTile rt0;
+    init_tile(rt0, 0);
     auto tile_runs = [&](int it, int64_t (&run)[2]) {
       const int t0 = t_begin + min(it, ntiles - 1) * kVTile;
 #pragma unroll
@@ -546,7 +587,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       const int t0 = t_begin + it * kVTile;
       issue((slot + kRing - 1) % kRing, run_next, k_off, v_off);
       __builtin_amdgcn_sched_barrier(0);
-      uint8_t* kst = k_stage[it % 3] + wave * kVStage;
+      uint8_t* kst = k_stage[it % NB] + wave * kVStage;
 #pragma unroll
       for (int l = 0; l < kVLoads; ++l) {
         const int P = 64 * l + lane;
@@ -556,17 +597,18 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       for (int q = 0; q < 4; ++q) {
         const u32x4 w = {vreg[slot][q >> 1][4 * (q & 1)], vreg[slot][q >> 1][4 * (q & 1) + 1],
                          vreg[slot][q >> 1][4 * (q & 1) + 2], vreg[slot][q >> 1][4 * (q & 1) + 3]};
-        v_stage[it % 3][wave][q][lane] = w;
+        v_stage[it % NB][wave][q][lane] = w;
       }
-      float* sc = sc_lds[0][it & 1];
-      qk_exchange(kst, sc);
+      float* sc = sc0_lds[it % NP];
+      qk_exchange(kst, rt0, sc);
       __syncthreads();
       float s2[16];
       read_scores(sc, s2);
       __builtin_amdgcn_sched_barrier(0);
       tile_runs(it + kRing, run_next);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_pv(t0, s2, vreg[slot]);
+      softmax_pv(t0, s2, vreg[slot], rt0);
+      if constexpr (R1 == 2) __syncthreads();
     };
     if (ntiles > 0) {
 #pragma unroll
@@ -586,52 +628,42 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       if (it < ntiles) body(it, 0);
       if (it + 1 < ntiles) body(it + 1, 1);
     }
-    // team 1 still computes the last tile: its barrier
+    // team 1 still computes the last tile: its barrier(s)
     __syncthreads();
+    if constexpr (R1 == 2) __syncthreads();
+    finish(rt0);
   } else {
-    // ---- team 1: row tile 1 of tile it - 1, from team 0's stages
+    // ---- team 1: row tiles 1..R1 of tile it - 1, from team 0's stages
+    RowTile rt1[R1];
+#pragma unroll
+    for (int r = 0; r < R1; ++r) init_tile(rt1[r], 1 + r);
     for (int it = 0; it <= ntiles; ++it) {
       const int t = it - 1;
-      float* sc = sc_lds[1][it & 1];
-      if (t >= 0) qk_exchange(k_stage[t % 3] + wave * kVStage, sc);
+      float* sc = sc1_lds[it % NP];
+      if (t >= 0) {
+#pragma unroll
+        for (int r = 0; r < R1; ++r) qk_exchange(k_stage[t % NB] + wave * kVStage, rt1[r], sc + r * kExch);
+      }
       __syncthreads();
       if (t >= 0) {
-        float s2[16];
-        read_scores(sc, s2);
         uint32_t vv[2][8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const u32x4 w = v_stage[t % 3][wave][q][lane];
+          const u32x4 w = v_stage[t % NB][wave][q][lane];
 #pragma unroll
           for (int e = 0; e < 4; ++e) vv[q >> 1][4 * (q & 1) + e] = w[e];
         }
-        softmax_pv(t_begin + t * kVTile, s2, vv);
-      }
-    }
-  }
-
-  // ---- normalise and write this wave's quarter of the team's live rows
-  const float l_row = halves_sum(l_lane);
-  const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
-  for (int x = 0; x < 16; ++x) {
-    const int rl = 8 * (x >> 2) + 4 * kh + (x & 3);
-    const float inv = __shfl(inv_row, rl);
-    const int row = row0 + rl;
-    if (row < rows) {
-      const int i = row / G, g = row % G;
-      const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
-      float2 w2;
-      w2.x = O[0][x] * inv;
-      w2.y = O[1][x] * inv;
-      *reinterpret_cast<float2*>(a.part_o + orow * kVD + wave * kVQ + 2 * c32) = w2;
+        for (int r = 0; r < R1; ++r) {
+          float s2[16];
+          read_scores(sc + r * kExch, s2);
+          softmax_pv(t_begin + t * kVTile, s2, vv, rt1[r]);
+        }
+      }
+      if constexpr (R1 == 2) __syncthreads();
     }
-  }
-  if (wave == 0 && lane < 32 && row0 + lane < rows) {
-    const int row = row0 + lane;
-    const int i = row / G, g = row % G;
-    const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
-    a.part_lse[orow] = l_row > 0.f ? (M + __log2f(l_row)) * kLn2 : kNegInf;
+#pragma unroll
+    for (int r = 0; r < R1; ++r) finish(rt1[r]);
   }
 }
 
@@ -642,8 +674,8 @@ static hipError_t launch_rt(int rt, bool single, const SplitArgs& a, int grid, h
   } else {
     switch (rt) {
       case 1: mfma_attn_kernel<G, 1, false><<<grid, 256, 0, st>>>(a); break;
-      case 2: mfma_attn_teams_kernel<G><<<grid, 512, 0, st>>>(a); break;
-      case 3: mfma_attn_kernel<G, 3, false><<<grid, 256, 0, st>>>(a); break;
+      case 2: mfma_attn_teams_kernel<G, 1><<<grid, 512, 0, st>>>(a); break;
+      case 3: mfma_attn_teams_kernel<G, 2><<<grid, 512, 0, st>>>(a); break;
       default: return hipErrorInvalidValue;
     }
   }
