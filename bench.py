@@ -671,7 +671,7 @@ def main():
             "draft_native_per_step": round(dnat_ms * 1e3, 2),
         },
         "roofline": {
-            "kernel": "mfma_attn_kernel<8, 1, false> (verify, 10 launches per step)",
+            "kernel": "mfma_attn_kernel<8, false> (verify, 10 launches per step)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

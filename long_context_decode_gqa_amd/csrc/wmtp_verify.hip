@@ -59,18 +59,16 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 
 }  // namespace
 
-// RT: tiles of 32 packed rows (t_q x G <= 32 RT); the K tile in LDS and the V
-// operand are shared by all row tiles.  SINGLE: one query token (t_q = 1, the
-// native full-context draft step); otherwise t_q comes from the arguments.
-// One row tile fits two workgroups per CU; more row tiles need one.
-template <int G, int RT, bool SINGLE>
-__global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const SplitArgs a) {
+// One row tile: t_q x G <= 32 packed rows, two workgroups per CU.  SINGLE: one
+// query token (t_q = 1, the native full-context draft step); otherwise t_q
+// comes from the arguments.
+template <int G, bool SINGLE>
+__global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
   constexpr int ROWB = kVD * 2;
   constexpr float TAU = 8.0f;
-  static_assert(!SINGLE || RT == 1, "one query token is one row tile");
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[4 * kVStage];
-  __shared__ __attribute__((aligned(16))) float sc_lds[2 * 4 * RT * 16 * 64];   // [buf][wave][4 RT][lane][4]
+  __shared__ __attribute__((aligned(16))) float sc_lds[2 * 4 * 16 * 64];   // [buf][wave][4][lane][4]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -92,40 +90,32 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
   const int c32 = lane & 31;     // key (A rows) / packed query row within a row tile (B, C columns)
   const int kh = lane >> 5;      // which 8-element half of a k-step
 
-  // ---- this wave's quarter of Q^T: lane (row 32 r + c32, half kh), k-step s -> piece 2s + kh
-  u32x4 qreg[RT][kVKS];
+  // ---- this wave's quarter of Q^T: lane (row c32, half kh), k-step s -> piece 2s + kh
+  u32x4 qreg[kVKS];
   {
     const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
+    const int j = c32;
+    const int i = j / G, g = j % G;
+    const int64_t qrow = ((int64_t)b * tq + i) * Hq + (int64_t)h * G + g;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int j = 32 * r + c32;
-      const int i = j / G, g = j % G;
-      const int64_t qrow = ((int64_t)b * tq + i) * Hq + (int64_t)h * G + g;
-#pragma unroll
-      for (int s = 0; s < kVKS; ++s) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (j < rows) x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + wave * (kVQ * 2) + (2 * s + kh) * 16);
-        qreg[r][s] = x;
-      }
+    for (int s = 0; s < kVKS; ++s) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (j < rows) x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + wave * (kVQ * 2) + (2 * s + kh) * 16);
+      qreg[s] = x;
     }
     // Settle the query loads here, so no load issued before the main loop is
     // still pending at its header (which would force a full drain per tile).
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(qreg[r][s]));
+    for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(qreg[s]));
   }
 
   uint8_t* my_k = k_lds + wave * kVStage;
   const float c = a.scale_log2;
-  // Last key packed row 32 r + c32 may see in this split (query token
-  // (32 r + c32) / G is causal at n - t_q + (32 r + c32) / G), and the last key
-  // every row sees: only tiles reaching past the latter need a mask.  Padding
-  // rows (>= rows) have zero queries and are never written, so they are left
-  // unmasked.
-  int row_last[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) row_last[r] = min(n - tq + (32 * r + c32) / G, t_end - 1);
+  // Last key packed row c32 may see in this split (query token c32 / G is causal
+  // at n - t_q + c32 / G), and the last key every row sees: only tiles reaching
+  // past the latter need a mask.  Padding rows (>= rows) have zero queries and
+  // are never written, so they are left unmasked.
+  const int row_last = min(n - tq + c32 / G, t_end - 1);
   const int all_last = min(n - tq, t_end - 1);
 
   // Byte offsets of the two (block, head) runs of 16 keys covering tile `it`
@@ -141,10 +131,8 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
   };
 
   // Register ring: tile i's K and V arrive in slot i % kRing, issued kRing - 1
-  // tiles ahead, so kRing - 1 tiles per wave are in flight while one is
-  // computed: two, or one with three row tiles (whose softmax state and
-  // accumulators leave no room for a third slot).
-  constexpr int kRing = RT >= 3 ? 2 : 3;
+  // tiles ahead, so two tiles per wave are in flight while one is computed.
+  constexpr int kRing = 3;
   u32x4 kreg[kRing][kVLoads];
   uint32_t vreg[kRing][2][8];
   int64_t run_next[2];
@@ -174,21 +162,14 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
         vreg[slot][ks][jj] = load_nt<uint32_t>(vbase + run[ks] + (8 * (jj >> 2)) * ROWB, v_off + (jj & 3) * ROWB);
   };
 
-  f32x16 O[RT][2];
+  f32x16 O[2];
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+  for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) O[r][e][x] = 0.f;
-  // Running maximum M of each of this lane's rows in scaled log2 units (scores
-  // times c); both halves of the wave hold the same M for a row.
-  float M[RT], l_lane[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    M[r] = kNegInf;
-    l_lane[r] = 0.f;
-  }
+    for (int x = 0; x < 16; ++x) O[e][x] = 0.f;
+  // Running maximum M of this lane's row in scaled log2 units (scores times c);
+  // both halves of the wave hold the same M for a row.
+  float M = kNegInf, l_lane = 0.f;
 
   auto body = [&](int it, int slot) {
     uint32_t k_off = k_off0, v_off = v_off0;
@@ -205,37 +186,30 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
       const int P = 64 * l + lane;
       *reinterpret_cast<u32x4*>(my_k + vpiece(P / kVNQ, P % kVNQ) * 16) = kreg[slot][l];
     }
-    f32x16 sacc[RT];
+    f32x16 sacc;
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) sacc[r][x] = 0.f;
+    for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
 #pragma unroll
     for (int s = 0; s < kVKS; ++s) {
       const u32x4 ka = *reinterpret_cast<const u32x4*>(my_k + vpiece(c32, 2 * s + kh) * 16);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) sacc[r] = mfma32(ka, qreg[r][s], sacc[r]);
+      sacc = mfma32(ka, qreg[s], sacc);
     }
-    float* sc = sc_lds + (it & 1) * (4 * RT * 16 * 64);
+    float* sc = sc_lds + (it & 1) * (4 * 16 * 64);
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 w4 = {sacc[r][4 * q], sacc[r][4 * q + 1], sacc[r][4 * q + 2], sacc[r][4 * q + 3]};
-        *reinterpret_cast<f32x4*>(sc + ((wave * 4 * RT + 4 * r + q) * 64 + lane) * 4) = w4;
-      }
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 w4 = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+      *reinterpret_cast<f32x4*>(sc + ((wave * 4 + q) * 64 + lane) * 4) = w4;
+    }
     __syncthreads();
-    float s2[RT][16];
+    float s2[16];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+    for (int q = 0; q < 4; ++q) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(sc + (q * 64 + lane) * 4);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 x = *reinterpret_cast<const f32x4*>(sc + ((4 * r + q) * 64 + lane) * 4);
+      for (int w = 1; w < 4; ++w) x += *reinterpret_cast<const f32x4*>(sc + ((w * 4 + q) * 64 + lane) * 4);
 #pragma unroll
-        for (int w = 1; w < 4; ++w) x += *reinterpret_cast<const f32x4*>(sc + ((w * 4 * RT + 4 * r + q) * 64 + lane) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s2[r][4 * q + e] = x[e];
-      }
+      for (int e = 0; e < 4; ++e) s2[4 * q + e] = x[e];
+    }
     // Block ids of the tile the next body issues: scalar loads placed after the
     // last LDS wait of this body, so they complete behind the softmax and PV.
     __builtin_amdgcn_sched_barrier(0);
@@ -245,56 +219,43 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
     // ---- mask (only tiles that reach a causal or split boundary), lazy row maximum
     if (t0 + kVTile - 1 > all_last) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int key = t0 + 8 * (x >> 2) + 4 * kh + (x & 3);
-          s2[r][x] = key <= row_last[r] ? s2[r][x] : kNegInf;
-        }
+      for (int x = 0; x < 16; ++x) {
+        const int key = t0 + 8 * (x >> 2) + 4 * kh + (x & 3);
+        s2[x] = key <= row_last ? s2[x] : kNegInf;
+      }
     }
-    float mx[RT];
-    bool grow = false;
+    float mx = s2[0];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      mx[r] = s2[r][0];
+    for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s2[x]);
+    mx = halves_max(mx) * c;       // c > 0 keeps the order and -inf
+    if (__ballot(mx > M + TAU) != 0) {
+      const float mn = fmaxf(M, mx);
+      const float alpha = (M == kNegInf) ? 0.f : fast_exp2(M - mn);
+      M = mn;
+      l_lane *= alpha;
+      // register x of O holds row 8(x/4) + 4kh + x%4, whose factor sits in that lane
 #pragma unroll
-      for (int x = 1; x < 16; ++x) mx[r] = fmaxf(mx[r], s2[r][x]);
-      mx[r] = halves_max(mx[r]) * c;       // c > 0 keeps the order and -inf
-      grow = grow || (mx[r] > M[r] + TAU);
-    }
-    if (__ballot(grow) != 0) {
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const float mn = fmaxf(M[r], mx[r]);
-        const float alpha = (M[r] == kNegInf) ? 0.f : fast_exp2(M[r] - mn);
-        M[r] = mn;
-        l_lane[r] *= alpha;
-        // register x of O[r] holds row 32 r + 8(x/4) + 4kh + x%4, whose factor sits in that lane
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const float ar = __shfl(alpha, 8 * (x >> 2) + 4 * kh + (x & 3));
-          O[r][0][x] *= ar;
-          O[r][1][x] *= ar;
-        }
+      for (int x = 0; x < 16; ++x) {
+        const float ar = __shfl(alpha, 8 * (x >> 2) + 4 * kh + (x & 3));
+        O[0][x] *= ar;
+        O[1][x] *= ar;
       }
     }
     // p = 2^(s c - M); a row with no visible key yet keeps M = -inf and gets p = 0.
-    uint32_t pk[RT][8];
+    uint32_t pk[8];
+    const float negM = M == kNegInf ? 0.f : -M;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const float negM = M[r] == kNegInf ? 0.f : -M[r];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float p0 = fast_exp2(fmaf(s2[r][2 * q], c, negM));
-        const float p1 = fast_exp2(fmaf(s2[r][2 * q + 1], c, negM));
-        pk[r][q] = pack_bf16x2(p0, p1);
-        l_lane[r] = dot2_bf16(pk[r][q], kBf16One2, l_lane[r]);   // normaliser from the same bf16 weights
-      }
+    for (int q = 0; q < 8; ++q) {
+      const float p0 = fast_exp2(fmaf(s2[2 * q], c, negM));
+      const float p1 = fast_exp2(fmaf(s2[2 * q + 1], c, negM));
+      pk[q] = pack_bf16x2(p0, p1);
+      l_lane = dot2_bf16(pk[q], kBf16One2, l_lane);   // normaliser from the same bf16 weights
     }
 
-    // ---- O += P V over this wave's quarter of D (2 output tiles per row tile, 2 k-steps of 16 keys)
+    // ---- O += P V over this wave's quarter of D (2 output tiles, 2 k-steps of 16 keys)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 pa = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         u32x4 vb;
@@ -302,11 +263,7 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
         for (int q = 0; q < 4; ++q)
           vb[q] = __builtin_amdgcn_perm(vreg[slot][ks][2 * q + 1], vreg[slot][ks][2 * q],
                                         e ? 0x07060302u : 0x05040100u);
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const u32x4 pa = {pk[r][4 * ks], pk[r][4 * ks + 1], pk[r][4 * ks + 2], pk[r][4 * ks + 3]};
-          O[r][e] = mfma32(pa, vb, O[r][e]);
-        }
+        O[e] = mfma32(pa, vb, O[e]);
       }
     }
   };
@@ -326,47 +283,36 @@ __global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void mfma_attn_kernel(const S
     tile_runs(kRing - 1, run_next);
     __builtin_amdgcn_sched_barrier(0);
     int it = 0;
-    if constexpr (kRing == 3) {
-      for (; it + 3 <= ntiles; it += 3) {
-        body(it, 0);
-        body(it + 1, 1);
-        body(it + 2, 2);
-      }
-      if (it < ntiles) body(it, 0);
-      if (it + 1 < ntiles) body(it + 1, 1);
-    } else {
-      for (; it + 2 <= ntiles; it += 2) {
-        body(it, 0);
-        body(it + 1, 1);
-      }
-      if (it < ntiles) body(it, 0);
+    for (; it + 3 <= ntiles; it += 3) {
+      body(it, 0);
+      body(it + 1, 1);
+      body(it + 2, 2);
     }
+    if (it < ntiles) body(it, 0);
+    if (it + 1 < ntiles) body(it + 1, 1);
   }
 
   // ---- normalise and write this wave's quarter of every live row
+  const float l_row = halves_sum(l_lane);       // lanes c32 and c32 + 32 share a row
+  const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const float l_row = halves_sum(l_lane[r]);       // lanes c32 and c32 + 32 share a row
-    const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int row = 32 * r + 8 * (x >> 2) + 4 * kh + (x & 3);
-      const float inv = __shfl(inv_row, row - 32 * r);
-      if (row < rows) {
-        const int i = row / G, g = row % G;
-        const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
-        float2 w2;
-        w2.x = O[r][0][x] * inv;
-        w2.y = O[r][1][x] * inv;
-        *reinterpret_cast<float2*>(a.part_o + orow * kVD + wave * kVQ + 2 * c32) = w2;
-      }
-    }
-    if (wave == 0 && 32 * r + lane < rows && lane < 32) {
-      const int row = 32 * r + lane;
+  for (int x = 0; x < 16; ++x) {
+    const int row = 8 * (x >> 2) + 4 * kh + (x & 3);
+    const float inv = __shfl(inv_row, row);
+    if (row < rows) {
       const int i = row / G, g = row % G;
       const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
-      a.part_lse[orow] = l_row > 0.f ? (M[r] + __log2f(l_row)) * kLn2 : kNegInf;
+      float2 w2;
+      w2.x = O[0][x] * inv;
+      w2.y = O[1][x] * inv;
+      *reinterpret_cast<float2*>(a.part_o + orow * kVD + wave * kVQ + 2 * c32) = w2;
     }
+  }
+  if (wave == 0 && lane < rows && lane < 32) {
+    const int row = lane;
+    const int i = row / G, g = row % G;
+    const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
+    a.part_lse[orow] = l_row > 0.f ? (M + __log2f(l_row)) * kLn2 : kNegInf;
   }
 }
 
@@ -670,10 +616,10 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
 template <int G>
 static hipError_t launch_rt(int rt, bool single, const SplitArgs& a, int grid, hipStream_t st) {
   if (single) {
-    mfma_attn_kernel<G, 1, true><<<grid, 256, 0, st>>>(a);
+    mfma_attn_kernel<G, true><<<grid, 256, 0, st>>>(a);
   } else {
     switch (rt) {
-      case 1: mfma_attn_kernel<G, 1, false><<<grid, 256, 0, st>>>(a); break;
+      case 1: mfma_attn_kernel<G, false><<<grid, 256, 0, st>>>(a); break;
       case 2: mfma_attn_teams_kernel<G, 1><<<grid, 512, 0, st>>>(a); break;
       case 3: mfma_attn_teams_kernel<G, 2><<<grid, 512, 0, st>>>(a); break;
       default: return hipErrorInvalidValue;
