@@ -41,8 +41,8 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "367c22f49888306f13292dfbe85a27737aea94d3e2664b492a95466fa7a21816",
-                  "fetch_kib": 1053696.33, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_TRAFFIC = {"sources_sha256": "5a3a405559cfd0914ac973d990a112e3e34394ab057347e8bd24f99e085899d9",
+                  "fetch_kib": 1053746.45, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
 
