@@ -94,15 +94,18 @@ def stream_ceiling_gbps(dev, nbytes=2 << 30):
 
 
 def paged_ceiling_gbps(step):
-    """Best rate of the paged streaming-read probe over one verify layer's pools, read in
-    the block table's order: (block, head) runs of 8 KiB, one head's blocks after another."""
+    """Best rate of the paged streaming-read probe over one verify layer's pool, read in the
+    block table's order, one head's blocks after another: per (block, head) the 8 KiB of K and
+    the 8 KiB of V after it, i.e. the verify's own access pattern without its arithmetic."""
     wl, n = step.wl, step.n0 + step.wl.gamma + 1
-    k, v, _ = step.layers[1]
+    pool = step.layers[1][0]
     nb = synth.blocks_for(n, 16)
     Hk = wl.num_kv_heads
+    run_bytes = 16 * wl.head_dim * 2                       # one (block, head) half: K or V
+    flat = pool.view(-1)
+    k, v = flat, flat[run_bytes // 2:]                     # V of a run starts 8 KiB after its K
     bt = step.bt[0, :nb].to(torch.int64)
-    runs = torch.cat([bt * Hk + h for h in range(Hk)]).to(torch.int32).contiguous()
-    run_bytes = 16 * wl.head_dim * 2
+    runs = (2 * torch.cat([bt * Hk + h for h in range(Hk)])).to(torch.int32).contiguous()
     nbytes = 2 * runs.numel() * run_bytes
     best = 0.0
     for wgs in (256, 512):
@@ -136,11 +139,12 @@ class Step:
         bt, total = synth.block_table(wl.seed, [blocks], permuted=True)
         self.bt = torch.from_numpy(bt).to(dev)
         self.total_blocks = total
-        self.layers = []                      # (k, v, desc): index 0 is the draft layer's native pool
+        # (pool, desc): index 0 is the draft layer's native pool.  Each pool holds K and V of a
+        # (block, head) side by side, [blocks][H_kv][2][16][D]: one 16 KiB run per block and head.
+        self.layers = []
         for layer in range(target_layers + 1):
-            k = synth.normal((total, Hk, 16, D), wl.seed, ("pool_k", layer), wl.kv_scale, "bf16", dev)
-            v = synth.normal((total, Hk, 16, D), wl.seed, ("pool_v", layer), wl.kv_scale, "bf16", dev)
-            self.layers.append((k, v, W.make_paged(k, v, self.bt)))
+            pool = synth.normal((total, Hk, 2, 16, D), wl.seed, ("pool_kv", layer), wl.kv_scale, "bf16", dev)
+            self.layers.append((pool, W.make_paged_interleaved(pool, self.bt)))
             log(f"  pool {layer} ready")
         S, Wn = wl.sink, wl.window
         self.R = R = g - 1                    # headroom for rolling back rejected drafts
@@ -186,12 +190,12 @@ class Step:
         g, n0 = self.wl.gamma, self.n0
         for j in range(g):
             pos, n = n0 + j, n0 + j + 1
-            kw = dict(paged=self.layers[0][2], chunk_tokens=self.chunk_full) if mode == W.FULL else \
+            kw = dict(paged=self.layers[0][1], chunk_tokens=self.chunk_full) if mode == W.FULL else \
                 dict(ring=self.ring, chunk_tokens=self.chunk_win)
             ws = self.ws_full if mode == W.FULL else self.ws_win
             if not fused:
                 if mode == W.FULL:
-                    W.paged_append(self.sh, self.layers[0][2], self.k_draft[j], self.v_draft[j], [pos])
+                    W.paged_append(self.sh, self.layers[0][1], self.k_draft[j], self.v_draft[j], [pos])
                 else:
                     W.ring_append(self.sh, self.ring, self.k_draft[j], self.v_draft[j], [pos])
             if ev is not None:
@@ -210,7 +214,7 @@ class Step:
         """The target layers' verify; fused: each layer's append runs inside its verify launch."""
         g, n0 = self.wl.gamma, self.n0
         for l in range(len(self.layers) - 1):
-            desc = self.layers[l + 1][2]
+            desc = self.layers[l + 1][1]
             if not fused:
                 W.paged_append(self.sh, desc, self.k_ver, self.v_ver, [n0])
             if ev_list is not None:
@@ -384,7 +388,7 @@ def native_split_measurements(step, flag, reps, dev):
     out = {}
     for chunk, name in ((256, "split_256"), (0, "split_default")):
         ws = W.workspace(W.draft_workspace_bytes(W.FULL, step.sh, [n], chunk), dev)
-        run = lambda: W.draft_attn(W.FULL | flag, step.sh, step.q_draft[0], [n], ws, paged=step.layers[0][2],
+        run = lambda: W.draft_attn(W.FULL | flag, step.sh, step.q_draft[0], [n], ws, paged=step.layers[0][1],
                                    chunk_tokens=chunk)
         run()
         out[name] = pct(_timed(run, reps))["median"]
@@ -400,9 +404,8 @@ def mixed_batch(flag, reps, dev):
     lens = [n + 1 for n in wl.contexts]                 # after this step's append
     B = len(lens)
     bt, total = synth.block_table(wl.seed, [synth.blocks_for(n, 16) for n in lens], permuted=True)
-    k = synth.normal((total, Hk, 16, D), wl.seed, "pool_k", wl.kv_scale, "bf16", dev)
-    v = synth.normal((total, Hk, 16, D), wl.seed, "pool_v", wl.kv_scale, "bf16", dev)
-    desc = W.make_paged(k, v, torch.from_numpy(bt).to(dev))
+    pool = synth.normal((total, Hk, 2, 16, D), wl.seed, "pool_kv", wl.kv_scale, "bf16", dev)   # K|V runs
+    desc = W.make_paged_interleaved(pool, torch.from_numpy(bt).to(dev))
     q = synth.normal((B, Hq, D), wl.seed, "q_draft", 1.0, "bf16", dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
@@ -445,7 +448,7 @@ def mixed_batch(flag, reps, dev):
             res["per_sequence_policy"] = {"sinks": mix_s, "windows": mix_w,
                                           "window_draft_step_us": pct(_timed(mixed, reps))["median"]}
         del rk, rv, tags, wsw
-    del k, v
+    del pool
     torch.cuda.empty_cache()
     return res
 

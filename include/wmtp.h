@@ -97,13 +97,23 @@ typedef struct wmtp_shape {
   int32_t dtype;          /* WMTP_F32 or WMTP_BF16, for q, k and v             */
 } wmtp_shape;
 
+/* Paged KV cache of one layer.  Token t of sequence b, KV head h, lives in
+ * physical block blk = block_table[b][t / 16] at token row
+ *     (blk * H_kv + h) * run_rows + t % 16
+ * of k and of v (a row is D elements).  run_rows = 16 (or 0) gives separate K
+ * and V pools [num_blocks][H_kv][16][D].  run_rows = 32 with v = k + 16 rows
+ * gives one pool [num_blocks][H_kv][2][16][D] in which K and V of a (block,
+ * head) form one contiguous 32-row run; the kernels then read one run of
+ * 32 * D elements per block and head instead of two of half the size, which
+ * streams faster from HBM.  Other run_rows >= 16 are accepted as strides. */
 typedef struct wmtp_paged {
-  void*          k;                   /* device, [num_blocks][H_kv][16][D]        */
-  void*          v;                   /* device, same layout as k                 */
+  void*          k;                   /* device, rows as above                    */
+  void*          v;                   /* device, rows as above                    */
   const int32_t* block_table;         /* device, [batch][max_blocks_per_seq]      */
   int32_t        block_size;          /* must be WMTP_BLOCK_SIZE                  */
   int32_t        max_blocks_per_seq;  /* row stride of block_table                */
   int64_t        num_blocks;          /* physical blocks in k and v               */
+  int32_t        run_rows;            /* 0 or 16: separate pools; >= 16: stride   */
 } wmtp_paged;
 
 /* The compact ring of the windowed draft (Windowed-MTP summary, Abstract).

@@ -73,9 +73,13 @@ int check_paged(const wmtp_paged* kv, bool need_table) {
   if (need_table && !kv->block_table) return WMTP_EINVAL;
   if (kv->block_size != WMTP_BLOCK_SIZE) return WMTP_EUNSUPPORTED;
   if (kv->max_blocks_per_seq <= 0 || kv->num_blocks <= 0) return WMTP_EINVAL;
+  if (kv->run_rows != 0 && kv->run_rows < WMTP_BLOCK_SIZE) return WMTP_EINVAL;
   if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return WMTP_EALIGN;
   return WMTP_OK;
 }
+
+// Token rows from one (block, head) run to the next: 0 means 16 (separate pools).
+int32_t run_rows_of(const wmtp_paged* kv) { return kv->run_rows ? kv->run_rows : WMTP_BLOCK_SIZE; }
 
 int check_ring(const wmtp_ring* r) {
   if (!r || !r->k || !r->v || !r->slot_pos) return WMTP_EINVAL;
@@ -283,6 +287,7 @@ int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_
     a.block_table = kv->block_table;
     a.bt_stride = kv->max_blocks_per_seq;
     a.max_block = kv->num_blocks - 1;
+    a.run_rows = run_rows_of(kv);
   } else {
     a.k = ring->k;
     a.v = ring->v;
@@ -343,6 +348,7 @@ int verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_
   a.block_table = kv->block_table;
   a.bt_stride = kv->max_blocks_per_seq;
   a.max_block = kv->num_blocks - 1;
+  a.run_rows = run_rows_of(kv);
   a.t_q = t_q;
   const int grid = p.total * shape->num_kv_heads;
   return launch_status(launch_verify(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, false, a, grid,
@@ -478,6 +484,7 @@ int wmtp_paged_append(const wmtp_shape* shape, const wmtp_paged* kv, const void*
   a.block_table = kv->block_table;
   a.bt_stride = kv->max_blocks_per_seq;
   a.max_block = kv->num_blocks - 1;
+  a.run_rows = run_rows_of(kv);
   return launch_status(launch_paged_append(a, batch, static_cast<hipStream_t>(stream)));
 }
 
@@ -486,11 +493,12 @@ int wmtp_debug_resolve_paged(const wmtp_paged* kv, int32_t num_kv_heads, int32_t
   if (!kv || !kv->block_table || kv->block_size != WMTP_BLOCK_SIZE || kv->num_blocks <= 0) return WMTP_EINVAL;
   if (kv->max_blocks_per_seq <= 0 || num_kv_heads <= 0 || head_dim <= 0 || b < 0 || h < 0 || h >= num_kv_heads)
     return WMTP_EINVAL;
+  if (kv->run_rows != 0 && kv->run_rows < WMTP_BLOCK_SIZE) return WMTP_EINVAL;
   if (n < 0 || (n > 0 && (!positions || !offsets_out))) return WMTP_EINVAL;
   if (!aligned(offsets_out, 8)) return WMTP_EALIGN;
   const int32_t* row = kv->block_table + (int64_t)b * kv->max_blocks_per_seq;
   return launch_status(launch_debug_resolve_paged(row, kv->max_blocks_per_seq, kv->num_blocks - 1, num_kv_heads,
-                                                  head_dim, h, positions, n, offsets_out,
+                                                  head_dim, run_rows_of(kv), h, positions, n, offsets_out,
                                                   static_cast<hipStream_t>(stream)));
 }
 

@@ -73,6 +73,7 @@ struct SplitArgs {
   float* part_o;
   float* part_lse;
   int64_t max_block;            // num_blocks - 1: block ids are clamped to this
+  int32_t run_rows;             // paged: token rows from one (block, head) run to the next
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t bt_stride;            // max_blocks_per_seq
@@ -96,10 +97,11 @@ struct SplitArgs {
 };
 
 // ----------------------------------------------------------------------------- resolvers
-// Paged pool layout [block][kv_head][16][D]: the byte offset of the start of a
-// (block, head) run of 16 token rows.
-__device__ __forceinline__ int64_t paged_block_run(int64_t blk, int h, int num_kv_heads, int row_bytes) {
-  return (blk * num_kv_heads + h) * (int64_t)kBlock * row_bytes;
+// Paged pool: (block, head) runs of 16 token rows, run_rows rows apart (16:
+// separate K and V pools [block][kv_head][16][D]; 32: K and V of a run
+// interleaved [block][kv_head][2][16][D]).  The byte offset of the start of a run.
+__device__ __forceinline__ int64_t paged_block_run(int64_t blk, int h, int num_kv_heads, int64_t run_bytes) {
+  return (blk * num_kv_heads + h) * run_bytes;
 }
 
 // Physical block of logical token t of a sequence (block-table row `bt_row`),
@@ -118,9 +120,9 @@ __device__ __forceinline__ int64_t paged_block_uniform(const_i32_ptr bt_row, int
 
 // Element offset of (token t, head h, d = 0) in the paged pool.
 __device__ __forceinline__ int64_t paged_elem_offset(const int32_t* bt_row, int64_t t, int h, int num_kv_heads,
-                                                     int head_dim, int64_t max_block) {
+                                                     int head_dim, int64_t max_block, int run_rows) {
   const int64_t blk = paged_block_of(bt_row, t, max_block);
-  return ((blk * num_kv_heads + h) * kBlock + (t % kBlock)) * (int64_t)head_dim;
+  return ((blk * num_kv_heads + h) * run_rows + (t % kBlock)) * (int64_t)head_dim;
 }
 
 // Compact ring: sinks keep slots 0..S-1, later positions cycle through the
@@ -170,7 +172,7 @@ __device__ __forceinline__ void append_own_rows(const SplitArgs& a, int b, int h
       dst = (((int64_t)b * Hkv + h) * a.slots + ring_slot(p, a.sink, cycle)) * row_bytes;
     } else {
       const int64_t blk = paged_block_of(a.block_table + (int64_t)b * a.bt_stride, p, a.max_block);
-      dst = paged_block_run(blk, h, Hkv, row_bytes) + (int64_t)(p % kBlock) * row_bytes;
+      dst = paged_block_run(blk, h, Hkv, (int64_t)a.run_rows * row_bytes) + (int64_t)(p % kBlock) * row_bytes;
     }
     const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(which ? a.v_new : a.k_new) + src);
     *reinterpret_cast<u32x4*>((which ? v : k) + dst + pc * 16) = x;

@@ -153,7 +153,8 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
         run[j] = ring_seq;
       } else {
         const int bi = min((t0 >> 4) + j, last_blk_idx);
-        run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, ROWB);
+        run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv,
+                                 (int64_t)a.run_rows * ROWB);
       }
     }
   };

@@ -31,6 +31,7 @@ struct AppendArgs {
   int64_t max_block;
   int32_t num_kv_heads;
   int32_t row_bytes;            // head_dim * element bytes
+  int32_t run_rows;             // paged: token rows from one (block, head) run to the next
   int32_t t_new;
   int32_t bt_stride;
   int32_t sink;
@@ -49,8 +50,8 @@ hipError_t launch_ring_append(const AppendArgs& a, int batch, hipStream_t st);
 hipError_t launch_paged_append(const AppendArgs& a, int batch, hipStream_t st);
 hipError_t launch_ring_rollback(const AppendArgs& a, int batch, hipStream_t st);
 hipError_t launch_debug_resolve_paged(const int32_t* bt_row, int32_t row_len, int64_t max_block, int num_kv_heads,
-                                      int head_dim, int h, const int32_t* positions, int n, int64_t* out,
-                                      hipStream_t st);
+                                      int head_dim, int run_rows, int h, const int32_t* positions, int n,
+                                      int64_t* out, hipStream_t st);
 hipError_t launch_debug_resolve_ring(int sink, int cycle, const int32_t* positions, int n, int32_t* out,
                                      hipStream_t st);
 hipError_t launch_debug_window_positions(int sink, int window, int headroom, int n, int32_t* out, hipStream_t st);

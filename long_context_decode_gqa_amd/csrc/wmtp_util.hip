@@ -144,7 +144,8 @@ __global__ __launch_bounds__(256) void paged_append_kernel(const AppendArgs a) {
     const int h = hp / pieces, pc = hp % pieces;
     const uint8_t* src = static_cast<const uint8_t*>(which ? a.v_new : a.k_new) + src_tok +
                          (int64_t)h * a.row_bytes + pc * 16;
-    uint8_t* dst = static_cast<uint8_t*>(which ? a.v : a.k) + paged_block_run(blk, h, a.num_kv_heads, a.row_bytes) +
+    uint8_t* dst = static_cast<uint8_t*>(which ? a.v : a.k) +
+                   paged_block_run(blk, h, a.num_kv_heads, (int64_t)a.run_rows * a.row_bytes) +
                    (p % kBlock) * a.row_bytes + pc * 16;
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
   }
@@ -182,13 +183,14 @@ hipError_t launch_paged_append(const AppendArgs& a, int batch, hipStream_t st) {
 
 // ----------------------------------------------------------------------------- index-resolution hooks
 __global__ void debug_resolve_paged_kernel(const int32_t* bt_row, int32_t row_len, int64_t max_block,
-                                           int num_kv_heads, int head_dim, int h, const int32_t* positions, int n,
-                                           int64_t* out) {
+                                           int num_kv_heads, int head_dim, int run_rows, int h,
+                                           const int32_t* positions, int n, int64_t* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int32_t p = positions[i];
-  out[i] = (p < 0 || p / kBlock >= row_len) ? -1
-                                             : paged_elem_offset(bt_row, p, h, num_kv_heads, head_dim, max_block);
+  out[i] = (p < 0 || p / kBlock >= row_len)
+               ? -1
+               : paged_elem_offset(bt_row, p, h, num_kv_heads, head_dim, max_block, run_rows);
 }
 
 __global__ void debug_resolve_ring_kernel(int sink, int cycle, const int32_t* positions, int n, int32_t* out) {
@@ -217,11 +219,11 @@ __global__ void debug_window_positions_kernel(int sink, int window, int cycle, i
 }
 
 hipError_t launch_debug_resolve_paged(const int32_t* bt_row, int32_t row_len, int64_t max_block, int num_kv_heads,
-                                      int head_dim, int h, const int32_t* positions, int n, int64_t* out,
-                                      hipStream_t st) {
+                                      int head_dim, int run_rows, int h, const int32_t* positions, int n,
+                                      int64_t* out, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  debug_resolve_paged_kernel<<<(n + 255) / 256, 256, 0, st>>>(bt_row, row_len, max_block, num_kv_heads, head_dim, h,
-                                                             positions, n, out);
+  debug_resolve_paged_kernel<<<(n + 255) / 256, 256, 0, st>>>(bt_row, row_len, max_block, num_kv_heads, head_dim,
+                                                             run_rows, h, positions, n, out);
   return hipGetLastError();
 }
 

@@ -84,6 +84,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
   const int last_blk_idx = (t_end - 1) >> 4;
   if (a.t_new > 0) append_own_rows<false>(a, b, h, n, max(t_begin, n - a.t_new), t_end, kVD * 2);
   const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
+  const int64_t run_bytes = (int64_t)a.run_rows * ROWB;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + wave * (kVQ * 2);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + wave * (kVQ * 2);
 
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int bi = min((t0 >> 4) + j, last_blk_idx);
-      run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, ROWB);
+      run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, run_bytes);
     }
   };
 
@@ -360,6 +361,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
   const int last_blk_idx = (t_end - 1) >> 4;
   if (a.t_new > 0) append_own_rows<false>(a, b, h, n, max(t_begin, n - a.t_new), t_end, kVD * 2);
   const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
+  const int64_t run_bytes = (int64_t)a.run_rows * ROWB;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + wave * (kVQ * 2);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + wave * (kVQ * 2);
 
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int bi = min((t0 >> 4) + j, last_blk_idx);
-        run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, ROWB);
+        run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, run_bytes);
       }
     };
     constexpr int kRing = 3;

@@ -42,7 +42,7 @@ class Shape(ctypes.Structure):
 class Paged(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("num_blocks", ctypes.c_int64)]
+                ("num_blocks", ctypes.c_int64), ("run_rows", ctypes.c_int32)]
 
 
 class Ring(ctypes.Structure):
@@ -161,9 +161,20 @@ def make_shape(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.
 
 
 def make_paged(k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor) -> Paged:
-    """k, v: [num_blocks][H_kv][16][D]; block_table: int32 [batch][max_blocks] (device)."""
+    """Separate pools k, v: [num_blocks][H_kv][16][D]; block_table: int32 [batch][max_blocks] (device)."""
     assert block_table.dtype == torch.int32 and block_table.dim() == 2
-    return Paged(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), BLOCK_SIZE, block_table.shape[1], k.shape[0])
+    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
+    return Paged(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), BLOCK_SIZE, block_table.shape[1], k.shape[0],
+                 BLOCK_SIZE)
+
+
+def make_paged_interleaved(pool: torch.Tensor, block_table: torch.Tensor) -> Paged:
+    """One pool [num_blocks][H_kv][2][16][D] holding K (index 0) and V (index 1) of each (block, head)
+    as one contiguous run of 32 rows; k and v views are pool[:, :, 0] and pool[:, :, 1]."""
+    assert block_table.dtype == torch.int32 and block_table.dim() == 2
+    assert pool.is_contiguous() and pool.dim() == 5 and pool.shape[2] == 2 and pool.shape[3] == BLOCK_SIZE
+    return Paged(pool[:, :, 0].data_ptr(), pool[:, :, 1].data_ptr(), block_table.data_ptr(), BLOCK_SIZE,
+                 block_table.shape[1], pool.shape[0], 2 * BLOCK_SIZE)
 
 
 def make_ring(k: torch.Tensor, v: torch.Tensor, slot_pos: torch.Tensor, sink: int, window: int,

@@ -38,7 +38,9 @@ design notes):
     sequence may change them between steps without moving any entry;
   * query head h reads KV head h // G (consecutive query heads share a KV head);
   * the softmax scale is 1/sqrt(D);
-  * the paged pool is laid out [block][kv_head][block_offset][D].
+  * the paged pool is laid out [block][kv_head][block_offset][D], or, with K and
+    V of a (block, head) side by side, [block][kv_head][K|V][block_offset][D]:
+    (block, head) runs of block_size rows that lie run_rows rows apart.
 
 Parity pins for every function live in tests/test_oracle_*.py; none of them
 re-types a formula from this file.
@@ -177,16 +179,19 @@ def ring_visible(tags: np.ndarray, n: int, sink: int, window: int) -> np.ndarray
 
 # --------------------------------------------------------------------------- paging
 def paged_element_offset(block_table_row: Sequence[int], t: int, h: int, num_kv_heads: int,
-                         block_size: int, head_dim: int) -> int:
+                         block_size: int, head_dim: int, run_rows: Optional[int] = None) -> int:
     """Element offset of (token t, KV head h, d=0) in a paged pool.
 
-    Reading of the layout: pool[block][kv_head][block_offset][D]; the token's
-    block is block_table_row[t // block_size] and its offset t % block_size.
+    Reading of the layout: the pool is a sequence of (block, kv_head) runs of
+    block_size token rows, run_rows rows apart (run_rows = block_size:
+    pool[block][kv_head][block_offset][D]); the token's block is
+    block_table_row[t // block_size] and its row in the run t % block_size.
     Plain Python integers, so offsets beyond 2**31 are exact.
     """
+    run_rows = block_size if run_rows is None else int(run_rows)
     blk = int(block_table_row[t // block_size])
     off = t % block_size
-    return ((blk * num_kv_heads + h) * block_size + off) * head_dim
+    return ((blk * num_kv_heads + h) * run_rows + off) * head_dim
 
 
 class LogicalKV:
@@ -204,18 +209,26 @@ class LogicalKV:
 class PagedKV:
     """K or V of one sequence read through a block table from a paged pool.
 
-    pool: [num_blocks][H_kv][block_size][D] (f32 values or bf16 bits).
+    pool: [num_blocks][H_kv][block_size][D] (f32 values or bf16 bits), or the
+    K|V pool [num_blocks][H_kv][2][block_size][D] with part = 0 (K) or 1 (V).
     Each position is resolved with `paged_element_offset` on a flat view.
     """
 
-    def __init__(self, pool: np.ndarray, block_table_row: Sequence[int], block_size: int, dtype: str, n: int):
+    def __init__(self, pool: np.ndarray, block_table_row: Sequence[int], block_size: int, dtype: str, n: int,
+                 part: Optional[int] = None):
         self.flat = pool.reshape(-1)
-        self.hk, self.d = pool.shape[1], pool.shape[3]
+        self.hk, self.d = pool.shape[1], pool.shape[-1]
         self.bt = [int(x) for x in block_table_row]
         self.bs, self.dtype, self.n = int(block_size), dtype, int(n)
+        if pool.ndim == 5:                       # K|V runs: 2 * block_size rows apart, V after K
+            assert part in (0, 1)
+            self.run_rows, self.base = 2 * self.bs, part * self.bs * self.d
+        else:
+            self.run_rows, self.base = self.bs, 0
 
     def rows(self, positions: np.ndarray, h: int) -> np.ndarray:
-        offs = np.fromiter((paged_element_offset(self.bt, int(t), h, self.hk, self.bs, self.d)
+        offs = np.fromiter((self.base + paged_element_offset(self.bt, int(t), h, self.hk, self.bs, self.d,
+                                                             self.run_rows)
                             for t in positions), dtype=np.int64, count=len(positions))
         idx = offs[:, None] + np.arange(self.d, dtype=np.int64)[None, :]
         return to_f64(self.flat[idx], self.dtype)

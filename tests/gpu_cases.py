@@ -36,23 +36,42 @@ def place_paged(pool: torch.Tensor, logical: torch.Tensor, bt_row: np.ndarray, b
 
 
 class PagedCache:
-    """One layer's paged K/V for `batch` sequences (device), sized for n0 + extra tokens."""
+    """One layer's paged K/V for `batch` sequences (device), sized for n0 + extra tokens.
 
-    def __init__(self, k_ctx, v_ctx, n0, extra, seed, permuted=True, spare=2):
+    interleaved: one pool [blocks][H_kv][2][16][D] with K and V of a (block, head)
+    side by side (k and v are views of it); else separate pools [blocks][H_kv][16][D]."""
+
+    def __init__(self, k_ctx, v_ctx, n0, extra, seed, permuted=True, spare=2, interleaved=False):
         B = k_ctx.shape[0]
         self.n0 = list(n0)
+        self.interleaved = interleaved
         blocks = [synth.blocks_for(n + extra, 16) for n in self.n0]
         bt, total = synth.block_table(seed, blocks, permuted=permuted, spare_blocks=spare)
         self.bt_np = bt
-        kpool = torch.zeros((total,) + (k_ctx.shape[2], 16, k_ctx.shape[3]), dtype=k_ctx.dtype)
-        vpool = torch.zeros_like(kpool)
+        shape = (total, k_ctx.shape[2], 16, k_ctx.shape[3])
+        if interleaved:
+            pool = torch.zeros((total, k_ctx.shape[2], 2, 16, k_ctx.shape[3]), dtype=k_ctx.dtype)
+            kpool, vpool = pool[:, :, 0], pool[:, :, 1]
+        else:
+            kpool = torch.zeros(shape, dtype=k_ctx.dtype)
+            vpool = torch.zeros_like(kpool)
         for b in range(B):
             place_paged(kpool, k_ctx[b, :self.n0[b]], bt[b])
             place_paged(vpool, v_ctx[b, :self.n0[b]], bt[b])
-        self.k = kpool.to(DEV)
-        self.v = vpool.to(DEV)
         self.bt = torch.from_numpy(bt).to(DEV)
-        self.desc = W.make_paged(self.k, self.v, self.bt)
+        if interleaved:
+            self.pool = pool.to(DEV)
+            self.k, self.v = self.pool[:, :, 0], self.pool[:, :, 1]
+            self.desc = W.make_paged_interleaved(self.pool, self.bt)
+        else:
+            self.k = kpool.to(DEV)
+            self.v = vpool.to(DEV)
+            self.desc = W.make_paged(self.k, self.v, self.bt)
+        self.run_rows = 32 if interleaved else 16
+
+    def element_offset(self, b, t, h):
+        """Oracle element offset of (sequence b, token t, head h) in k (add 16 D for v when interleaved)."""
+        return O.paged_element_offset(self.bt_np[b], t, h, self.k.shape[1], 16, self.k.shape[3], self.run_rows)
 
 
 class RingCache:

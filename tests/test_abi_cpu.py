@@ -50,8 +50,8 @@ def lens(*xs):
     return ctypes.cast((ctypes.c_int32 * len(xs))(*xs), ctypes.c_void_p)
 
 
-def paged(k=FAKE, v=FAKE, bt=FAKE, bs=16, mb=100, nb=100):
-    return W.Paged(k, v, bt, bs, mb, nb)
+def paged(k=FAKE, v=FAKE, bt=FAKE, bs=16, mb=100, nb=100, rr=0):
+    return W.Paged(k, v, bt, bs, mb, nb, rr)
 
 
 def ring(k=FAKE, v=FAKE, tags=FAKE, s=4, w=64, r=0):
@@ -87,6 +87,8 @@ def draft(mode=W.FULL, sh=None, q=FAKE, kv="default", rg="default", seq=(1000,),
     (dict(kv=paged(bs=32)), W.EUNSUPPORTED),
     (dict(kv=paged(k=FAKE_ODD)), W.EALIGN),
     (dict(kv=paged(mb=10)), W.EINVAL),                          # table too short for 1000 tokens
+    (dict(kv=paged(rr=8)), W.EINVAL),                           # runs closer than 16 rows overlap
+    (dict(kv=paged(rr=-16)), W.EINVAL),
     (dict(seq=(-1,)), W.EINVAL),
     (dict(chunk=100), W.EINVAL),                                # not a multiple of 64
     (dict(ws=None), W.EINVAL),
@@ -224,6 +226,8 @@ def test_verify_pointer_checks():
     assert call(wsb=64) == W.EWORKSPACE
     bad = paged(mb=2)
     assert call(kvp=ctypes.byref(bad)) == W.EINVAL
+    bad = paged(rr=15)
+    assert call(kvp=ctypes.byref(bad)) == W.EINVAL
 
 
 def test_combine_checks():
@@ -259,6 +263,9 @@ def test_append_checks():
     assert lib.wmtp_ring_append(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, pos, 0, 1, None) == W.EINVAL
     # paged: 4 blocks cover positions < 64
     assert lib.wmtp_paged_append(ctypes.byref(sh), ctypes.byref(kv), FAKE, FAKE, lens(60), 1, 5, None) == W.EINVAL
+    short_runs = paged(rr=1)
+    assert lib.wmtp_paged_append(ctypes.byref(sh), ctypes.byref(short_runs), FAKE, FAKE, lens(0), 1, 1,
+                                 None) == W.EINVAL
     assert lib.wmtp_paged_append(ctypes.byref(sh), None, FAKE, FAKE, lens(0), 1, 1, None) == W.EINVAL
 
 
@@ -370,6 +377,8 @@ def test_debug_hook_checks():
     kv = paged()
     assert lib.wmtp_debug_resolve_paged(ctypes.byref(kv), 2, 256, 0, 2, FAKE, 1, FAKE, None) == W.EINVAL   # h >= H_kv
     assert lib.wmtp_debug_resolve_paged(None, 2, 256, 0, 0, FAKE, 1, FAKE, None) == W.EINVAL
+    short_runs = paged(rr=4)
+    assert lib.wmtp_debug_resolve_paged(ctypes.byref(short_runs), 2, 256, 0, 0, FAKE, 1, FAKE, None) == W.EINVAL
     assert lib.wmtp_debug_resolve_ring(4, 0, 0, FAKE, 1, FAKE, None) == W.EINVAL
     assert lib.wmtp_debug_window_positions(-1, 4, 0, 10, FAKE, None) == W.EINVAL
     assert lib.wmtp_debug_window_positions(4, 4, 0, 10, None, None) == W.EINVAL

@@ -42,6 +42,13 @@ def test_resolve_paged_bit_exact_past_2_pow_31():
             want = np.array([O.paged_element_offset(bt[b], int(t), h, 2, 16, 256) for t in pos], dtype=np.int64)
             assert np.array_equal(got, want)
     assert want.max() > 2 ** 31
+    # K|V runs of 32 rows (K and V of a block and head side by side)
+    desc32 = W.Paged(0, 0, bt_dev.data_ptr(), 16, bt.shape[1], nb_pool, 32)
+    for b in range(2):
+        for h in range(2):
+            got = W.debug_resolve_paged(desc32, 2, 256, b, h, pos_dev).cpu().numpy()
+            want = np.array([O.paged_element_offset(bt[b], int(t), h, 2, 16, 256, 32) for t in pos], dtype=np.int64)
+            assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("S,Wn", [(4, 4096), (0, 7), (1, 1), (4, 256), (16, 1000)])
@@ -85,29 +92,44 @@ def test_ring_append_sequence_bit_exact(dtype):
                     assert torch.equal(kr[b, :, s_], k_all[b, p]) and torch.equal(vr[b, :, s_], v_all[b, p])
 
 
-def test_paged_append_bit_exact():
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_paged_append_bit_exact(interleaved):
     Hk, D, B = 2, 256, 3
     sh = W.make_shape(16, Hk, D, torch.bfloat16)
     n0 = [5, 16, 33]
     T = 20
     k_ctx = synth.normal((B, 40, Hk, D), 8, "pk", 0.5, "bf16")
-    cache = PagedCache(k_ctx, k_ctx, n0, extra=T, seed=8)
+    cache = PagedCache(k_ctx, k_ctx, n0, extra=T, seed=8, interleaved=interleaved)
     k_new = synth.normal((B, T, Hk, D), 8, "pkn", 0.5, "bf16")
     v_new = synth.normal((B, T, Hk, D), 8, "pvn", 0.5, "bf16")
-    before_k = cache.k.cpu().clone()
+    # flat memory of k and v, and the element offset of v's rows relative to k's
+    if interleaved:
+        flat = lambda: (cache.pool.cpu().reshape(-1),) * 2
+        v_shift = 16 * D
+    else:
+        flat = lambda: (cache.k.cpu().reshape(-1), cache.v.cpu().reshape(-1))
+        v_shift = 0
+    before_k, before_v = (x.clone() for x in flat())
     W.paged_append(sh, cache.desc, k_new.to(DEV), v_new.to(DEV), n0)
     torch.cuda.synchronize()
-    kf = cache.k.cpu().reshape(-1)
-    vf = cache.v.cpu().reshape(-1)
-    touched = np.zeros(kf.numel(), dtype=bool)
+    kf, vf = flat()
+    touched_k = np.zeros(kf.numel(), dtype=bool)
+    touched_v = np.zeros(vf.numel(), dtype=bool)
     for b in range(B):
         for i in range(T):
             for h in range(Hk):
-                off = O.paged_element_offset(cache.bt_np[b], n0[b] + i, h, Hk, 16, D)
-                assert torch.equal(kf[off:off + D], k_new[b, i, h]) and torch.equal(vf[off:off + D], v_new[b, i, h])
-                touched[off:off + D] = True
-    untouched = torch.from_numpy(~touched)
-    assert torch.equal(kf[untouched], before_k.reshape(-1)[untouched])
+                off = cache.element_offset(b, n0[b] + i, h)
+                assert torch.equal(kf[off:off + D], k_new[b, i, h])
+                assert torch.equal(vf[off + v_shift:off + v_shift + D], v_new[b, i, h])
+                touched_k[off:off + D] = True
+                touched_v[off + v_shift:off + v_shift + D] = True
+    if interleaved:                      # one pool: every row not appended is unchanged
+        untouched = torch.from_numpy(~(touched_k | touched_v))
+        assert torch.equal(kf[untouched], before_k[untouched])
+    else:
+        for f, before, touched in ((kf, before_k, touched_k), (vf, before_v, touched_v)):
+            untouched = torch.from_numpy(~touched)
+            assert torch.equal(f[untouched], before[untouched])
 
 
 # ============================================================== headroom and rollback
@@ -265,7 +287,7 @@ def test_per_sequence_sinks_and_windows_parity(fast_pv):
 
 # ============================================================== draft attention
 def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtype=torch.float32, fused=False,
-                headroom=0, record=None):
+                headroom=0, record=None, interleaved=False):
     """Run gamma draft steps on the GPU and the oracle; return the worst max-abs errors (o, lse).
 
     fused: append and attend in one call (wmtp_draft_attn_append) instead of an
@@ -281,7 +303,8 @@ def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtyp
     new_k = host_array(case.k_new, dt)      # [gamma][B][1][Hk][D]
     new_v = host_array(case.v_new, dt)
     if mode == O.FULL:
-        cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=steps, seed=wl.seed, permuted=wl.permuted)
+        cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=steps, seed=wl.seed, permuted=wl.permuted,
+                           interleaved=interleaved)
     else:
         ring = RingCache(B, Hk, D, wl.sink, wl.window, TDT[dt], headroom)
         for b in range(B):                   # bulk-fill each sequence's ring with its context
@@ -384,14 +407,15 @@ def test_window_covering_context_equals_full_on_gpu():
 
 
 # ============================================================== verify attention
-def verify_run(wl, contexts, t_q, split=0, layer=0, fused=False, record=None):
+def verify_run(wl, contexts, t_q, split=0, layer=0, fused=False, record=None, interleaved=False):
     """Verify on the GPU (append + verify, or the fused call) against the oracle: worst (o, lse) errors.
     record: a list that receives (out, lse, k pool, v pool)."""
     case = synth.verify_case(wl, contexts, t_q, layer=layer)
     B, Hq, Hk, D = len(case.n0), wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     dt = wl.dtype
     sh = W.make_shape(Hq, Hk, D, TDT[dt], wl.scale)
-    cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=t_q, seed=wl.seed + 100 + layer)
+    cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=t_q, seed=wl.seed + 100 + layer,
+                       interleaved=interleaved)
     kn, vn = case.k_new.contiguous().to(DEV), case.v_new.contiguous().to(DEV)
     lens = [n + t_q for n in case.n0]
     ws = W.workspace(W.verify_workspace_bytes(sh, t_q, lens, split), DEV)
@@ -506,15 +530,63 @@ def test_draft_fused_append_fp32_and_other_shapes(mode):
         assert eo <= tol and el <= tol, (eo, el)
 
 
+# ============================================================== K|V runs: one pool, K and V of a (block, head) side by side
+# The same tokens in a [blocks][H_kv][2][16][D] pool must give the oracle's
+# result and, bit for bit, the result over separate K and V pools.
+@pytest.mark.parametrize("contexts,t_q,split,fused", [((500, 7), 4, 64, False), ((62, 4000), 4, 0, True),
+                                                      ((29, 300), 6, 32, True), ((2044, 17), 9, 256, False)])
+def test_verify_kv_runs_pool(contexts, t_q, split, fused):
+    wl = synth.workload("step_1m_bf16")
+    say("verify K|V runs", contexts, t_q, split, fused)
+    runs, sep = [], []
+    eo, el = verify_run(wl, contexts, t_q, split, fused=fused, record=runs, interleaved=True)
+    verify_run(wl, contexts, t_q, split, fused=fused, record=sep, interleaved=False)
+    for a, b in zip(runs[0], sep[0]):            # out, lse, and the K and V token rows (views)
+        assert torch.equal(a, b)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
+@pytest.mark.parametrize("fast_pv", [False, True])
+@pytest.mark.parametrize("fused", [False, True])
+def test_draft_kv_runs_pool(fast_pv, fused):
+    wl = synth.workload("draft_131k_bf16", window=1024)
+    say("draft K|V runs", fast_pv, fused)
+    runs, sep = [], []
+    eo, el = draft_steps(wl, (63, 0, 2000), O.FULL, chunk=64, fast_pv=fast_pv, fused=fused, record=runs,
+                         interleaved=True)
+    draft_steps(wl, (63, 0, 2000), O.FULL, chunk=64, fast_pv=fast_pv, fused=fused, record=sep)
+    for got, want in zip(runs, sep):
+        for a, b in zip(got, want):
+            assert torch.equal(a, b)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+    wl = synth.workload("tiny_fp32_4k")
+    eo, el = draft_steps(wl, None, O.FULL, fused=fused, interleaved=True)
+    assert eo <= TOL["f32"] and el <= TOL["f32"], (eo, el)
+
+
 # ============================================================== 1M-token cases (sampled)
-def _paged_1m(seed, hk=2, d=256, extra=8):
+def _paged_1m(seed, hk=2, d=256, extra=8, interleaved=False):
+    """A 1,048,576-token paged layer (random block permutation): separate K and V pools, or one
+    K|V pool as the benchmark lays them out.  Returns n0, the block table (host and device), the k
+    and v token views, the descriptor and src(part, n): the oracle's view of K (0) or V (1)
+    positions < n as generated."""
     n0 = 1 << 20
     blocks = synth.blocks_for(n0 + extra, 16)
     bt, total = synth.block_table(seed, [blocks], permuted=True)
-    k = synth.normal((total, hk, 16, d), seed, "pool_k", 0.5, "bf16", DEV)
-    v = synth.normal((total, hk, 16, d), seed, "pool_v", 0.5, "bf16", DEV)
     btd = torch.from_numpy(bt).to(DEV)
-    return n0, bt, k, v, btd
+    if interleaved:
+        pool = synth.normal((total, hk, 2, 16, d), seed, "pool_kv", 0.5, "bf16", DEV)
+        k, v = pool[:, :, 0], pool[:, :, 1]
+        desc = W.make_paged_interleaved(pool, btd)
+        bits = synth.bf16_bits(pool)
+        src = lambda part, n: O.PagedKV(bits, bt[0], 16, "bf16", n, part=part)
+    else:
+        k = synth.normal((total, hk, 16, d), seed, "pool_k", 0.5, "bf16", DEV)
+        v = synth.normal((total, hk, 16, d), seed, "pool_v", 0.5, "bf16", DEV)
+        desc = W.make_paged(k, v, btd)
+        kb, vb = synth.bf16_bits(k), synth.bf16_bits(v)
+        src = lambda part, n: O.PagedKV(kb if part == 0 else vb, bt[0], 16, "bf16", n)
+    return n0, bt, k, v, btd, desc, src
 
 
 @pytest.mark.slow
@@ -522,9 +594,8 @@ def test_draft_full_1m_paged_sampled_head():
     """Native draft step over a 1,048,576-token paged pool (random block permutation), fp32 PV
     weights and 256-token splits (the dot-product kernel); one KV head checked."""
     say("draft 1M")
-    n0, bt, k, v, btd = _paged_1m(2)
+    n0, bt, k, v, btd, desc, src = _paged_1m(2)
     sh = W.make_shape(16, 2, 256, torch.bfloat16, 1 / 16)
-    desc = W.make_paged(k, v, btd)
     kn = synth.normal((1, 1, 2, 256), 2, "kn1m", 0.5, "bf16", DEV)
     vn = synth.normal((1, 1, 2, 256), 2, "vn1m", 0.5, "bf16", DEV)
     q = synth.normal((1, 16, 256), 2, "q1m", 1.0, "bf16", DEV)
@@ -535,10 +606,9 @@ def test_draft_full_1m_paged_sampled_head():
     out, lse = run_combine(parts, 16, 256, 1)
     torch.cuda.synchronize()
     # oracle: context from the pool as generated (never the appended pool), plus the new token
-    kh, vh = synth.bf16_bits(k), synth.bf16_bits(v)
     h = 1
-    sk = O.ConcatKV(O.PagedKV(kh, bt[0], 16, "bf16", n0), O.LogicalKV(synth.bf16_bits(kn[0]), "bf16"))
-    sv = O.ConcatKV(O.PagedKV(vh, bt[0], 16, "bf16", n0), O.LogicalKV(synth.bf16_bits(vn[0]), "bf16"))
+    sk = O.ConcatKV(src(0, n0), O.LogicalKV(synth.bf16_bits(kn[0]), "bf16"))
+    sv = O.ConcatKV(src(1, n0), O.LogicalKV(synth.bf16_bits(vn[0]), "bf16"))
     qf = O.to_f64(synth.bf16_bits(q[0]), "bf16")
     o_ref, l_ref = O.attention_over(qf[h * 8:(h + 1) * 8], sk, sv, np.arange(n), h, 1 / 16)
     eo = max_err(out[0, h * 8:(h + 1) * 8], o_ref)
@@ -551,22 +621,19 @@ def test_verify_1m_paged_sampled_head():
     """One target layer's verify at 1M context in the benchmark's launch configuration (default
     splits): 4 causal queries over 1,048,580 keys, two query tokens checked on one KV head."""
     say("verify 1M")
-    n0, bt, k, v, btd = _paged_1m(3)
+    n0, bt, k, v, btd, desc, src = _paged_1m(3, interleaved=True)
     sh = W.make_shape(16, 2, 256, torch.bfloat16, 1 / 16)
-    desc = W.make_paged(k, v, btd)
     kn = synth.normal((1, 4, 2, 256), 3, "kn1m", 0.5, "bf16", DEV)
     vn = synth.normal((1, 4, 2, 256), 3, "vn1m", 0.5, "bf16", DEV)
     q = synth.normal((1, 4, 16, 256), 3, "q1m", 1.0, "bf16", DEV)
-    W.paged_append(sh, desc, kn, vn, [n0])
     n = n0 + 4
     ws = W.workspace(W.verify_workspace_bytes(sh, 4, [n], 0), DEV)
-    parts = W.verify_attn(sh, q, 4, desc, [n], ws, 0)
+    parts = W.verify_attn_append(sh, q, 4, desc, kn, vn, [n], ws, 0)
     out, lse = run_combine(parts, 64, 256, 1)
     torch.cuda.synchronize()
-    kh, vh = synth.bf16_bits(k), synth.bf16_bits(v)
     h = 0
-    sk = O.ConcatKV(O.PagedKV(kh, bt[0], 16, "bf16", n0), O.LogicalKV(synth.bf16_bits(kn[0]), "bf16"))
-    sv = O.ConcatKV(O.PagedKV(vh, bt[0], 16, "bf16", n0), O.LogicalKV(synth.bf16_bits(vn[0]), "bf16"))
+    sk = O.ConcatKV(src(0, n0), O.LogicalKV(synth.bf16_bits(kn[0]), "bf16"))
+    sv = O.ConcatKV(src(1, n0), O.LogicalKV(synth.bf16_bits(vn[0]), "bf16"))
     qf = O.to_f64(synth.bf16_bits(q[0]), "bf16")          # [4][16][256]
     for i in (0, 3):
         o_ref, l_ref = O.attention_over(qf[i, h * 8:(h + 1) * 8], sk, sv, np.arange(n0 + i + 1), h, 1 / 16)
@@ -599,29 +666,25 @@ def test_draft_1m_benchmark_launch_config(mode):
     headroom; one KV head checked."""
     S, Wn, R = 4, 4096, 2
     say("draft 1M bench config", mode)
-    n0, bt, k, v, btd = _paged_1m(6)
+    n0, bt, k, v, btd, desc, src = _paged_1m(6, interleaved=True)
     sh = W.make_shape(16, 2, 256, torch.bfloat16, 1 / 16)
-    desc = W.make_paged(k, v, btd)
     kn = synth.normal((1, 1, 2, 256), 6, "kn", 0.5, "bf16", DEV)
     vn = synth.normal((1, 1, 2, 256), 6, "vn", 0.5, "bf16", DEV)
     q = synth.normal((1, 16, 256), 6, "q", 1.0, "bf16", DEV)
     n = n0 + 1
     if mode == O.FULL:
-        W.paged_append(sh, desc, kn, vn, [n0])
         ws = W.workspace(W.draft_workspace_bytes(W.FULL, sh, [n], 0), DEV)
-        parts = W.draft_attn(W.FULL | W.DRAFT_FAST_PV, sh, q, [n], ws, paged=desc)
+        parts = W.draft_attn_append(W.FULL | W.DRAFT_FAST_PV, sh, q, kn, vn, [n], ws, paged=desc)
     else:
         ring = RingCache(1, 2, 256, S, Wn, torch.bfloat16, headroom=R)
         _fill_ring(sh, ring.desc, k, v, btd[0], n0, S, Wn, R)
-        W.ring_append(sh, ring.desc, kn, vn, [n0])
         ws = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, [n], 0, S, Wn, R), DEV)
-        parts = W.draft_attn(W.SINK_WINDOW | W.DRAFT_FAST_PV, sh, q, [n], ws, ring=ring.desc)
+        parts = W.draft_attn_append(W.SINK_WINDOW | W.DRAFT_FAST_PV, sh, q, kn, vn, [n], ws, ring=ring.desc)
     out, lse = run_combine(parts, 16, 256, 1)
     torch.cuda.synchronize()
-    kh, vh = synth.bf16_bits(k), synth.bf16_bits(v)
     h = 1
-    sk = O.ConcatKV(O.PagedKV(kh, bt[0], 16, "bf16", n0), O.LogicalKV(synth.bf16_bits(kn[0]), "bf16"))
-    sv = O.ConcatKV(O.PagedKV(vh, bt[0], 16, "bf16", n0), O.LogicalKV(synth.bf16_bits(vn[0]), "bf16"))
+    sk = O.ConcatKV(src(0, n0), O.LogicalKV(synth.bf16_bits(kn[0]), "bf16"))
+    sv = O.ConcatKV(src(1, n0), O.LogicalKV(synth.bf16_bits(vn[0]), "bf16"))
     qf = O.to_f64(synth.bf16_bits(q[0]), "bf16")
     rows = slice(h * 8, h * 8 + 8)
     o_ref, l_ref = O.attention_over(qf[rows], sk, sv, O.visible_positions(n, mode, S, Wn), h, 1 / 16)
@@ -641,11 +704,11 @@ def test_draft_131k_three_steps_full_size(mode):
     nb = synth.blocks_for(n0 + wl.gamma, 16)
     bt, total = synth.block_table(wl.seed, [nb], permuted=False)
     btd = torch.from_numpy(bt).to(DEV)
-    k = synth.normal((total, 2, 16, 256), wl.seed, "c2k", wl.kv_scale, "bf16", DEV)
-    v = synth.normal((total, 2, 16, 256), wl.seed, "c2v", wl.kv_scale, "bf16", DEV)
-    kh, vh = synth.bf16_bits(k), synth.bf16_bits(v)                 # the context as generated (before appends)
+    pool = synth.normal((total, 2, 2, 16, 256), wl.seed, "c2kv", wl.kv_scale, "bf16", DEV)   # K|V runs
+    k, v = pool[:, :, 0], pool[:, :, 1]
+    bits = synth.bf16_bits(pool)                                    # the context as generated (before appends)
     sh = W.make_shape(16, 2, 256, torch.bfloat16, wl.scale)
-    desc = W.make_paged(k, v, btd)
+    desc = W.make_paged_interleaved(pool, btd)
     if mode == O.SINK_WINDOW:
         ring = RingCache(1, 2, 256, S, Wn, torch.bfloat16)
         _fill_ring(sh, ring.desc, k, v, btd[0], n0, S, Wn, 0)
@@ -656,19 +719,18 @@ def test_draft_131k_three_steps_full_size(mode):
     for j in range(wl.gamma):
         n = n0 + j + 1
         if mode == O.FULL:
-            W.paged_append(sh, desc, kn[j], vn[j], [n - 1])
             ws = W.workspace(W.draft_workspace_bytes(W.FULL, sh, [n], 0), DEV)
-            parts = W.draft_attn(W.FULL | W.DRAFT_FAST_PV, sh, q[j], [n], ws, paged=desc)
+            parts = W.draft_attn_append(W.FULL | W.DRAFT_FAST_PV, sh, q[j], kn[j], vn[j], [n], ws, paged=desc)
         else:
-            W.ring_append(sh, ring.desc, kn[j], vn[j], [n - 1])
             ws = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, [n], 0, S, Wn), DEV)
-            parts = W.draft_attn(W.SINK_WINDOW | W.DRAFT_FAST_PV, sh, q[j], [n], ws, ring=ring.desc)
+            parts = W.draft_attn_append(W.SINK_WINDOW | W.DRAFT_FAST_PV, sh, q[j], kn[j], vn[j], [n], ws,
+                                        ring=ring.desc)
         out, lse = run_combine(parts, 16, 256, 1)
         torch.cuda.synchronize()
         new_k = synth.bf16_bits(kn[:j + 1, 0, 0])                   # [j+1][H_kv][D]
         new_v = synth.bf16_bits(vn[:j + 1, 0, 0])
-        sk = O.ConcatKV(O.PagedKV(kh, bt[0], 16, "bf16", n0), O.LogicalKV(new_k, "bf16"))
-        sv = O.ConcatKV(O.PagedKV(vh, bt[0], 16, "bf16", n0), O.LogicalKV(new_v, "bf16"))
+        sk = O.ConcatKV(O.PagedKV(bits, bt[0], 16, "bf16", n0, part=0), O.LogicalKV(new_k, "bf16"))
+        sv = O.ConcatKV(O.PagedKV(bits, bt[0], 16, "bf16", n0, part=1), O.LogicalKV(new_v, "bf16"))
         qf = O.to_f64(synth.bf16_bits(q[j, 0]), "bf16")
         rows = slice(h * 8, h * 8 + 8)
         o_ref, l_ref = O.attention_over(qf[rows], sk, sv, O.visible_positions(n, mode, S, Wn), h, wl.scale)
@@ -689,11 +751,11 @@ def test_mixed_batch_full_sizes():
     B = len(lens0)
     bt, total = synth.block_table(wl.seed, [synth.blocks_for(n + 1, 16) for n in lens0], permuted=True)
     btd = torch.from_numpy(bt).to(DEV)
-    k = synth.normal((total, 2, 16, 256), wl.seed, "c5k", wl.kv_scale, "bf16", DEV)
-    v = synth.normal((total, 2, 16, 256), wl.seed, "c5v", wl.kv_scale, "bf16", DEV)
-    kh, vh = synth.bf16_bits(k), synth.bf16_bits(v)
+    pool = synth.normal((total, 2, 2, 16, 256), wl.seed, "c5kv", wl.kv_scale, "bf16", DEV)   # K|V runs
+    k, v = pool[:, :, 0], pool[:, :, 1]
+    bits = synth.bf16_bits(pool)
     sh = W.make_shape(16, 2, 256, torch.bfloat16, wl.scale)
-    desc = W.make_paged(k, v, btd)
+    desc = W.make_paged_interleaved(pool, btd)
     kn = synth.normal((B, 1, 2, 256), wl.seed, "c5kn", wl.kv_scale, "bf16", DEV)
     vn = synth.normal((B, 1, 2, 256), wl.seed, "c5vn", wl.kv_scale, "bf16", DEV)
     q = synth.normal((B, 16, 256), wl.seed, "c5q", 1.0, "bf16", DEV)
@@ -703,8 +765,10 @@ def test_mixed_batch_full_sizes():
     rows = slice(h * 8, h * 8 + 8)
 
     def ref(b, mode, Wn):
-        sk = O.ConcatKV(O.PagedKV(kh, bt[b], 16, "bf16", lens0[b]), O.LogicalKV(synth.bf16_bits(kn[b]), "bf16"))
-        sv = O.ConcatKV(O.PagedKV(vh, bt[b], 16, "bf16", lens0[b]), O.LogicalKV(synth.bf16_bits(vn[b]), "bf16"))
+        sk = O.ConcatKV(O.PagedKV(bits, bt[b], 16, "bf16", lens0[b], part=0),
+                        O.LogicalKV(synth.bf16_bits(kn[b]), "bf16"))
+        sv = O.ConcatKV(O.PagedKV(bits, bt[b], 16, "bf16", lens0[b], part=1),
+                        O.LogicalKV(synth.bf16_bits(vn[b]), "bf16"))
         return O.attention_over(qf[b, rows], sk, sv, O.visible_positions(lens[b], mode, S, Wn), h, wl.scale)
 
     # window mode first (the pool is left as generated), one ring per W

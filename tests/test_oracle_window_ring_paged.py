@@ -265,6 +265,39 @@ def test_paged_gather_equals_contiguous(n, bs):
     assert np.array_equal(a[0], b[0])
 
 
+def _place_paged_kv_runs(k_logical, v_logical, bt_row, bs, num_blocks):
+    """Build a K|V pool [block][H][2][bs][D] from logical K and V by block-level slicing."""
+    n, H, D = k_logical.shape
+    pool = np.zeros((num_blocks, H, 2, bs, D), dtype=k_logical.dtype)
+    for j in range(-(-n // bs)):
+        for part, logical in ((0, k_logical), (1, v_logical)):
+            seg = logical[j * bs:(j + 1) * bs]
+            pool[bt_row[j], :, part, :seg.shape[0], :] = seg.transpose(1, 0, 2)
+    return pool
+
+
+@pytest.mark.parametrize("n,bs", [(1, 16), (16, 16), (17, 16), (300, 16), (100, 8)])
+def test_paged_kv_runs_gather_equals_contiguous(n, bs):
+    rng = np.random.default_rng(100 + n)
+    H, D = 2, 8
+    nb = -(-n // bs) + 3
+    bt = rng.permutation(nb).astype(np.int32)
+    k_log = rng.standard_normal((n, H, D)).astype(np.float32)
+    v_log = rng.standard_normal((n, H, D)).astype(np.float32)
+    pool = _place_paged_kv_runs(k_log, v_log, bt, bs, nb)
+    ks, vs = O.PagedKV(pool, bt, bs, "f32", n, part=0), O.PagedKV(pool, bt, bs, "f32", n, part=1)
+    pos = rng.permutation(n)
+    for h in range(H):
+        assert np.array_equal(ks.rows(pos, h), k_log[pos, h].astype(np.float64))
+        assert np.array_equal(vs.rows(pos, h), v_log[pos, h].astype(np.float64))
+    # the same tokens in separate pools give the same attention, bit for bit
+    q = rng.standard_normal((4, D))
+    a = O.draft_attention(q, ks, vs, n, O.FULL, 0, 0, 0.3)
+    b = O.draft_attention(q, O.PagedKV(_place_paged(k_log, bt, bs, nb), bt, bs, "f32", n),
+                          O.PagedKV(_place_paged(v_log, bt, bs, nb), bt, bs, "f32", n), n, O.FULL, 0, 0, 0.3)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_paged_offsets_hand_worked_and_past_2_pow_31():
     # pool [block][kv_head][16][D]: block 5, head 1, offset 3, D 256, 2 heads
     assert O.paged_element_offset([9, 5], 16 + 3, 1, 2, 16, 256) == ((5 * 2 + 1) * 16 + 3) * 256
@@ -273,3 +306,8 @@ def test_paged_offsets_hand_worked_and_past_2_pow_31():
     off = O.paged_element_offset([big] * 2, 15, 1, 2, 16, 256)
     assert off == big * 2 * 16 * 256 + 1 * 16 * 256 + 15 * 256
     assert off > 2 ** 31
+    # K|V runs of 32 rows: block 5, head 1, offset 3 -> run (5 * 2 + 1), row 3 of its K half
+    assert O.paged_element_offset([9, 5], 16 + 3, 1, 2, 16, 256, 32) == ((5 * 2 + 1) * 32 + 3) * 256
+    # run_rows = block_size is the separate-pool layout
+    assert O.paged_element_offset([9, 5], 16 + 3, 1, 2, 16, 256, 16) == O.paged_element_offset([9, 5], 19, 1, 2,
+                                                                                                16, 256)
