@@ -41,8 +41,8 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "5a3a405559cfd0914ac973d990a112e3e34394ab057347e8bd24f99e085899d9",
-                  "fetch_kib": 1053746.45, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_TRAFFIC = {"sources_sha256": "10dd6fbc1e8502018e7e0e64a31ed521f02baffa3d1c5db80f68fa38075e15da",
+                  "fetch_kib": 1053689.26, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
 
@@ -102,10 +102,15 @@ def paged_ceiling_gbps(step):
     nb = synth.blocks_for(n, 16)
     Hk = wl.num_kv_heads
     run_bytes = 16 * wl.head_dim * 2                       # one (block, head) half: K or V
-    flat = pool.view(-1)
-    k, v = flat, flat[run_bytes // 2:]                     # V of a run starts 8 KiB after its K
     bt = step.bt[0, :nb].to(torch.int64)
-    runs = (2 * torch.cat([bt * Hk + h for h in range(Hk)])).to(torch.int32).contiguous()
+    runs = torch.cat([bt * Hk + h for h in range(Hk)])
+    if step.kv_runs:
+        flat = pool.view(-1)
+        k, v = flat, flat[run_bytes // 2:]                 # V of a run starts 8 KiB after its K
+        runs = 2 * runs
+    else:
+        k, v = pool
+    runs = runs.to(torch.int32).contiguous()
     nbytes = 2 * runs.numel() * run_bytes
     best = 0.0
     for wgs in (256, 512):
@@ -130,7 +135,7 @@ def log(*a):
 class Step:
     """Device state of one decode step: draft layer (pool + ring) and target layers."""
 
-    def __init__(self, wl, n0, target_layers, chunk_full, chunk_win, split, dev):
+    def __init__(self, wl, n0, target_layers, chunk_full, chunk_win, split, dev, kv_runs=True):
         self.wl, self.n0, self.dev = wl, n0, dev
         Hq, Hk, D, g = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma
         self.sh = W.make_shape(Hq, Hk, D, torch.bfloat16, wl.scale)
@@ -139,12 +144,19 @@ class Step:
         bt, total = synth.block_table(wl.seed, [blocks], permuted=True)
         self.bt = torch.from_numpy(bt).to(dev)
         self.total_blocks = total
-        # (pool, desc): index 0 is the draft layer's native pool.  Each pool holds K and V of a
-        # (block, head) side by side, [blocks][H_kv][2][16][D]: one 16 KiB run per block and head.
+        # (pool, desc): index 0 is the draft layer's native pool.  kv_runs: each pool holds K and V
+        # of a (block, head) side by side, [blocks][H_kv][2][16][D] (one 16 KiB run per block and
+        # head); else separate K and V pools [blocks][H_kv][16][D] (pool = (k, v)).
+        self.kv_runs = kv_runs
         self.layers = []
         for layer in range(target_layers + 1):
-            pool = synth.normal((total, Hk, 2, 16, D), wl.seed, ("pool_kv", layer), wl.kv_scale, "bf16", dev)
-            self.layers.append((pool, W.make_paged_interleaved(pool, self.bt)))
+            if kv_runs:
+                pool = synth.normal((total, Hk, 2, 16, D), wl.seed, ("pool_kv", layer), wl.kv_scale, "bf16", dev)
+                self.layers.append((pool, W.make_paged_interleaved(pool, self.bt)))
+            else:
+                k = synth.normal((total, Hk, 16, D), wl.seed, ("pool_k", layer), wl.kv_scale, "bf16", dev)
+                v = synth.normal((total, Hk, 16, D), wl.seed, ("pool_v", layer), wl.kv_scale, "bf16", dev)
+                self.layers.append(((k, v), W.make_paged(k, v, self.bt)))
             log(f"  pool {layer} ready")
         S, Wn = wl.sink, wl.window
         self.R = R = g - 1                    # headroom for rolling back rejected drafts
@@ -568,6 +580,8 @@ def main():
                     help="skip the extra measurements (graph replay, cold window, split and batch variants)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step at --context: steps over contexts 2K..1M and gamma 3/5/8")
+    ap.add_argument("--pool-layout", choices=("kv_runs", "separate"), default="kv_runs",
+                    help="paged pools: K and V of a (block, head) side by side (default), or separate K and V")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 256 MiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -602,7 +616,7 @@ def main():
     ceiling = stream_ceiling_gbps(dev)
     log(f"setup: {wl.target_layers} target layers + 1 draft layer at {n0} tokens")
     step = Step(wl, n0, wl.target_layers, args.chunk_full, args.chunk_window,
-                args.split, dev)
+                args.split, dev, kv_runs=args.pool_layout == "kv_runs")
 
     log("paged streaming-read ceiling")
     paged_ceiling = paged_ceiling_gbps(step)
@@ -660,6 +674,8 @@ def main():
                          f"mode S={wl.sink} W={wl.window}"),
             "context": n0, "gamma": g, "target_layers": wl.target_layers,
             "draft_pv": "fp32 weights" if args.exact_pv else "bf16 weight pairs",
+            "pool_layout": ("[blocks][H_kv][K|V][16][D]" if args.pool_layout == "kv_runs"
+                            else "[blocks][H_kv][16][D] per K and V"),
         },
         "windowed_us_per_step": round(win_ms * 1e3, 1),
         "native_us_per_step": round(nat_ms * 1e3, 1),
