@@ -797,3 +797,82 @@ def test_mixed_batch_full_sizes():
         eo, el = max_err(out[b, rows], o_ref), max_err(lse[b, rows], l_ref)
         assert eo <= TOL["bf16"] and el <= TOL["bf16"], ("full", b, eo, el)
 
+
+
+# ============================================================== HIP graph capture
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+def test_decode_step_graph_replays_match_eager(mode):
+    """A small decode step (3 fused draft steps + combines, 2 fused verify layers + combines)
+    captured in a HIP graph: every replay, with eager work and synchronisations between replays,
+    gives the eager step's outputs bit for bit (the kernels are deterministic), and the eager
+    step matches the oracle."""
+    wl = synth.workload("draft_131k_bf16", window=256)
+    say("graph replay", mode)
+    Hq, Hk, D, S, Wn, g = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.sink, wl.window, wl.gamma
+    sh = W.make_shape(Hq, Hk, D, torch.bfloat16, wl.scale)
+    n0, layers = 3000, 2
+    case = synth.draft_case(wl, (n0,))
+    vcases = [synth.verify_case(wl, (n0 + g,), g + 1, layer=l) for l in range(layers)]
+    draft_cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=g, seed=wl.seed, interleaved=True)
+    ring = RingCache(1, Hk, D, S, Wn, torch.bfloat16, headroom=g - 1)
+    W.ring_append(sh, ring.desc, case.k_ctx[:, :n0].contiguous().to(DEV), case.v_ctx[:, :n0].contiguous().to(DEV),
+                  [0])
+    # each target layer: the context (n0 + g tokens) already cached, then g + 1 new tokens
+    vkeys = [torch.cat([case.k_ctx[:, :n0], case.k_new[:, :, 0].transpose(0, 1)], dim=1) for _ in range(layers)]
+    vvals = [torch.cat([case.v_ctx[:, :n0], case.v_new[:, :, 0].transpose(0, 1)], dim=1) for _ in range(layers)]
+    vcache = [PagedCache(vkeys[l], vvals[l], [n0 + g], extra=g + 1, seed=wl.seed + 7 + l, interleaved=True)
+              for l in range(layers)]
+    q = case.q.contiguous().to(DEV)
+    kn, vn = case.k_new.contiguous().to(DEV), case.v_new.contiguous().to(DEV)
+    qv = [c.q.contiguous().to(DEV) for c in vcases]
+    knv = [c.k_new.contiguous().to(DEV) for c in vcases]
+    vnv = [c.v_new.contiguous().to(DEV) for c in vcases]
+    R = g - 1
+    lens_d = [n0 + g]
+    ws_d = W.workspace(W.draft_workspace_bytes(mode, sh, lens_d, 0, S, Wn, R), DEV)
+    ws_v = W.workspace(W.verify_workspace_bytes(sh, g + 1, [n0 + 2 * g + 1], 0), DEV)
+    out_d = torch.zeros((g, 1, Hq, D), dtype=torch.float32, device=DEV)
+    out_v = torch.zeros((layers, 1, (g + 1) * Hq, D), dtype=torch.float32, device=DEV)
+
+    def step():
+        for j in range(g):
+            kw = dict(paged=draft_cache.desc) if mode == O.FULL else dict(ring=ring.desc)
+            parts = W.draft_attn_append(mode | W.DRAFT_FAST_PV, sh, q[j], kn[j], vn[j], [n0 + j + 1], ws_d, **kw)
+            W.combine(parts, out_d[j])
+        for l in range(layers):
+            parts = W.verify_attn_append(sh, qv[l], g + 1, vcache[l].desc, knv[l], vnv[l], [n0 + 2 * g + 1], ws_v)
+            W.combine(parts, out_v[l])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                     # eager (appends are idempotent: the same tokens at the same positions)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref_d, ref_v = out_d.clone(), out_v.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out_d.zero_()
+        out_v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_d, ref_d) and torch.equal(out_v, ref_v), rep
+    del graph
+    # the eager step against the oracle: the last draft step, and the last verify layer
+    dt = "bf16"
+    kb, vb = host_array(case.k_ctx, dt)[0], host_array(case.v_ctx, dt)[0]
+    nk, nvv = host_array(case.k_new, dt)[:, 0, 0], host_array(case.v_new, dt)[:, 0, 0]
+    sk = O.ConcatKV(O.LogicalKV(kb, dt, n0), O.LogicalKV(nk, dt))
+    sv = O.ConcatKV(O.LogicalKV(vb, dt, n0), O.LogicalKV(nvv, dt))
+    qf = O.to_f64(host_array(case.q[g - 1], dt), dt)[0]
+    o_ref, _ = O.draft_attention(qf, sk, sv, n0 + g, mode, S, Wn, wl.scale)
+    assert max_err(ref_d[g - 1, 0], o_ref) <= TOL["bf16"]
+    vc = vcases[layers - 1]
+    vk = O.ConcatKV(sk, O.LogicalKV(host_array(vc.k_new, dt)[0], dt))
+    vv = O.ConcatKV(sv, O.LogicalKV(host_array(vc.v_new, dt)[0], dt))
+    o_ref, _ = O.verify_attention(O.to_f64(host_array(vc.q, dt)[0], dt), vk, vv, n0 + 2 * g + 1, wl.scale)
+    assert max_err(ref_v[layers - 1, 0], o_ref.reshape((g + 1) * Hq, D)) <= TOL["bf16"]
