@@ -317,34 +317,47 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
   }
 }
 
+// One row tile of one wave in the two-team kernel: the queries of the NQ
+// quarters of D the wave covers (quarters q0 .. q0 + NQ - 1), the row tile's
+// softmax state and the wave's accumulators (32 rows x 32 d per quarter half).
+template <int NQ>
+struct TeamRowTile {
+  u32x4 q[NQ][kVKS];
+  f32x16 O[NQ][2];
+  float M, l;
+  int row0, row_last, q0;
+};
+
 // Two or three row tiles (33..96 packed rows) on two teams of 4 waves, 512
 // threads.  With all row tiles in one wave the per-tile chain of LDS stages,
 // barriers, MFMA and softmax has nothing to hide behind at one wave per SIMD;
 // here team 0 loads K and V exactly as the one-row-tile kernel, stages both in
-// LDS and computes row tile 0 of tile t, while team 1 computes the other R1
-// row tiles (1, or 2 and 3) of tile t - 1 from those stages: every SIMD runs
-// one wave of each team, and HBM is read once.
-//   R1 = 1: one barrier per tile step.  The K/V stages rotate over three
-//   buffers and each team's score exchange over two; neither team can pass a
-//   step's barrier before the other reaches it, so team 0 rewrites a stage only
-//   after team 1 has passed the barrier that follows its last read of it
-//   (160 KiB of LDS, the per-workgroup limit).
-//   R1 = 2: team 1's exchange is twice as large, so the stages use two buffers
-//   and the exchanges one, with a second barrier per tile step after the
-//   softmax and PV (112 KiB of LDS).
+// LDS and computes row tile 0 of tile t, each wave over its quarter of D, while
+// team 1 computes the other row tiles of tile t - 1 from those stages: every
+// SIMD runs one wave of each team, and HBM is read once.
+//   R1 = 1: team 1's waves split row tile 1's D in quarters, like team 0.
+//   R1 = 2: team 1's waves form two pairs, one per row tile (1 and 2); each wave
+//   covers half of D, so it contracts twice the keys' width per row tile but
+//   runs one row tile's softmax instead of two, and sums 2 partial scores
+//   instead of 4.  Both waves of a pair add the same two partials (addition is
+//   commutative), so they hold identical scores and weights.
+// One barrier per tile step: the K/V stages rotate over three buffers and each
+// team's score exchange over two; neither team can pass a step's barrier
+// before the other reaches it, so team 0 rewrites a stage only after team 1
+// has passed the barrier that follows its last read of it (160 KiB of LDS, the
+// per-workgroup limit).
 template <int G, int R1>
 __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs a) {
   static_assert(R1 == 1 || R1 == 2, "team 1 computes one or two row tiles");
   constexpr int ROWB = kVD * 2;
   constexpr float TAU = 8.0f;
-  constexpr int NB = R1 == 1 ? 3 : 2;          // K/V stage buffers
-  constexpr int NP = R1 == 1 ? 2 : 1;          // score-exchange buffers per team
-  constexpr int kExch = 4 * 4 * 64 * 4;        // floats of one row tile's exchange
+  constexpr int NB = 3;                        // K/V stage buffers
+  constexpr int NP = 2;                        // score-exchange buffers per team
+  constexpr int kPart = 4 * 64 * 4;            // floats of one wave's partial S^T (16 per lane)
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_stage[NB][4 * kVStage];   // [tile % NB][wave quarter]
-  __shared__ __attribute__((aligned(16))) u32x4 v_stage[NB][4][4][64];        // [tile % NB][wave][piece][lane]
-  __shared__ __attribute__((aligned(16))) float sc0_lds[NP][kExch];           // team 0: [tile % NP]
-  __shared__ __attribute__((aligned(16))) float sc1_lds[NP][R1 * kExch];      // team 1: [tile % NP][row tile]
+  __shared__ __attribute__((aligned(16))) uint8_t k_stage[NB][4 * kVStage];   // [tile % NB][quarter]
+  __shared__ __attribute__((aligned(16))) u32x4 v_stage[NB][4][4][64];        // [tile % NB][quarter][piece][lane]
+  __shared__ __attribute__((aligned(16))) float sc_lds[2][NP][4 * kPart];     // [team][tile % NP][wave partial]
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -370,64 +383,69 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
   const float c = a.scale_log2;
   const int all_last = min(n - tq, t_end - 1);
 
-  // One row tile's queries (this wave's quarter of D), softmax state and accumulators.
-  struct RowTile {
-    u32x4 q[kVKS];
-    f32x16 O[2];
-    float M, l;
-    int row0, row_last;
-  };
-  auto init_tile = [&](RowTile& rt, int r) {
+  auto init_tile = [&](auto& rt, int r, int q0) {
+    constexpr int NQ = sizeof(rt.q) / sizeof(rt.q[0]);
     rt.row0 = 32 * r;
+    rt.q0 = q0;
     const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
     const int j = rt.row0 + c32;
     const int i = j / G, g = j % G;
     const int64_t qrow = ((int64_t)b * tq + i) * Hq + (int64_t)h * G + g;
 #pragma unroll
-    for (int s = 0; s < kVKS; ++s) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (j < rows) x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + wave * (kVQ * 2) + (2 * s + kh) * 16);
-      rt.q[s] = x;
-    }
+    for (int hq = 0; hq < NQ; ++hq)
 #pragma unroll
-    for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(rt.q[s]));
+      for (int s = 0; s < kVKS; ++s) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (j < rows)
+          x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + (q0 + hq) * (kVQ * 2) + (2 * s + kh) * 16);
+        rt.q[hq][s] = x;
+      }
+#pragma unroll
+    for (int hq = 0; hq < NQ; ++hq)
+#pragma unroll
+      for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(rt.q[hq][s]));
     rt.row_last = min(n - tq + j / G, t_end - 1);
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int hq = 0; hq < NQ; ++hq)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) rt.O[e][x] = 0.f;
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) rt.O[hq][e][x] = 0.f;
     rt.M = kNegInf;
     rt.l = 0.f;
   };
 
-  // partial S^T of this wave's quarter of D for one row tile, into an exchange buffer
-  auto qk_exchange = [&](const uint8_t* kst, const RowTile& rt, float* sc) {
+  // partial S^T of one row tile over the wave's quarters of D (K from the stage of one tile)
+  auto qk_partial = [&](const uint8_t* kstage, const auto& rt) {
+    constexpr int NQ = sizeof(rt.q) / sizeof(rt.q[0]);
     f32x16 sacc;
 #pragma unroll
     for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
 #pragma unroll
-    for (int s = 0; s < kVKS; ++s) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + vpiece(c32, 2 * s + kh) * 16);
-      sacc = mfma32(ka, rt.q[s], sacc);
+    for (int hq = 0; hq < NQ; ++hq) {
+      const uint8_t* kst = kstage + (rt.q0 + hq) * kVStage;
+#pragma unroll
+      for (int s = 0; s < kVKS; ++s) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + vpiece(c32, 2 * s + kh) * 16);
+        sacc = mfma32(ka, rt.q[hq][s], sacc);
+      }
     }
+    return sacc;
+  };
+  auto store_partial = [&](const f32x16& sacc, float* part) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 w4 = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
-      *reinterpret_cast<f32x4*>(sc + ((wave * 4 + q) * 64 + lane) * 4) = w4;
+      *reinterpret_cast<f32x4*>(part + (q * 64 + lane) * 4) = w4;
     }
   };
-  auto read_scores = [&](const float* sc, float (&s2)[16]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 x = *reinterpret_cast<const f32x4*>(sc + (q * 64 + lane) * 4);
-#pragma unroll
-      for (int w = 1; w < 4; ++w) x += *reinterpret_cast<const f32x4*>(sc + ((w * 4 + q) * 64 + lane) * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s2[4 * q + e] = x[e];
-    }
+  auto load_partial = [&](const float* part, int q) {
+    return *reinterpret_cast<const f32x4*>(part + (q * 64 + lane) * 4);
   };
-  // mask, lazy maximum, bf16 weights and O += P V for the tile starting at key t0
-  auto softmax_pv = [&](int t0, float (&s2)[16], const uint32_t (&vv)[2][8], RowTile& rt) {
+  // mask, lazy maximum, bf16 weights and O += P V for the tile starting at key t0;
+  // vv[hq]: V dwords of the wave's quarter q0 + hq (key pairs regrouped here)
+  auto softmax_pv = [&](int t0, float (&s2)[16], const auto& vv, auto& rt) {
+    constexpr int NQ = sizeof(rt.q) / sizeof(rt.q[0]);
     if (t0 + kVTile - 1 > all_last) {
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
@@ -447,8 +465,11 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const float ar = __shfl(alpha, 8 * (x >> 2) + 4 * kh + (x & 3));
-        rt.O[0][x] *= ar;
-        rt.O[1][x] *= ar;
+#pragma unroll
+        for (int hq = 0; hq < NQ; ++hq) {
+          rt.O[hq][0][x] *= ar;
+          rt.O[hq][1][x] *= ar;
+        }
       }
     }
     const float negM = rt.M == kNegInf ? 0.f : -rt.M;
@@ -464,17 +485,21 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 pa = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        u32x4 vb;
+      for (int hq = 0; hq < NQ; ++hq)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          vb[q] = __builtin_amdgcn_perm(vv[ks][2 * q + 1], vv[ks][2 * q], e ? 0x07060302u : 0x05040100u);
-        rt.O[e] = mfma32(pa, vb, rt.O[e]);
-      }
+        for (int e = 0; e < 2; ++e) {
+          u32x4 vb;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            vb[q] = __builtin_amdgcn_perm(vv[hq][ks][2 * q + 1], vv[hq][ks][2 * q], e ? 0x07060302u : 0x05040100u);
+          rt.O[hq][e] = mfma32(pa, vb, rt.O[hq][e]);
+        }
     }
   };
-  // normalise and write this wave's quarter of the row tile's live rows
-  auto finish = [&](const RowTile& rt) {
+  // normalise and write the wave's quarters of the row tile's live rows; the lse
+  // comes from the wave that covers quarter 0
+  auto finish = [&](const auto& rt) {
+    constexpr int NQ = sizeof(rt.q) / sizeof(rt.q[0]);
     const float l_row = halves_sum(rt.l);
     const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
@@ -485,24 +510,38 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       if (row < rows) {
         const int i = row / G, g = row % G;
         const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
-        float2 w2;
-        w2.x = rt.O[0][x] * inv;
-        w2.y = rt.O[1][x] * inv;
-        *reinterpret_cast<float2*>(a.part_o + orow * kVD + wave * kVQ + 2 * c32) = w2;
+#pragma unroll
+        for (int hq = 0; hq < NQ; ++hq) {
+          float2 w2;
+          w2.x = rt.O[hq][0][x] * inv;
+          w2.y = rt.O[hq][1][x] * inv;
+          *reinterpret_cast<float2*>(a.part_o + orow * kVD + (rt.q0 + hq) * kVQ + 2 * c32) = w2;
+        }
       }
     }
-    if (wave == 0 && lane < 32 && rt.row0 + lane < rows) {
+    if (rt.q0 == 0 && lane < 32 && rt.row0 + lane < rows) {
       const int row = rt.row0 + lane;
       const int i = row / G, g = row % G;
       const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
       a.part_lse[orow] = l_row > 0.f ? (rt.M + __log2f(l_row)) * kLn2 : kNegInf;
     }
   };
+  // S of a row tile whose D quarters are split over the 4 waves: the sum of the 4 partials
+  auto sum4 = [&](const float* parts, float (&s2)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 x = load_partial(parts, q);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) x += load_partial(parts + w * kPart, q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s2[4 * q + e] = x[e];
+    }
+  };
 
   if (team == 0) {
     // ---- loader team: the one-row-tile kernel's loads and ring, plus the stages for team 1
-    RowTile rt0;
-    init_tile(rt0, 0);
+    TeamRowTile<1> rt0;
+    init_tile(rt0, 0, wave);
     auto tile_runs = [&](int it, int64_t (&run)[2]) {
       const int t0 = t_begin + min(it, ntiles - 1) * kVTile;
 #pragma unroll
@@ -513,7 +552,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
     };
     constexpr int kRing = 3;
     u32x4 kreg[kRing][kVLoads];
-    uint32_t vreg[kRing][2][8];
+    uint32_t vreg[kRing][1][2][8];
     int64_t run_next[2];
     const uint32_t k_off0 = (uint32_t)((lane >> 3) * ROWB + (lane & 7) * 16);
     const uint8_t* kbase_hi = kbase + 8 * ROWB;
@@ -526,7 +565,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
-          vreg[slot][ks][jj] =
+          vreg[slot][0][ks][jj] =
               load_nt<uint32_t>(vbase + run[ks] + (8 * (jj >> 2)) * ROWB, v_off + (jj & 3) * ROWB);
     };
     auto body = [&](int it, int slot) {
@@ -543,20 +582,19 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const u32x4 w = {vreg[slot][q >> 1][4 * (q & 1)], vreg[slot][q >> 1][4 * (q & 1) + 1],
-                         vreg[slot][q >> 1][4 * (q & 1) + 2], vreg[slot][q >> 1][4 * (q & 1) + 3]};
+        const u32x4 w = {vreg[slot][0][q >> 1][4 * (q & 1)], vreg[slot][0][q >> 1][4 * (q & 1) + 1],
+                         vreg[slot][0][q >> 1][4 * (q & 1) + 2], vreg[slot][0][q >> 1][4 * (q & 1) + 3]};
         v_stage[it % NB][wave][q][lane] = w;
       }
-      float* sc = sc0_lds[it % NP];
-      qk_exchange(kst, rt0, sc);
+      float* parts = sc_lds[0][it % NP];
+      store_partial(qk_partial(k_stage[it % NB], rt0), parts + wave * kPart);
       __syncthreads();
       float s2[16];
-      read_scores(sc, s2);
+      sum4(parts, s2);
       __builtin_amdgcn_sched_barrier(0);
       tile_runs(it + kRing, run_next);
       __builtin_amdgcn_sched_barrier(0);
       softmax_pv(t0, s2, vreg[slot], rt0);
-      if constexpr (R1 == 2) __syncthreads();
     };
     if (ntiles > 0) {
 #pragma unroll
@@ -576,42 +614,68 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       if (it < ntiles) body(it, 0);
       if (it + 1 < ntiles) body(it + 1, 1);
     }
-    // team 1 still computes the last tile: its barrier(s)
+    // team 1 still computes the last tile: its barrier
     __syncthreads();
-    if constexpr (R1 == 2) __syncthreads();
     finish(rt0);
-  } else {
-    // ---- team 1: row tiles 1..R1 of tile it - 1, from team 0's stages
-    RowTile rt1[R1];
-#pragma unroll
-    for (int r = 0; r < R1; ++r) init_tile(rt1[r], 1 + r);
+  } else if constexpr (R1 == 1) {
+    // ---- team 1: row tile 1 of tile it - 1, each wave over its quarter of D
+    TeamRowTile<1> rt;
+    init_tile(rt, 1, wave);
     for (int it = 0; it <= ntiles; ++it) {
       const int t = it - 1;
-      float* sc = sc1_lds[it % NP];
-      if (t >= 0) {
-#pragma unroll
-        for (int r = 0; r < R1; ++r) qk_exchange(k_stage[t % NB] + wave * kVStage, rt1[r], sc + r * kExch);
-      }
+      float* parts = sc_lds[1][it % NP];
+      if (t >= 0) store_partial(qk_partial(k_stage[t % NB], rt), parts + wave * kPart);
       __syncthreads();
       if (t >= 0) {
-        uint32_t vv[2][8];
+        float s2[16];
+        sum4(parts, s2);
+        uint32_t vv[1][2][8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x4 w = v_stage[t % NB][wave][q][lane];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vv[q >> 1][4 * (q & 1) + e] = w[e];
+          for (int e = 0; e < 4; ++e) vv[0][q >> 1][4 * (q & 1) + e] = w[e];
         }
-#pragma unroll
-        for (int r = 0; r < R1; ++r) {
-          float s2[16];
-          read_scores(sc + r * kExch, s2);
-          softmax_pv(t_begin + t * kVTile, s2, vv, rt1[r]);
-        }
+        softmax_pv(t_begin + t * kVTile, s2, vv, rt);
       }
-      if constexpr (R1 == 2) __syncthreads();
     }
+    finish(rt);
+  } else {
+    // ---- team 1: row tiles 1 and 2 of tile it - 1; waves 2r and 2r + 1 take row tile
+    // 1 + r, each over one half of D (quarters 2 dh and 2 dh + 1)
+    const int r = wave >> 1, dh = wave & 1;
+    TeamRowTile<2> rt;
+    init_tile(rt, 1 + r, 2 * dh);
+    for (int it = 0; it <= ntiles; ++it) {
+      const int t = it - 1;
+      float* parts = sc_lds[1][it % NP] + 2 * r * kPart;      // the pair's two partials
+      f32x16 own;
+      if (t >= 0) {
+        own = qk_partial(k_stage[t % NB], rt);
+        store_partial(own, parts + dh * kPart);
+      }
+      __syncthreads();
+      if (t >= 0) {
+        float s2[16];
 #pragma unroll
-    for (int r = 0; r < R1; ++r) finish(rt1[r]);
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 other = load_partial(parts + (dh ^ 1) * kPart, q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s2[4 * q + e] = own[4 * q + e] + other[e];
+        }
+        uint32_t vv[2][2][8];
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 w = v_stage[t % NB][2 * dh + hq][q][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vv[hq][q >> 1][4 * (q & 1) + e] = w[e];
+          }
+        softmax_pv(t_begin + t * kVTile, s2, vv, rt);
+      }
+    }
+    finish(rt);
   }
 }
 
