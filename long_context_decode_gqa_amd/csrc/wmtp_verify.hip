@@ -317,15 +317,213 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
   }
 }
 
-// One row tile of one wave in the two-team kernel: the queries of the NQ
-// quarters of D the wave covers (quarters q0 .. q0 + NQ - 1), the row tile's
-// softmax state and the wave's accumulators (32 rows x 32 d per quarter half).
+// One row tile of one wave in the two-team kernel: the queries of the
+// NQ quarters of D the wave covers (quarters q0 .. q0 + NQ - 1), the row
+// tile's softmax state and the wave's accumulators (32 rows x 32 d per
+// quarter half).
 template <int NQ>
-struct TeamRowTile {
+struct RowTile {
   u32x4 q[NQ][kVKS];
   f32x16 O[NQ][2];
   float M, l;
   int row0, row_last, q0;
+};
+
+// What a wave of a two-team work item needs to know about it.
+struct WorkItem {
+  const SplitArgs* a;
+  int lane, c32, kh;
+  int b, h, sg, n, tq, rows, t_end, all_last;
+  float c;                      // score scale in log2 units
+};
+
+constexpr int kPart = 4 * 64 * 4;   // floats of one wave's partial S^T tile (16 per lane)
+
+// Queries of row tile r (packed rows 32 r ..), quarters q0 .. q0 + NQ - 1, and a cleared state.
+template <int G, int NQ>
+__device__ __forceinline__ void init_row_tile(const WorkItem& w, RowTile<NQ>& rt, int r, int q0) {
+  constexpr int ROWB = kVD * 2;
+  rt.row0 = 32 * r;
+  rt.q0 = q0;
+  const uint8_t* q8 = static_cast<const uint8_t*>(w.a->q);
+  const int j = rt.row0 + w.c32;
+  const int i = j / G, g = j % G;
+  const int64_t qrow = ((int64_t)w.b * w.tq + i) * w.a->num_q_heads + (int64_t)w.h * G + g;
+#pragma unroll
+  for (int hq = 0; hq < NQ; ++hq)
+#pragma unroll
+    for (int s = 0; s < kVKS; ++s) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (j < w.rows)
+        x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + (q0 + hq) * (kVQ * 2) + (2 * s + w.kh) * 16);
+      rt.q[hq][s] = x;
+    }
+#pragma unroll
+  for (int hq = 0; hq < NQ; ++hq)
+#pragma unroll
+    for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(rt.q[hq][s]));
+  rt.row_last = min(w.n - w.tq + j / G, w.t_end - 1);
+#pragma unroll
+  for (int hq = 0; hq < NQ; ++hq)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) rt.O[hq][e][x] = 0.f;
+  rt.M = kNegInf;
+  rt.l = 0.f;
+}
+
+// Partial S^T of one row tile over the wave's quarters of D, K from one tile's stage.
+template <int NQ>
+__device__ __forceinline__ f32x16 qk_partial(const WorkItem& w, const uint8_t* kstage, const RowTile<NQ>& rt) {
+  f32x16 sacc;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
+#pragma unroll
+  for (int hq = 0; hq < NQ; ++hq) {
+    const uint8_t* kst = kstage + (rt.q0 + hq) * kVStage;
+#pragma unroll
+    for (int s = 0; s < kVKS; ++s) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + vpiece(w.c32, 2 * s + w.kh) * 16);
+      sacc = mfma32(ka, rt.q[hq][s], sacc);
+    }
+  }
+  return sacc;
+}
+
+__device__ __forceinline__ void store_partial(const WorkItem& w, const f32x16& sacc, float* part) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 w4 = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+    *reinterpret_cast<f32x4*>(part + (q * 64 + w.lane) * 4) = w4;
+  }
+}
+
+__device__ __forceinline__ f32x4 load_partial(const WorkItem& w, const float* part, int q) {
+  return *reinterpret_cast<const f32x4*>(part + (q * 64 + w.lane) * 4);
+}
+
+// S of a row tile whose D quarters are split over 4 waves: the sum of their 4 partials, in order.
+__device__ __forceinline__ void sum4_partials(const WorkItem& w, const float* parts, float (&s2)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4 x = load_partial(w, parts, q);
+#pragma unroll
+    for (int k = 1; k < 4; ++k) x += load_partial(w, parts + k * kPart, q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s2[4 * q + e] = x[e];
+  }
+}
+
+// S of a row tile whose D halves are split over a pair of waves: own partial plus the
+// partner's.  Addition is commutative, so both waves of the pair get identical scores.
+__device__ __forceinline__ void sum2_partials(const WorkItem& w, const f32x16& own, const float* other,
+                                              float (&s2)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 x = load_partial(w, other, q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s2[4 * q + e] = own[4 * q + e] + x[e];
+  }
+}
+
+// Mask, lazy maximum, bf16 weights and O += P V for the tile starting at key t0;
+// vv[hq]: V dwords of the wave's quarter q0 + hq (key pairs regrouped here).
+template <int NQ>
+__device__ __forceinline__ void softmax_pv(const WorkItem& w, int t0, float (&s2)[16],
+                                           const uint32_t (&vv)[NQ][2][8], RowTile<NQ>& rt) {
+  constexpr float TAU = 8.0f;
+  if (t0 + kVTile - 1 > w.all_last) {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int key = t0 + 8 * (x >> 2) + 4 * w.kh + (x & 3);
+      s2[x] = key <= rt.row_last ? s2[x] : kNegInf;
+    }
+  }
+  float mx = s2[0];
+#pragma unroll
+  for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s2[x]);
+  mx = halves_max(mx) * w.c;
+  if (__ballot(mx > rt.M + TAU) != 0) {
+    const float mn = fmaxf(rt.M, mx);
+    const float alpha = (rt.M == kNegInf) ? 0.f : fast_exp2(rt.M - mn);
+    rt.M = mn;
+    rt.l *= alpha;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const float ar = __shfl(alpha, 8 * (x >> 2) + 4 * w.kh + (x & 3));
+#pragma unroll
+      for (int hq = 0; hq < NQ; ++hq) {
+        rt.O[hq][0][x] *= ar;
+        rt.O[hq][1][x] *= ar;
+      }
+    }
+  }
+  const float negM = rt.M == kNegInf ? 0.f : -rt.M;
+  uint32_t pk[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float p0 = fast_exp2(fmaf(s2[2 * q], w.c, negM));
+    const float p1 = fast_exp2(fmaf(s2[2 * q + 1], w.c, negM));
+    pk[q] = pack_bf16x2(p0, p1);
+    rt.l = dot2_bf16(pk[q], kBf16One2, rt.l);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const u32x4 pa = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
+#pragma unroll
+    for (int hq = 0; hq < NQ; ++hq)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        u32x4 vb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          vb[q] = __builtin_amdgcn_perm(vv[hq][ks][2 * q + 1], vv[hq][ks][2 * q], e ? 0x07060302u : 0x05040100u);
+        rt.O[hq][e] = mfma32(pa, vb, rt.O[hq][e]);
+      }
+  }
+}
+
+// Normalise and write the wave's quarters of the row tile's live rows; the lse
+// comes from the wave that covers quarter 0.
+template <int G, int NQ>
+__device__ __forceinline__ void finish_row_tile(const WorkItem& w, const RowTile<NQ>& rt) {
+  const SplitArgs& a = *w.a;
+  const int Hq = a.num_q_heads;
+  const float l_row = halves_sum(rt.l);
+  const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const int rl = 8 * (x >> 2) + 4 * w.kh + (x & 3);
+    const float inv = __shfl(inv_row, rl);
+    const int row = rt.row0 + rl;
+    if (row < w.rows) {
+      const int i = row / G, g = row % G;
+      const int64_t orow = (int64_t)w.sg * (w.tq * Hq) + (int64_t)i * Hq + (int64_t)w.h * G + g;
+#pragma unroll
+      for (int hq = 0; hq < NQ; ++hq) {
+        float2 w2;
+        w2.x = rt.O[hq][0][x] * inv;
+        w2.y = rt.O[hq][1][x] * inv;
+        *reinterpret_cast<float2*>(a.part_o + orow * kVD + (rt.q0 + hq) * kVQ + 2 * w.c32) = w2;
+      }
+    }
+  }
+  if (rt.q0 == 0 && w.lane < 32 && rt.row0 + w.lane < w.rows) {
+    const int row = rt.row0 + w.lane;
+    const int i = row / G, g = row % G;
+    const int64_t orow = (int64_t)w.sg * (w.tq * Hq) + (int64_t)i * Hq + (int64_t)w.h * G + g;
+    a.part_lse[orow] = l_row > 0.f ? (rt.M + __log2f(l_row)) * kLn2 : kNegInf;
+  }
+}
+
+// The paged K/V loads of one wave's quarter of D, issued kRing - 1 tiles ahead
+// into a register ring exactly as in the one-row-tile kernel (the two-team
+// kernel's loader team).
+struct QuarterLoader {
+  static constexpr int kRing = 3;
+  u32x4 kreg[kRing][kVLoads];
+  uint32_t vreg[kRing][1][2][8];
 };
 
 // Two or three row tiles (33..96 packed rows) on two teams of 4 waves, 512
@@ -339,8 +537,7 @@ struct TeamRowTile {
 //   R1 = 2: team 1's waves form two pairs, one per row tile (1 and 2); each wave
 //   covers half of D, so it contracts twice the keys' width per row tile but
 //   runs one row tile's softmax instead of two, and sums 2 partial scores
-//   instead of 4.  Both waves of a pair add the same two partials (addition is
-//   commutative), so they hold identical scores and weights.
+//   instead of 4.
 // One barrier per tile step: the K/V stages rotate over three buffers and each
 // team's score exchange over two; neither team can pass a step's barrier
 // before the other reaches it, so team 0 rewrites a stage only after team 1
@@ -350,209 +547,56 @@ template <int G, int R1>
 __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs a) {
   static_assert(R1 == 1 || R1 == 2, "team 1 computes one or two row tiles");
   constexpr int ROWB = kVD * 2;
-  constexpr float TAU = 8.0f;
   constexpr int NB = 3;                        // K/V stage buffers
   constexpr int NP = 2;                        // score-exchange buffers per team
-  constexpr int kPart = 4 * 64 * 4;            // floats of one wave's partial S^T (16 per lane)
 
   __shared__ __attribute__((aligned(16))) uint8_t k_stage[NB][4 * kVStage];   // [tile % NB][quarter]
   __shared__ __attribute__((aligned(16))) u32x4 v_stage[NB][4][4][64];        // [tile % NB][quarter][piece][lane]
   __shared__ __attribute__((aligned(16))) float sc_lds[2][NP][4 * kPart];     // [team][tile % NP][wave partial]
 
-  const int lane = threadIdx.x & 63;
+  WorkItem w;
+  w.a = &a;
+  w.lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int team = wid >> 2, wave = wid & 3;
-  const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, tq = a.t_q;
-  const int rows = tq * G;
-  const int h = blockIdx.x % Hkv;
-  const int sg = blockIdx.x / Hkv;
-  const int b = seq_of_split(a, sg);
-  const int n = a.seq_len[b];
-  const int t_begin = (sg - a.split_base[b]) * a.chunk;
-  const int t_end = min(t_begin + a.chunk, n);
-  const int ntiles = (t_end - t_begin + kVTile - 1) / kVTile;
-  const int last_blk_idx = (t_end - 1) >> 4;
-  if (a.t_new > 0) append_own_rows<false>(a, b, h, n, max(t_begin, n - a.t_new), t_end, kVD * 2);
-  const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
+  const int Hkv = a.num_kv_heads;
+  w.tq = a.t_q;
+  w.rows = w.tq * G;
+  w.h = blockIdx.x % Hkv;
+  w.sg = blockIdx.x / Hkv;
+  w.b = seq_of_split(a, w.sg);
+  w.n = a.seq_len[w.b];
+  const int t_begin = (w.sg - a.split_base[w.b]) * a.chunk;
+  w.t_end = min(t_begin + a.chunk, w.n);
+  const int ntiles = (w.t_end - t_begin + kVTile - 1) / kVTile;
+  const int last_blk_idx = (w.t_end - 1) >> 4;
+  if (a.t_new > 0) append_own_rows<false>(a, w.b, w.h, w.n, max(t_begin, w.n - a.t_new), w.t_end, kVD * 2);
+  const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)w.b * a.bt_stride;
   const int64_t run_bytes = (int64_t)a.run_rows * ROWB;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + wave * (kVQ * 2);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + wave * (kVQ * 2);
-
-  const int c32 = lane & 31;
-  const int kh = lane >> 5;
-  const float c = a.scale_log2;
-  const int all_last = min(n - tq, t_end - 1);
-
-  auto init_tile = [&](auto& rt, int r, int q0) {
-    constexpr int NQ = sizeof(rt.q) / sizeof(rt.q[0]);
-    rt.row0 = 32 * r;
-    rt.q0 = q0;
-    const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
-    const int j = rt.row0 + c32;
-    const int i = j / G, g = j % G;
-    const int64_t qrow = ((int64_t)b * tq + i) * Hq + (int64_t)h * G + g;
-#pragma unroll
-    for (int hq = 0; hq < NQ; ++hq)
-#pragma unroll
-      for (int s = 0; s < kVKS; ++s) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (j < rows)
-          x = *reinterpret_cast<const u32x4*>(q8 + qrow * ROWB + (q0 + hq) * (kVQ * 2) + (2 * s + kh) * 16);
-        rt.q[hq][s] = x;
-      }
-#pragma unroll
-    for (int hq = 0; hq < NQ; ++hq)
-#pragma unroll
-      for (int s = 0; s < kVKS; ++s) asm volatile("" ::"v"(rt.q[hq][s]));
-    rt.row_last = min(n - tq + j / G, t_end - 1);
-#pragma unroll
-    for (int hq = 0; hq < NQ; ++hq)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) rt.O[hq][e][x] = 0.f;
-    rt.M = kNegInf;
-    rt.l = 0.f;
-  };
-
-  // partial S^T of one row tile over the wave's quarters of D (K from the stage of one tile)
-  auto qk_partial = [&](const uint8_t* kstage, const auto& rt) {
-    constexpr int NQ = sizeof(rt.q) / sizeof(rt.q[0]);
-    f32x16 sacc;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
-#pragma unroll
-    for (int hq = 0; hq < NQ; ++hq) {
-      const uint8_t* kst = kstage + (rt.q0 + hq) * kVStage;
-#pragma unroll
-      for (int s = 0; s < kVKS; ++s) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + vpiece(c32, 2 * s + kh) * 16);
-        sacc = mfma32(ka, rt.q[hq][s], sacc);
-      }
-    }
-    return sacc;
-  };
-  auto store_partial = [&](const f32x16& sacc, float* part) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 w4 = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
-      *reinterpret_cast<f32x4*>(part + (q * 64 + lane) * 4) = w4;
-    }
-  };
-  auto load_partial = [&](const float* part, int q) {
-    return *reinterpret_cast<const f32x4*>(part + (q * 64 + lane) * 4);
-  };
-  // mask, lazy maximum, bf16 weights and O += P V for the tile starting at key t0;
-  // vv[hq]: V dwords of the wave's quarter q0 + hq (key pairs regrouped here)
-  auto softmax_pv = [&](int t0, float (&s2)[16], const auto& vv, auto& rt) {
-    constexpr int NQ = sizeof(rt.q) / sizeof(rt.q[0]);
-    if (t0 + kVTile - 1 > all_last) {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int key = t0 + 8 * (x >> 2) + 4 * kh + (x & 3);
-        s2[x] = key <= rt.row_last ? s2[x] : kNegInf;
-      }
-    }
-    float mx = s2[0];
-#pragma unroll
-    for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s2[x]);
-    mx = halves_max(mx) * c;
-    if (__ballot(mx > rt.M + TAU) != 0) {
-      const float mn = fmaxf(rt.M, mx);
-      const float alpha = (rt.M == kNegInf) ? 0.f : fast_exp2(rt.M - mn);
-      rt.M = mn;
-      rt.l *= alpha;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float ar = __shfl(alpha, 8 * (x >> 2) + 4 * kh + (x & 3));
-#pragma unroll
-        for (int hq = 0; hq < NQ; ++hq) {
-          rt.O[hq][0][x] *= ar;
-          rt.O[hq][1][x] *= ar;
-        }
-      }
-    }
-    const float negM = rt.M == kNegInf ? 0.f : -rt.M;
-    uint32_t pk[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float p0 = fast_exp2(fmaf(s2[2 * q], c, negM));
-      const float p1 = fast_exp2(fmaf(s2[2 * q + 1], c, negM));
-      pk[q] = pack_bf16x2(p0, p1);
-      rt.l = dot2_bf16(pk[q], kBf16One2, rt.l);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 pa = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
-#pragma unroll
-      for (int hq = 0; hq < NQ; ++hq)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          u32x4 vb;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            vb[q] = __builtin_amdgcn_perm(vv[hq][ks][2 * q + 1], vv[hq][ks][2 * q], e ? 0x07060302u : 0x05040100u);
-          rt.O[hq][e] = mfma32(pa, vb, rt.O[hq][e]);
-        }
-    }
-  };
-  // normalise and write the wave's quarters of the row tile's live rows; the lse
-  // comes from the wave that covers quarter 0
-  auto finish = [&](const auto& rt) {
-    constexpr int NQ = sizeof(rt.q) / sizeof(rt.q[0]);
-    const float l_row = halves_sum(rt.l);
-    const float inv_row = l_row > 0.f ? 1.f / l_row : 0.f;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int rl = 8 * (x >> 2) + 4 * kh + (x & 3);
-      const float inv = __shfl(inv_row, rl);
-      const int row = rt.row0 + rl;
-      if (row < rows) {
-        const int i = row / G, g = row % G;
-        const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
-#pragma unroll
-        for (int hq = 0; hq < NQ; ++hq) {
-          float2 w2;
-          w2.x = rt.O[hq][0][x] * inv;
-          w2.y = rt.O[hq][1][x] * inv;
-          *reinterpret_cast<float2*>(a.part_o + orow * kVD + (rt.q0 + hq) * kVQ + 2 * c32) = w2;
-        }
-      }
-    }
-    if (rt.q0 == 0 && lane < 32 && rt.row0 + lane < rows) {
-      const int row = rt.row0 + lane;
-      const int i = row / G, g = row % G;
-      const int64_t orow = (int64_t)sg * (tq * Hq) + (int64_t)i * Hq + (int64_t)h * G + g;
-      a.part_lse[orow] = l_row > 0.f ? (rt.M + __log2f(l_row)) * kLn2 : kNegInf;
-    }
-  };
-  // S of a row tile whose D quarters are split over the 4 waves: the sum of the 4 partials
-  auto sum4 = [&](const float* parts, float (&s2)[16]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 x = load_partial(parts, q);
-#pragma unroll
-      for (int w = 1; w < 4; ++w) x += load_partial(parts + w * kPart, q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s2[4 * q + e] = x[e];
-    }
-  };
+  const int lane = w.lane;
+  w.c32 = lane & 31;
+  w.kh = lane >> 5;
+  w.c = a.scale_log2;
+  w.all_last = min(w.n - w.tq, w.t_end - 1);
+  const int c32 = w.c32, kh = w.kh;
 
   if (team == 0) {
     // ---- loader team: the one-row-tile kernel's loads and ring, plus the stages for team 1
-    TeamRowTile<1> rt0;
-    init_tile(rt0, 0, wave);
+    RowTile<1> rt0;
+    init_row_tile<G>(w, rt0, 0, wave);
     auto tile_runs = [&](int it, int64_t (&run)[2]) {
       const int t0 = t_begin + min(it, ntiles - 1) * kVTile;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int bi = min((t0 >> 4) + j, last_blk_idx);
-        run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), h, Hkv, run_bytes);
+        run[j] = paged_block_run(paged_block_uniform(bt_row, (int64_t)bi * kBlock, a.max_block), w.h, Hkv,
+                                 run_bytes);
       }
     };
-    constexpr int kRing = 3;
-    u32x4 kreg[kRing][kVLoads];
-    uint32_t vreg[kRing][1][2][8];
+    constexpr int kRing = QuarterLoader::kRing;
+    QuarterLoader ld;
     int64_t run_next[2];
     const uint32_t k_off0 = (uint32_t)((lane >> 3) * ROWB + (lane & 7) * 16);
     const uint8_t* kbase_hi = kbase + 8 * ROWB;
@@ -560,12 +604,12 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
     auto issue = [&](int slot, const int64_t (&run)[2], uint32_t k_off, uint32_t v_off) {
 #pragma unroll
       for (int l = 0; l < kVLoads; ++l)
-        kreg[slot][l] = load_nt<u32x4>(((l & 1) ? kbase_hi : kbase) + run[l >> 1], k_off);
+        ld.kreg[slot][l] = load_nt<u32x4>(((l & 1) ? kbase_hi : kbase) + run[l >> 1], k_off);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
-          vreg[slot][0][ks][jj] =
+          ld.vreg[slot][0][ks][jj] =
               load_nt<uint32_t>(vbase + run[ks] + (8 * (jj >> 2)) * ROWB, v_off + (jj & 3) * ROWB);
     };
     auto body = [&](int it, int slot) {
@@ -578,23 +622,23 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
 #pragma unroll
       for (int l = 0; l < kVLoads; ++l) {
         const int P = 64 * l + lane;
-        *reinterpret_cast<u32x4*>(kst + vpiece(P / kVNQ, P % kVNQ) * 16) = kreg[slot][l];
+        *reinterpret_cast<u32x4*>(kst + vpiece(P / kVNQ, P % kVNQ) * 16) = ld.kreg[slot][l];
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const u32x4 w = {vreg[slot][0][q >> 1][4 * (q & 1)], vreg[slot][0][q >> 1][4 * (q & 1) + 1],
-                         vreg[slot][0][q >> 1][4 * (q & 1) + 2], vreg[slot][0][q >> 1][4 * (q & 1) + 3]};
-        v_stage[it % NB][wave][q][lane] = w;
+        const u32x4 v4 = {ld.vreg[slot][0][q >> 1][4 * (q & 1)], ld.vreg[slot][0][q >> 1][4 * (q & 1) + 1],
+                          ld.vreg[slot][0][q >> 1][4 * (q & 1) + 2], ld.vreg[slot][0][q >> 1][4 * (q & 1) + 3]};
+        v_stage[it % NB][wave][q][lane] = v4;
       }
       float* parts = sc_lds[0][it % NP];
-      store_partial(qk_partial(k_stage[it % NB], rt0), parts + wave * kPart);
+      store_partial(w, qk_partial(w, k_stage[it % NB], rt0), parts + wave * kPart);
       __syncthreads();
       float s2[16];
-      sum4(parts, s2);
+      sum4_partials(w, parts, s2);
       __builtin_amdgcn_sched_barrier(0);
       tile_runs(it + kRing, run_next);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_pv(t0, s2, vreg[slot], rt0);
+      softmax_pv(w, t0, s2, ld.vreg[slot], rt0);
     };
     if (ntiles > 0) {
 #pragma unroll
@@ -616,66 +660,61 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
     }
     // team 1 still computes the last tile: its barrier
     __syncthreads();
-    finish(rt0);
+    finish_row_tile<G>(w, rt0);
   } else if constexpr (R1 == 1) {
     // ---- team 1: row tile 1 of tile it - 1, each wave over its quarter of D
-    TeamRowTile<1> rt;
-    init_tile(rt, 1, wave);
+    RowTile<1> rt;
+    init_row_tile<G>(w, rt, 1, wave);
     for (int it = 0; it <= ntiles; ++it) {
       const int t = it - 1;
       float* parts = sc_lds[1][it % NP];
-      if (t >= 0) store_partial(qk_partial(k_stage[t % NB], rt), parts + wave * kPart);
+      if (t >= 0) store_partial(w, qk_partial(w, k_stage[t % NB], rt), parts + wave * kPart);
       __syncthreads();
       if (t >= 0) {
         float s2[16];
-        sum4(parts, s2);
+        sum4_partials(w, parts, s2);
         uint32_t vv[1][2][8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const u32x4 w = v_stage[t % NB][wave][q][lane];
+          const u32x4 v4 = v_stage[t % NB][wave][q][lane];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vv[0][q >> 1][4 * (q & 1) + e] = w[e];
+          for (int e = 0; e < 4; ++e) vv[0][q >> 1][4 * (q & 1) + e] = v4[e];
         }
-        softmax_pv(t_begin + t * kVTile, s2, vv, rt);
+        softmax_pv(w, t_begin + t * kVTile, s2, vv, rt);
       }
     }
-    finish(rt);
+    finish_row_tile<G>(w, rt);
   } else {
     // ---- team 1: row tiles 1 and 2 of tile it - 1; waves 2r and 2r + 1 take row tile
     // 1 + r, each over one half of D (quarters 2 dh and 2 dh + 1)
     const int r = wave >> 1, dh = wave & 1;
-    TeamRowTile<2> rt;
-    init_tile(rt, 1 + r, 2 * dh);
+    RowTile<2> rt;
+    init_row_tile<G>(w, rt, 1 + r, 2 * dh);
     for (int it = 0; it <= ntiles; ++it) {
       const int t = it - 1;
       float* parts = sc_lds[1][it % NP] + 2 * r * kPart;      // the pair's two partials
       f32x16 own;
       if (t >= 0) {
-        own = qk_partial(k_stage[t % NB], rt);
-        store_partial(own, parts + dh * kPart);
+        own = qk_partial(w, k_stage[t % NB], rt);
+        store_partial(w, own, parts + dh * kPart);
       }
       __syncthreads();
       if (t >= 0) {
         float s2[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 other = load_partial(parts + (dh ^ 1) * kPart, q);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s2[4 * q + e] = own[4 * q + e] + other[e];
-        }
+        sum2_partials(w, own, parts + (dh ^ 1) * kPart, s2);
         uint32_t vv[2][2][8];
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const u32x4 w = v_stage[t % NB][2 * dh + hq][q][lane];
+            const u32x4 v4 = v_stage[t % NB][2 * dh + hq][q][lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vv[hq][q >> 1][4 * (q & 1) + e] = w[e];
+            for (int e = 0; e < 4; ++e) vv[hq][q >> 1][4 * (q & 1) + e] = v4[e];
           }
-        softmax_pv(t_begin + t * kVTile, s2, vv, rt);
+        softmax_pv(w, t_begin + t * kVTile, s2, vv, rt);
       }
     }
-    finish(rt);
+    finish_row_tile<G>(w, rt);
   }
 }
 
