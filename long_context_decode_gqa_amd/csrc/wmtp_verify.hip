@@ -119,11 +119,13 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
   const int row_last = min(n - tq + c32 / G, t_end - 1);
   const int all_last = min(n - tq, t_end - 1);
 
-  // Byte offsets of the two (block, head) runs of 16 keys covering tile `it`
-  // (clamped to the split's last tile and block).  The block ids come in through
-  // scalar loads one tile before the loads that use them.
+  // Byte offsets of the two (block, head) runs of 16 keys covering tile `it`.
+  // The ring's prefetches past the split's end (never consumed) read the
+  // sequence's first tile instead: every work item of the sequence and head
+  // asks for the same bytes, which the caches then serve.  The block ids come
+  // in through scalar loads one tile before the loads that use them.
   auto tile_runs = [&](int it, int64_t (&run)[2]) {
-    const int t0 = t_begin + min(it, ntiles - 1) * kVTile;
+    const int t0 = it < ntiles ? t_begin + it * kVTile : 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int bi = min((t0 >> 4) + j, last_blk_idx);
@@ -145,8 +147,8 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
   // + 4 kh + jj % 4 (block run ks); the lane holds d = 2 c32, 2 c32 + 1 of the
   // wave's quarter (one dword), at lane offset v_off + (8 (jj / 4) + jj % 4) rows.
   // K and V are read once per launch: non-temporal loads.
-  // Tiles past the end re-load the last tile (never consumed), so every body
-  // issues the same loads and the loop has no load-carrying branch.  The two
+  // Tiles past the end load the sequence's first tile (never consumed), so every
+  // body issues the same loads and the loop has no load-carrying branch.  The two
   // 32-bit lane offsets are passed opaque, so they are not widened and hoisted
   // but feed the "uniform base + 32-bit offset" load form directly.
   const uint32_t k_off0 = (uint32_t)((lane >> 3) * ROWB + (lane & 7) * 16);
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
     RowTile<1> rt0;
     init_row_tile<G>(w, rt0, 0, wave);
     auto tile_runs = [&](int it, int64_t (&run)[2]) {
-      const int t0 = t_begin + min(it, ntiles - 1) * kVTile;
+      const int t0 = it < ntiles ? t_begin + it * kVTile : 0;     // past the end: the sequence's first tile
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int bi = min((t0 >> 4) + j, last_blk_idx);
