@@ -186,10 +186,12 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
   uint2 vreg[kRing][NV];
   int tag[kRing] = {};
 
-  // Loads of tile `it`, clamped to the last tile so every body issues the same
-  // number of loads.  `ln` is this lane's index.
+  // Loads of tile `it`; every body issues the same number of loads.  The ring's
+  // prefetches past the split's end (full mode, never consumed) read the
+  // sequence's first tile, the same bytes for every work item of the sequence
+  // and head, which the caches then serve.  `ln` is this lane's index.
   auto issue = [&](int it, int slot, int ln) {
-    const int t0 = t_begin + min(it, ntiles - 1) * S::TILE;
+    const int t0 = it < ntiles ? t_begin + it * S::TILE : 0;
     int64_t run[4];
     tile_runs(t0, run);
     const int k_tok = ln / NCH, k_c = ln % NCH;

@@ -876,3 +876,19 @@ def test_decode_step_graph_replays_match_eager(mode):
     vv = O.ConcatKV(sv, O.LogicalKV(host_array(vc.v_new, dt)[0], dt))
     o_ref, _ = O.verify_attention(O.to_f64(host_array(vc.q, dt)[0], dt), vk, vv, n0 + 2 * g + 1, wl.scale)
     assert max_err(ref_v[layers - 1, 0], o_ref.reshape((g + 1) * Hq, D)) <= TOL["bf16"]
+
+
+# ============================================================== the batch limit
+def test_max_batch_of_64_sequences():
+    """64 sequences (the ABI's limit) of mixed lengths in one call: draft in both modes and
+    verify, each checked against the oracle on every sequence."""
+    wl = synth.workload("draft_131k_bf16", window=128)
+    rng = np.random.default_rng(64)
+    contexts = tuple(int(x) for x in rng.integers(0, 400, size=64))
+    say("batch of 64")
+    for mode in (O.FULL, O.SINK_WINDOW):
+        eo, el = draft_steps(wl, contexts, mode, chunk=64, fast_pv=True, steps=1, fused=True)
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"], (mode, eo, el)
+    wlv = synth.workload("step_1m_bf16")
+    eo, el = verify_run(wlv, contexts, 4, 64, fused=True, interleaved=True)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
