@@ -479,6 +479,8 @@ def test_verify_mixed_batch():
     ((2044, 17), 9, 256, 16, 2),    # three row tiles, straddling 2048
     ((1000, 4000), 4, 0, 16, 2),    # library default split
     ((33, 500), 4, 32, 8, 1),       # G = 8 on one KV head
+    ((100, 40), 33, 32, 1, 1),      # 33 new tokens over two splits of 32 (G = 1, two row tiles)
+    ((64, 5), 4, 32, 16, 2),        # a split made only of new tokens (64..67)
 ])
 def test_verify_fused_append_equals_separate_calls(contexts, t_q, split, hq, hk):
     wl = synth.workload("step_1m_bf16", num_q_heads=hq, num_kv_heads=hk)
