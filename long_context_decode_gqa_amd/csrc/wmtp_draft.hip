@@ -30,9 +30,10 @@
 //      up to rounding because numerator and denominator share the reference.
 //   5. PV: each wave owns its slice of D; V rows arrive in registers two tiles
 //      ahead; probabilities are handed from the entry lanes through LDS.
-// K and V go through a 3-slot register ring; the loop body is unrolled over the
-// slots and every body issues the same loads, so the compiler's wait counts
-// keep two tiles in flight.
+// In full mode K and V go through a 3-slot register ring; the loop body is
+// unrolled over the slots and every body issues the same loads, so the
+// compiler's wait counts keep two tiles in flight.  Window mode's work items
+// read one or a few tiles and use a single slot.
 // The split writes o = sum p v / sum p and lse = ln sum exp(s) for every packed
 // row; a separate LSE combine merges the splits.
 #include "wmtp_device.hpp"

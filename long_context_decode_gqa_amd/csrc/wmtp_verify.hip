@@ -6,10 +6,12 @@
 // ("Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token
 // Context", arxivlens summary, Abstract; howtospark case study, Method: one
 // batched verify per cycle).  Per KV head the t_q query tokens x G query heads
-// form up to 32 packed rows, so QK^T and PV are real dense contractions (rows x
+// form packed rows, so QK^T and PV are real dense contractions (rows x
 // head_dim against each key tile) and run on v_mfma_f32_32x32x16_bf16.  With
 // t_q = 1 this is the native MTP draft step, whose read grows with the context
-// (same summary, Abstract).
+// (same summary, Abstract).  Up to 32 packed rows (one row tile) run on the
+// kernel described here; 33..96 rows (two or three row tiles) on the two-team
+// kernel further down, which reads K and V the same way.
 //
 // Work item = (sequence, KV head, split of `chunk` keys); one 256-thread
 // workgroup whose 4 waves each own a quarter of head_dim.  Each wave keeps a
