@@ -537,7 +537,10 @@ def sweep(flag, steps, warmup, dev, contexts, gammas):
     """Decode steps across context length and draft depth, both draft modes, beside the
     bytes model's native/windowed ratio (which widens as the context grows)."""
     rows = []
-    for n0 in contexts:
+    # Largest contexts first: they are bandwidth-bound and the most sensitive to the
+    # device's state after minutes of sustained load; the small, launch-bound ones
+    # come last.  Rows are reported in context order.
+    for n0 in sorted(contexts, reverse=True):
         for g in gammas:
             wl = synth.workload("step_1m_bf16", contexts=(n0,), gamma=g)
             log(f"sweep n0={n0} gamma={g}")
@@ -560,7 +563,7 @@ def sweep(flag, steps, warmup, dev, contexts, gammas):
                          "graph_replays_match_eager": bool(okw and okn)})
             del step
             torch.cuda.empty_cache()
-    return rows
+    return sorted(rows, key=lambda r: (r["context"], r["gamma"]))
 
 
 def main():
