@@ -533,23 +533,26 @@ struct QuarterLoader {
 // Two or three row tiles (33..96 packed rows) on two teams of 4 waves, 512
 // threads.  With all row tiles in one wave the per-tile chain of LDS stages,
 // barriers, MFMA and softmax has nothing to hide behind at one wave per SIMD;
-// here team 0 loads K and V exactly as the one-row-tile kernel, stages both in
-// LDS and computes row tile 0 of tile t, each wave over its quarter of D, while
-// team 1 computes the other row tiles of tile t - 1 from those stages: every
-// SIMD runs one wave of each team, and HBM is read once.
-//   R1 = 1: team 1's waves split row tile 1's D in quarters, like team 0.
-//   R1 = 2: team 1's waves form two pairs, one per row tile (1 and 2); each wave
-//   covers half of D, so it contracts twice the keys' width per row tile but
-//   runs one row tile's softmax instead of two, and sums 2 partial scores
-//   instead of 4.
-// One barrier per tile step: the K/V stages rotate over three buffers and each
-// team's score exchange over two; neither team can pass a step's barrier
-// before the other reaches it, so team 0 rewrites a stage only after team 1
-// has passed the barrier that follows its last read of it (160 KiB of LDS, the
-// per-workgroup limit).
-template <int G, int R1>
+// here team 0 loads K and V exactly as the one-row-tile kernel and stages both
+// in LDS, while team 1 computes tile t - 1 from those stages: every SIMD runs
+// one wave of each team, and HBM is read once.  Team 1's waves form two pairs,
+// one per row tile; each wave covers half of D, so it contracts its row tile
+// over two quarters of D, runs one row tile's softmax and sums two partial
+// score tiles.  Both waves of a pair add the same two partials (addition is
+// commutative), so they hold identical weights.
+//   RT = 2: team 1 computes row tiles 0 and 1; team 0 only loads and stages.
+//   RT = 3: team 1 computes row tiles 1 and 2; team 0 also computes row tile 0
+//   of tile t, each wave over its quarter of D.
+// Every SIMD thus runs one or two row tiles' softmax per tile.  One barrier per
+// tile step: the K/V stages rotate over three buffers and each team's score
+// exchange over two; neither team can pass a step's barrier before the other
+// reaches it, so team 0 rewrites a stage only after team 1 has passed the
+// barrier that follows its last read of it (160 KiB of LDS, the per-workgroup
+// limit).
+template <int G, int RT>
 __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs a) {
-  static_assert(R1 == 1 || R1 == 2, "team 1 computes one or two row tiles");
+  static_assert(RT == 2 || RT == 3, "two or three row tiles");
+  constexpr bool kTeam0Computes = RT == 3;
   constexpr int ROWB = kVD * 2;
   constexpr int NB = 3;                        // K/V stage buffers
   constexpr int NP = 2;                        // score-exchange buffers per team
@@ -589,7 +592,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
   if (team == 0) {
     // ---- loader team: the one-row-tile kernel's loads and ring, plus the stages for team 1
     RowTile<1> rt0;
-    init_row_tile<G>(w, rt0, 0, wave);
+    if constexpr (kTeam0Computes) init_row_tile<G>(w, rt0, 0, wave);
     auto tile_runs = [&](int it, int64_t (&run)[2]) {
       const int t0 = it < ntiles ? t_begin + it * kVTile : 0;     // past the end: the sequence's first tile
 #pragma unroll
@@ -634,15 +637,22 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
                           ld.vreg[slot][0][q >> 1][4 * (q & 1) + 2], ld.vreg[slot][0][q >> 1][4 * (q & 1) + 3]};
         v_stage[it % NB][wave][q][lane] = v4;
       }
-      float* parts = sc_lds[0][it % NP];
-      store_partial(w, qk_partial(w, k_stage[it % NB], rt0), parts + wave * kPart);
-      __syncthreads();
-      float s2[16];
-      sum4_partials(w, parts, s2);
-      __builtin_amdgcn_sched_barrier(0);
-      tile_runs(it + kRing, run_next);
-      __builtin_amdgcn_sched_barrier(0);
-      softmax_pv(w, t0, s2, ld.vreg[slot], rt0);
+      if constexpr (kTeam0Computes) {
+        float* parts = sc_lds[0][it % NP];
+        store_partial(w, qk_partial(w, k_stage[it % NB], rt0), parts + wave * kPart);
+        __syncthreads();
+        float s2[16];
+        sum4_partials(w, parts, s2);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_runs(it + kRing, run_next);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax_pv(w, t0, s2, ld.vreg[slot], rt0);
+      } else {
+        (void)t0;
+        __syncthreads();
+        tile_runs(it + kRing, run_next);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
     if (ntiles > 0) {
 #pragma unroll
@@ -664,36 +674,13 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
     }
     // team 1 still computes the last tile: its barrier
     __syncthreads();
-    finish_row_tile<G>(w, rt0);
-  } else if constexpr (R1 == 1) {
-    // ---- team 1: row tile 1 of tile it - 1, each wave over its quarter of D
-    RowTile<1> rt;
-    init_row_tile<G>(w, rt, 1, wave);
-    for (int it = 0; it <= ntiles; ++it) {
-      const int t = it - 1;
-      float* parts = sc_lds[1][it % NP];
-      if (t >= 0) store_partial(w, qk_partial(w, k_stage[t % NB], rt), parts + wave * kPart);
-      __syncthreads();
-      if (t >= 0) {
-        float s2[16];
-        sum4_partials(w, parts, s2);
-        uint32_t vv[1][2][8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 v4 = v_stage[t % NB][wave][q][lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vv[0][q >> 1][4 * (q & 1) + e] = v4[e];
-        }
-        softmax_pv(w, t_begin + t * kVTile, s2, vv, rt);
-      }
-    }
-    finish_row_tile<G>(w, rt);
+    if constexpr (kTeam0Computes) finish_row_tile<G>(w, rt0);
   } else {
-    // ---- team 1: row tiles 1 and 2 of tile it - 1; waves 2r and 2r + 1 take row tile
-    // 1 + r, each over one half of D (quarters 2 dh and 2 dh + 1)
+    // ---- team 1: the last two row tiles of tile it - 1; waves 2r and 2r + 1 take row
+    // tile RT - 2 + r, each over one half of D (quarters 2 dh and 2 dh + 1)
     const int r = wave >> 1, dh = wave & 1;
     RowTile<2> rt;
-    init_row_tile<G>(w, rt, 1 + r, 2 * dh);
+    init_row_tile<G>(w, rt, RT - 2 + r, 2 * dh);
     for (int it = 0; it <= ntiles; ++it) {
       const int t = it - 1;
       float* parts = sc_lds[1][it % NP] + 2 * r * kPart;      // the pair's two partials
@@ -729,8 +716,8 @@ static hipError_t launch_rt(int rt, bool single, const SplitArgs& a, int grid, h
   } else {
     switch (rt) {
       case 1: mfma_attn_kernel<G, false><<<grid, 256, 0, st>>>(a); break;
-      case 2: mfma_attn_teams_kernel<G, 1><<<grid, 512, 0, st>>>(a); break;
-      case 3: mfma_attn_teams_kernel<G, 2><<<grid, 512, 0, st>>>(a); break;
+      case 2: mfma_attn_teams_kernel<G, 2><<<grid, 512, 0, st>>>(a); break;
+      case 3: mfma_attn_teams_kernel<G, 3><<<grid, 512, 0, st>>>(a); break;
       default: return hipErrorInvalidValue;
     }
   }
