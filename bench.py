@@ -569,7 +569,7 @@ def sweep(flag, steps, warmup, dev, contexts, gammas):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     # ~35 ms of sustained load at 1M: after an idle spell the first launches run fast, then
     # slow for a few ms, and settle after ~20 ms of load; the warmup absorbs that
     ap.add_argument("--warmup", type=int, default=10)
