@@ -451,7 +451,7 @@ def test_verify_bf16_gamma3(n0, split):
 
 @pytest.mark.parametrize("t_q,hq,hk", [(1, 16, 2), (2, 16, 2), (3, 16, 2), (4, 8, 1), (8, 8, 2), (32, 2, 2),
                                        (5, 16, 2), (6, 16, 2), (8, 16, 2), (9, 16, 2), (12, 16, 2), (48, 4, 2),
-                                       (33, 1, 1)])
+                                       (33, 1, 1), (17, 4, 2), (12, 8, 2), (24, 8, 2), (70, 1, 1)])
 def test_verify_row_packings(t_q, hq, hk):
     wl = synth.workload("step_1m_bf16", num_q_heads=hq, num_kv_heads=hk)
     say("verify rows", t_q, hq, hk)
