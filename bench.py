@@ -513,10 +513,14 @@ def cpu_baseline(wl, n0, budget_s=12.0):
         lambda r: O.attention_over(qs[r % 4, 0], src_k, src_v, win, 0, wl.scale), 0.05 * budget_s)
     Hk, L = wl.num_kv_heads, wl.target_layers
     verify_step = t_verify * Hk * L
+    win_s, nat_s = verify_step + t_win * Hk * g, verify_step + t_native * Hk * g
     return {
-        "value": round((verify_step + t_win * Hk * g) * 1e6, 1),
+        "value": round(win_s * 1e6, 1),
         "unit": "us/decode-step",
-        "native_value": round((verify_step + t_native * Hk * g) * 1e6, 1),
+        "native_value": round(nat_s * 1e6, 1),
+        # oracle-equivalent rate: the step's algorithmic K/V bytes over the oracle's time
+        "gbps": round(step_bytes(n0, wl, True) / win_s / 1e9, 3),
+        "native_gbps": round(step_bytes(n0, wl, False) / nat_s / 1e9, 3),
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"float64 oracle on 1 KV head: {r_v} verify layer(s) ({g + 1} causal queries x {G} heads over "
