@@ -41,9 +41,10 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "ffcc651b692c60e575f90567bbcc1c041946893ef6141ba4dcd2cc85398be782",
-                  "fetch_kib": 1049662.08, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
-VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
+VERIFY_TRAFFIC = {"sources_sha256": "69bb55b0b94a3c537ca5c51281f78924660ea526e4e47736a90190ca76fee87c",
+                  "fetch_kib": 1049669.91, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_row_tile.hpp",
+                  "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
 
 def verify_sources_sha256() -> str:
@@ -639,8 +640,8 @@ def main():
         un = time_steps(step, W.FULL, flag, args.steps, args.warmup, fused=False)
         details["unfused_step_us"] = {"windowed": pct(uw[3]), "native": pct(un[3])}
         log("graph-captured steps")
-        gw, okw = graph_step(step, W.SINK_WINDOW, flag, 5)
-        gn, okn = graph_step(step, W.FULL, flag, 5)
+        gw, okw = graph_step(step, W.SINK_WINDOW, flag, 20)
+        gn, okn = graph_step(step, W.FULL, flag, 20)
         details["graph_step_us"] = {"windowed": pct(gw), "native": pct(gn), "replays_match_eager": bool(okw and okn)}
         log("window draft: warm, cold, across contexts")
         details["window_draft_step_us"] = window_measurements(
@@ -697,7 +698,7 @@ def main():
             "draft_native_per_step": round(dnat_ms * 1e3, 2),
         },
         "roofline": {
-            "kernel": "mfma_attn_kernel<8, false> (verify, 10 launches per step)",
+            "kernel": "mfma_attn_kernel<8, false, false> (verify, 10 launches per step)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -78,10 +78,10 @@ extern "C" {
 /* Optional flag OR-ed into the draft mode (bf16 only): the PV product takes the
  * softmax weights rounded to bf16 (bf16 x bf16 products, fp32 sums) instead of
  * fp32 weights.  The normaliser is summed from the same rounded weights.  With
- * this flag, WMTP_FULL and head_dim 256 run on the matrix-core kernel of
- * wmtp_verify_attn with one query token (the same arithmetic); other shapes use
- * v_dot2_f32_bf16 over key pairs.  Without it the PV product uses the fp32
- * weights. */
+ * this flag and head_dim 256, both modes run on the matrix-core kernel of
+ * wmtp_verify_attn with one query token (the same arithmetic), over the paged
+ * pool or over the ring's visible entries; other shapes use v_dot2_f32_bf16
+ * over key pairs.  Without it the PV product uses the fp32 weights. */
 #define WMTP_DRAFT_FAST_PV 0x10
 
 #define WMTP_MAX_BATCH   64     /* sequences per call                                         */

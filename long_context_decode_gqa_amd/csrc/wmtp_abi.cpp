@@ -302,14 +302,17 @@ int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_
   }
   const int grid = p.total * shape->num_kv_heads;
   const bool fast_pv = (mode & WMTP_DRAFT_FAST_PV) != 0 && shape->dtype == WMTP_BF16;
-  if (base_mode == WMTP_FULL && fast_pv && shape->head_dim == 256) {
-    // The native draft is full-context attention of a single query token, i.e.
-    // the verify contraction with t_q = 1; both round p to bf16 before PV, so the
-    // G packed rows run on the matrix-core kernel, which spends fewer vector
-    // instructions per key than the dot-product kernel.
+  if (fast_pv && shape->head_dim == 256) {
+    // A draft step is attention of a single query token, i.e. the verify
+    // contraction with t_q = 1; both round p to bf16 before PV, so the G packed
+    // rows run on the matrix-core kernel, which spends fewer vector instructions
+    // per key than the dot-product kernel: over the paged context (native) or
+    // over the ring's visible entries (window).
     a.t_q = 1;
-    return launch_status(launch_verify(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, true, a, grid,
-                                       static_cast<hipStream_t>(stream)));
+    const int group = shape->num_q_heads / shape->num_kv_heads;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return launch_status(base_mode == WMTP_FULL ? launch_verify(shape->head_dim, group, true, a, grid, st)
+                                                : launch_window_mfma(shape->head_dim, group, a, grid, st));
   }
   return launch_status(launch_draft(shape->dtype, shape->head_dim, shape->num_q_heads / shape->num_kv_heads,
                                     base_mode == WMTP_SINK_WINDOW, fast_pv, a, grid,

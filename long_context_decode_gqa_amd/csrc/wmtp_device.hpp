@@ -143,6 +143,33 @@ __device__ __forceinline__ int seq_of_split(const SplitArgs& a, int sg) {
   return b;
 }
 
+// Window mode: the visible entries of sequence b's query at length n, in
+// position order.  Entry t < s_vis is sink t; entry t >= s_vis is position
+// w_start + t - s_vis, one of the last W_b positions before n.  slot(t) is the
+// ring slot that holds it: positions below the layout's S keep their own slot,
+// later ones cycle through the C = slots - S others.  The window spans at most
+// C positions, so its cycle index wraps at most once from ws_mod, the cycle
+// index of w_start: no per-lane division.
+struct WindowView {
+  int s_vis = 0, w_start = 0, nvis = 0, sink = 0, cycle = 1, ws_mod = 0;
+  WindowView() = default;
+  __device__ __forceinline__ WindowView(const SplitArgs& a, int b, int n) {
+    s_vis = min(a.seq_sink[b], n);
+    w_start = max(s_vis, n - a.seq_window[b]);
+    nvis = s_vis + (n - w_start);
+    sink = a.sink;
+    cycle = a.slots - a.sink;
+    ws_mod = (w_start >= sink && cycle > 0) ? (w_start - sink) % cycle : 0;
+  }
+  __device__ __forceinline__ int pos(int t) const { return t < s_vis ? t : w_start + (t - s_vis); }
+  __device__ __forceinline__ int slot(int t) const {
+    const int p = pos(t);
+    if (p < sink) return p;
+    const int c = w_start >= sink ? ws_mod + (p - w_start) : p - sink;
+    return sink + (c >= cycle ? c - cycle : c);
+  }
+};
+
 // Fused append: write the step's new tokens at positions [lo, hi) of sequence
 // b, KV head h, into the cache (paged through the block table, or the ring
 // with the slot tag), then make them visible to the whole workgroup before

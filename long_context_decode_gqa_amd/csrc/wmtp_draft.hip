@@ -99,11 +99,9 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
   const int sg = blockIdx.x / Hkv;
   const int b = seq_of_split(a, sg);
   const int n = a.seq_len[b];
-  // Window mode reads the visible set in position order: entry t < s_vis is sink
-  // t, entry t >= s_vis is position w_start + t - s_vis (the last W_b before n).
-  const int s_vis = min(a.seq_sink[b], n);
-  const int w_start = max(s_vis, n - a.seq_window[b]);
-  const int nvis = WINDOW ? s_vis + (n - w_start) : n;
+  // Window mode reads the visible set in position order (sinks, then the window).
+  const WindowView wv(a, b, n);
+  const int nvis = WINDOW ? wv.nvis : n;
   const int t_begin = (sg - a.split_base[b]) * a.chunk;
   const int t_end = min(t_begin + a.chunk, nvis);
   const int ntiles = (t_end - t_begin + S::TILE - 1) / S::TILE;
@@ -121,20 +119,6 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
   const const_i32_ptr bt_row = as_const_i32(a.block_table) + (int64_t)b * a.bt_stride;
   const int64_t ring_seq = ((int64_t)b * Hkv + h) * a.slots * (int64_t)ROWB;
   const int32_t* tags = a.slot_pos + (int64_t)b * a.slots;
-  // Ring slot of visible entry t (clamped to the split): positions below the
-  // layout's S sit in their own slot, later ones cycle through C = slots - S.
-  // The window spans at most C positions, so its cycle index wraps at most once
-  // from ws_mod, the cycle index of w_start: no per-lane division.
-  const int cyc = a.slots - a.sink;
-  const int ws_mod = w_start >= a.sink ? (w_start - a.sink) % cyc : 0;
-  auto entry_pos = [&](int t) -> int { return t < s_vis ? t : w_start + (t - s_vis); };
-  auto entry_slot = [&](int t) -> int {
-    const int p = entry_pos(t);
-    if (p < a.sink) return p;
-    int c = w_start >= a.sink ? ws_mod + (p - w_start) : p - a.sink;
-    c = c >= cyc ? c - cyc : c;
-    return a.sink + c;
-  };
   const int last_blk_idx = (t_end - 1) >> 4;
 
   // query rows of this KV head, this wave's slice of D (wave-uniform -> SGPRs)
@@ -160,7 +144,7 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
     }
   };
   auto lane_off = [&](int t0, int tt) -> uint32_t {
-    if constexpr (WINDOW) return (uint32_t)entry_slot(min(t0 + tt, t_end - 1)) * ROWB;
+    if constexpr (WINDOW) return (uint32_t)wv.slot(min(t0 + tt, t_end - 1)) * ROWB;
     return (uint32_t)(tt & 15) * ROWB;
   };
   auto run_base = [&](const uint8_t* base, const int64_t (&run)[4], int first, int span, int tt) -> const uint8_t* {
@@ -215,7 +199,7 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
         vreg[slot][k] = load_at<uint2>(run_base(vbase, run, k * TPV, TPV, tt), lane_off(t0, tt) + v_d * 8);
       }
     }
-    if constexpr (WINDOW) tag[slot] = tags[entry_slot(min(t0 + ln, t_end - 1))];
+    if constexpr (WINDOW) tag[slot] = tags[wv.slot(min(t0 + ln, t_end - 1))];
   };
 
   float o[G][EV];
@@ -293,7 +277,7 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
     // ---- online softmax (log2 domain, lazy maximum)
     bool valid = t0 + ln < t_end;
     // the slot must hold exactly the entry's position (a hole or a stale entry is masked)
-    if constexpr (WINDOW) valid = valid && tag[slot] == entry_pos(t0 + ln);
+    if constexpr (WINDOW) valid = valid && tag[slot] == wv.pos(t0 + ln);
     bool exceed = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {

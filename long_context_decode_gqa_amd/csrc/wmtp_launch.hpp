@@ -45,6 +45,8 @@ hipError_t launch_draft(int dtype, int head_dim, int group, bool window, bool pv
 // Matrix-core split-K attention over the paged pool (bf16, head_dim 256) for
 // a.t_q query tokens, or for exactly one when single_query is set.
 hipError_t launch_verify(int head_dim, int group, bool single_query, const SplitArgs& a, int grid, hipStream_t st);
+// The same kernel for one query token over the ring's visible entries (window mode).
+hipError_t launch_window_mfma(int head_dim, int group, const SplitArgs& a, int grid, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_ring_append(const AppendArgs& a, int batch, hipStream_t st);
 hipError_t launch_paged_append(const AppendArgs& a, int batch, hipStream_t st);

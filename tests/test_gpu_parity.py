@@ -285,6 +285,50 @@ def test_per_sequence_sinks_and_windows_parity(fast_pv):
     assert worst <= TOL["bf16"], worst
 
 
+@pytest.mark.parametrize("fast_pv", [False, True])
+def test_window_holes_are_masked(fast_pv):
+    """A visible entry whose slot tag does not hold its position is left out.
+
+    The ring is rolled back below the query's length, so the newest visible
+    positions are holes (tag -1); the result must equal attention over the rest
+    of the window set.  Sequence 0 has wrapped (n > S + W); sequence 1 is
+    shorter than S + W, so sinks and window overlap.  Both kernels that serve
+    window mode are covered (bf16 PV weights at d = 256: the matrix-core one).
+    """
+    S, Wn, R, Hq, Hk, D, B = 4, 64, 2, 16, 2, 256, 2
+    G = Hq // Hk
+    scale = D ** -0.5
+    sh = W.make_shape(Hq, Hk, D, torch.bfloat16, scale)
+    n0, kept = [200, 61], [198, 60]
+    ring = RingCache(B, Hk, D, S, Wn, torch.bfloat16, headroom=R)
+    kc = synth.normal((B, max(n0), Hk, D), 41, "hole_k", 0.5, "bf16")
+    vc = synth.normal((B, max(n0), Hk, D), 41, "hole_v", 0.5, "bf16")
+    for b in range(B):
+        sub = W.Ring(ring.k[b].data_ptr(), ring.v[b].data_ptr(), ring.tags[b].data_ptr(), S, Wn, R)
+        W.ring_append(sh, sub, kc[b:b + 1, :n0[b]].contiguous().to(DEV), vc[b:b + 1, :n0[b]].contiguous().to(DEV), [0])
+    W.ring_rollback(ring.desc, kept)
+    q = synth.normal((B, Hq, D), 41, "hole_q", 1.0, "bf16")
+    qf = O.to_f64(synth.bf16_bits(q), "bf16")
+    flag = W.DRAFT_FAST_PV if fast_pv else 0
+    worst = 0.0
+    for chunk in (64, 0):
+        say("window holes", fast_pv, chunk)
+        ws = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW | flag, sh, n0, chunk, S, Wn, R), DEV)
+        parts = W.draft_attn(W.SINK_WINDOW | flag, sh, q.to(DEV), n0, ws, ring=ring.desc, chunk_tokens=chunk)
+        out, lse = run_combine(parts, Hq, D, B)
+        torch.cuda.synchronize()
+        for b in range(B):
+            pos = O.visible_positions(n0[b], O.SINK_WINDOW, S, Wn)
+            pos = pos[pos < kept[b]]
+            kk = O.LogicalKV(synth.bf16_bits(kc[b]), "bf16", n0[b])
+            vv = O.LogicalKV(synth.bf16_bits(vc[b]), "bf16", n0[b])
+            for h in range(Hk):
+                o_ref, l_ref = O.attention_over(qf[b, h * G:(h + 1) * G], kk, vv, pos, h, scale)
+                worst = max(worst, max_err(out[b, h * G:(h + 1) * G], o_ref), max_err(lse[b, h * G:(h + 1) * G], l_ref))
+    say("window holes worst", worst)
+    assert worst <= TOL["bf16"], worst
+
+
 # ============================================================== draft attention
 def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtype=torch.float32, fused=False,
                 headroom=0, record=None, interleaved=False):
