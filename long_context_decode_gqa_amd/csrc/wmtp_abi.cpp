@@ -26,8 +26,9 @@ constexpr int kVerifyTile = 32;    // keys per verify tile
 // round.  Full-context launches target 256 slots, one item per MI355X compute
 // unit: each CU streams one long run of blocks, measured faster than two
 // co-resident items per CU at 1M keys.  The window draft is latency-bound and
-// its 512-thread items fit two per CU, so it targets 512 slots with splits of
-// at least one 64-entry tile.
+// its items fit two per CU (512-thread dot-product or 256-thread matrix-core
+// items), so it targets 512 slots with splits of at least 64 entries: longer
+// items add a memory round trip of latency per 64 entries.
 constexpr int64_t kFullSlots = 256;
 constexpr int64_t kWindowSlots = 512;
 constexpr int64_t kFullMinSplit = 256;
