@@ -97,18 +97,6 @@ __device__ __forceinline__ f32x4 load_partial(const WorkItem& w, const float* pa
   return *reinterpret_cast<const f32x4*>(part + (q * 64 + w.lane) * 4);
 }
 
-// S of a row tile whose D quarters are split over 4 waves: the sum of their 4 partials, in order.
-__device__ __forceinline__ void sum4_partials(const WorkItem& w, const float* parts, float (&s2)[16]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f32x4 x = load_partial(w, parts, q);
-#pragma unroll
-    for (int k = 1; k < 4; ++k) x += load_partial(w, parts + k * kPart, q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s2[4 * q + e] = x[e];
-  }
-}
-
 // S of a row tile whose D halves are split over a pair of waves: own partial plus the
 // partner's.  Addition is commutative, so both waves of the pair get identical scores.
 __device__ __forceinline__ void sum2_partials(const WorkItem& w, const f32x16& own, const float* other,
@@ -121,12 +109,25 @@ __device__ __forceinline__ void sum2_partials(const WorkItem& w, const f32x16& o
   }
 }
 
-// Mask, lazy maximum, bf16 weights and O += P V for the tile starting at key t0;
-// vv[hq]: V dwords of the wave's quarter q0 + hq (key pairs regrouped here).
+// Mask, lazy maximum, bf16 weights and O += P V for the tile starting at key t0.
+// V comes from the tile's LDS stage (layout [quarter][piece][lane]: piece 2 ks
+// and 2 ks + 1 hold the lane's 8 dwords of k-step ks) for the wave's NQ
+// quarters q0 ..; key pairs are regrouped here.  Up to two quarters the V
+// operands are read before the softmax, so the LDS reads overlap it; a wave
+// that covers all of D reads them one quarter at a time during PV (four
+// quarters' operands do not fit in its registers beside the accumulators).
 template <int NQ>
-__device__ __forceinline__ void softmax_pv(const WorkItem& w, int t0, float (&s2)[16],
-                                           const uint32_t (&vv)[NQ][2][8], RowTile<NQ>& rt) {
+__device__ __forceinline__ void softmax_pv(const WorkItem& w, int t0, float (&s2)[16], const u32x4 (*vst)[4][64],
+                                           RowTile<NQ>& rt) {
   constexpr float TAU = 8.0f;
+  constexpr bool kEarlyV = NQ <= 2;
+  u32x4 vpre[kEarlyV ? NQ : 1][4];
+  if constexpr (kEarlyV) {
+#pragma unroll
+    for (int hq = 0; hq < NQ; ++hq)
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) vpre[hq][pc] = vst[rt.q0 + hq][pc][w.lane];
+  }
   if (t0 + kVTile - 1 > w.all_last) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
@@ -166,15 +167,19 @@ __device__ __forceinline__ void softmax_pv(const WorkItem& w, int t0, float (&s2
   for (int ks = 0; ks < 2; ++ks) {
     const u32x4 pa = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
 #pragma unroll
-    for (int hq = 0; hq < NQ; ++hq)
+    for (int hq = 0; hq < NQ; ++hq) {
+      const u32x4 v0 = kEarlyV ? vpre[hq][2 * ks] : vst[rt.q0 + hq][2 * ks][w.lane];
+      const u32x4 v1 = kEarlyV ? vpre[hq][2 * ks + 1] : vst[rt.q0 + hq][2 * ks + 1][w.lane];
+      const uint32_t vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         u32x4 vb;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          vb[q] = __builtin_amdgcn_perm(vv[hq][ks][2 * q + 1], vv[hq][ks][2 * q], e ? 0x07060302u : 0x05040100u);
+          vb[q] = __builtin_amdgcn_perm(vv[2 * q + 1], vv[2 * q], e ? 0x07060302u : 0x05040100u);
         rt.O[hq][e] = mfma32(pa, vb, rt.O[hq][e]);
       }
+    }
   }
 }
 
@@ -217,7 +222,7 @@ __device__ __forceinline__ void finish_row_tile(const WorkItem& w, const RowTile
 struct QuarterLoader {
   static constexpr int kRing = 3;
   u32x4 kreg[kRing][kVLoads];
-  uint32_t vreg[kRing][1][2][8];
+  uint32_t vreg[kRing][2][8];
 };
 
 // Two or three row tiles (33..96 packed rows) on two teams of 4 waves, 512
@@ -225,31 +230,29 @@ struct QuarterLoader {
 // barriers, MFMA and softmax has nothing to hide behind at one wave per SIMD;
 // here team 0 loads K and V exactly as the one-row-tile kernel and stages both
 // in LDS, while team 1 computes tile t - 1 from those stages: every SIMD runs
-// one wave of each team, and HBM is read once.  Team 1's waves form two pairs,
-// one per row tile; each wave covers half of D, so it contracts its row tile
-// over two quarters of D, runs one row tile's softmax and sums two partial
-// score tiles.  Both waves of a pair add the same two partials (addition is
-// commutative), so they hold identical weights.
-//   RT = 2: team 1 computes row tiles 0 and 1; team 0 only loads and stages.
-//   RT = 3: team 1 computes row tiles 1 and 2; team 0 also computes row tile 0
-//   of tile t, each wave over its quarter of D.
-// Every SIMD thus runs one or two row tiles' softmax per tile.  One barrier per
-// tile step: the K/V stages rotate over three buffers and each team's score
-// exchange over two; neither team can pass a step's barrier before the other
-// reaches it, so team 0 rewrites a stage only after team 1 has passed the
-// barrier that follows its last read of it (160 KiB of LDS, the per-workgroup
-// limit).
+// one wave of each team, and HBM is read once.
+//   RT = 2: team 1's waves form two pairs, one per row tile; each wave covers
+//   half of D, so it contracts its row tile over two quarters of D, runs one
+//   row tile's softmax and adds its partner's partial score tile to its own.
+//   Both waves of a pair add the same two partials (addition is commutative),
+//   so they hold identical weights.
+//   RT = 3: waves 0..2 of team 1 each take one row tile over all of D (16
+//   MFMAs for S, 16 for PV per tile), so no partial scores are exchanged and
+//   each row tile's softmax runs once; wave 3 only keeps the barrier count.
+// One barrier per tile step: the K/V stages rotate over three buffers and the
+// pairs' score exchange over two; neither team can pass a step's barrier
+// before the other reaches it, so team 0 rewrites a stage only after team 1
+// has passed the barrier that follows its last read of it.
 template <int G, int RT>
 __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs a) {
   static_assert(RT == 2 || RT == 3, "two or three row tiles");
-  constexpr bool kTeam0Computes = RT == 3;
   constexpr int ROWB = kVD * 2;
   constexpr int NB = 3;                        // K/V stage buffers
-  constexpr int NP = 2;                        // score-exchange buffers per team
+  constexpr int NP = 2;                        // score-exchange buffers (pairs)
 
   __shared__ __attribute__((aligned(16))) uint8_t k_stage[NB][4 * kVStage];   // [tile % NB][quarter]
   __shared__ __attribute__((aligned(16))) u32x4 v_stage[NB][4][4][64];        // [tile % NB][quarter][piece][lane]
-  __shared__ __attribute__((aligned(16))) float sc_lds[2][NP][4 * kPart];     // [team][tile % NP][wave partial]
+  __shared__ __attribute__((aligned(16))) float sc_lds[NP][RT == 2 ? 4 * kPart : 1];   // [tile % NP][wave partial]
 
   WorkItem w;
   w.a = &a;
@@ -280,9 +283,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
   const int c32 = w.c32, kh = w.kh;
 
   if (team == 0) {
-    // ---- loader team: the one-row-tile kernel's loads and ring, plus the stages for team 1
-    RowTile<1> rt0;
-    if constexpr (kTeam0Computes) init_row_tile<G>(w, rt0, 0, wave);
+    // ---- loader team: the one-row-tile kernel's loads and ring, staged for team 1
     auto tile_runs = [&](int it, int64_t (&run)[2]) {
       const int t0 = it < ntiles ? t_begin + it * kVTile : 0;     // past the end: the sequence's first tile
 #pragma unroll
@@ -306,13 +307,11 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
-          ld.vreg[slot][0][ks][jj] =
-              load_nt<uint32_t>(vbase + run[ks] + (8 * (jj >> 2)) * ROWB, v_off + (jj & 3) * ROWB);
+          ld.vreg[slot][ks][jj] = load_nt<uint32_t>(vbase + run[ks] + (8 * (jj >> 2)) * ROWB, v_off + (jj & 3) * ROWB);
     };
     auto body = [&](int it, int slot) {
       uint32_t k_off = k_off0, v_off = v_off0;
       asm volatile("" : "+v"(k_off), "+v"(v_off));
-      const int t0 = t_begin + it * kVTile;
       issue((slot + kRing - 1) % kRing, run_next, k_off, v_off);
       __builtin_amdgcn_sched_barrier(0);
       uint8_t* kst = k_stage[it % NB] + wave * kVStage;
@@ -323,26 +322,13 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const u32x4 v4 = {ld.vreg[slot][0][q >> 1][4 * (q & 1)], ld.vreg[slot][0][q >> 1][4 * (q & 1) + 1],
-                          ld.vreg[slot][0][q >> 1][4 * (q & 1) + 2], ld.vreg[slot][0][q >> 1][4 * (q & 1) + 3]};
+        const u32x4 v4 = {ld.vreg[slot][q >> 1][4 * (q & 1)], ld.vreg[slot][q >> 1][4 * (q & 1) + 1],
+                          ld.vreg[slot][q >> 1][4 * (q & 1) + 2], ld.vreg[slot][q >> 1][4 * (q & 1) + 3]};
         v_stage[it % NB][wave][q][lane] = v4;
       }
-      if constexpr (kTeam0Computes) {
-        float* parts = sc_lds[0][it % NP];
-        store_partial(w, qk_partial(w, k_stage[it % NB], rt0), parts + wave * kPart);
-        __syncthreads();
-        float s2[16];
-        sum4_partials(w, parts, s2);
-        __builtin_amdgcn_sched_barrier(0);
-        tile_runs(it + kRing, run_next);
-        __builtin_amdgcn_sched_barrier(0);
-        softmax_pv(w, t0, s2, ld.vreg[slot], rt0);
-      } else {
-        (void)t0;
-        __syncthreads();
-        tile_runs(it + kRing, run_next);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      __syncthreads();
+      tile_runs(it + kRing, run_next);
+      __builtin_amdgcn_sched_barrier(0);
     };
     if (ntiles > 0) {
 #pragma unroll
@@ -364,16 +350,36 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
     }
     // team 1 still computes the last tile: its barrier
     __syncthreads();
-    if constexpr (kTeam0Computes) finish_row_tile<G>(w, rt0);
+  } else if constexpr (RT == 3) {
+    // ---- team 1, three row tiles: wave r < 3 takes row tile r of tile it - 1 over all of D
+    if (wave < 3) {
+      RowTile<4> rt;
+      init_row_tile<G>(w, rt, wave, 0);
+      for (int it = 0; it <= ntiles; ++it) {
+        const int t = it - 1;
+        f32x16 sacc;
+        if (t >= 0) sacc = qk_partial(w, k_stage[t % NB], rt);
+        __syncthreads();
+        if (t >= 0) {
+          float s2[16];
+#pragma unroll
+          for (int x = 0; x < 16; ++x) s2[x] = sacc[x];
+          softmax_pv(w, t_begin + t * kVTile, s2, v_stage[t % NB], rt);
+        }
+      }
+      finish_row_tile<G>(w, rt);
+    } else {
+      for (int it = 0; it <= ntiles; ++it) __syncthreads();
+    }
   } else {
-    // ---- team 1: the last two row tiles of tile it - 1; waves 2r and 2r + 1 take row
-    // tile RT - 2 + r, each over one half of D (quarters 2 dh and 2 dh + 1)
+    // ---- team 1, two row tiles: waves 2r and 2r + 1 take row tile r of tile it - 1,
+    // each over one half of D (quarters 2 dh and 2 dh + 1)
     const int r = wave >> 1, dh = wave & 1;
     RowTile<2> rt;
-    init_row_tile<G>(w, rt, RT - 2 + r, 2 * dh);
+    init_row_tile<G>(w, rt, r, 2 * dh);
     for (int it = 0; it <= ntiles; ++it) {
       const int t = it - 1;
-      float* parts = sc_lds[1][it % NP] + 2 * r * kPart;      // the pair's two partials
+      float* parts = sc_lds[it % NP] + 2 * r * kPart;      // the pair's two partials
       f32x16 own;
       if (t >= 0) {
         own = qk_partial(w, k_stage[t % NB], rt);
@@ -383,16 +389,7 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
       if (t >= 0) {
         float s2[16];
         sum2_partials(w, own, parts + (dh ^ 1) * kPart, s2);
-        uint32_t vv[2][2][8];
-#pragma unroll
-        for (int hq = 0; hq < 2; ++hq)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 v4 = v_stage[t % NB][2 * dh + hq][q][lane];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vv[hq][q >> 1][4 * (q & 1) + e] = v4[e];
-          }
-        softmax_pv(w, t_begin + t * kVTile, s2, vv, rt);
+        softmax_pv(w, t_begin + t * kVTile, s2, v_stage[t % NB], rt);
       }
     }
     finish_row_tile<G>(w, rt);
