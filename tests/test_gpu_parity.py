@@ -426,6 +426,18 @@ def test_draft_mixed_batch_paged_permuted(mode):
     assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
 
 
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+@pytest.mark.parametrize("hq,hk", [(2, 2), (4, 2), (8, 2), (4, 1)])
+def test_draft_matrix_core_groupings(mode, hq, hk):
+    """bf16 PV weights at d = 256 run the draft step on the matrix-core kernel in both modes
+    (paged pool or ring); every query-head grouping G = 1, 2, 4 it is built for, beside the
+    benchmark's G = 8, with fused appends, several splits and a wrapped ring."""
+    wl = synth.workload("draft_131k_bf16", num_q_heads=hq, num_kv_heads=hk, head_dim=256, window=300)
+    say("draft matrix-core groupings", mode, hq, hk)
+    eo, el = draft_steps(wl, (1500, 77), mode, chunk=128, fast_pv=True, fused=True, headroom=2)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
 @pytest.mark.parametrize("hq,hk,d", [(8, 8, 64), (4, 2, 128), (4, 1, 64), (16, 4, 256)])
 def test_draft_other_head_shapes(hq, hk, d):
     wl = synth.workload("draft_131k_bf16", num_q_heads=hq, num_kv_heads=hk, head_dim=d, window=300)
