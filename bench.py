@@ -409,6 +409,53 @@ def native_split_measurements(step, flag, reps, dev):
     return out
 
 
+def other_head_reading(flag, reps, dev):
+    """The 1M paged draft workload under the other reading of its head shapes: 4 query heads on
+    1 KV head, d=64, bf16 (256 B per token).  Native and windowed draft step (append inside the
+    attention launch, then the combine) in the launch configuration of the main step."""
+    wl = synth.workload("paged_1m_bf16", num_q_heads=4, num_kv_heads=1, head_dim=64)
+    Hq, Hk, D, S, Wn, R = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.sink, wl.window, wl.gamma - 1
+    n0 = wl.contexts[0]
+    n = n0 + 1
+    sh = W.make_shape(Hq, Hk, D, torch.bfloat16, wl.scale)
+    bt, total = synth.block_table(wl.seed, [synth.blocks_for(n, 16)], permuted=True)
+    pool = synth.normal((total, Hk, 2, 16, D), wl.seed, "pool_kv", wl.kv_scale, "bf16", dev)   # K|V runs
+    btd = torch.from_numpy(bt).to(dev)
+    desc = W.make_paged_interleaved(pool, btd)
+    q = synth.normal((1, Hq, D), wl.seed, "q_draft", 1.0, "bf16", dev)
+    kn = synth.normal((1, 1, Hk, D), wl.seed, "k_new", wl.kv_scale, "bf16", dev)
+    vn = synth.normal((1, 1, Hk, D), wl.seed, "v_new", wl.kv_scale, "bf16", dev)
+    out = torch.empty((1, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, Hq), dtype=torch.float32, device=dev)
+    ws = W.workspace(W.draft_workspace_bytes(W.FULL, sh, [n], 0), dev)
+
+    def native():
+        W.combine(W.draft_attn_append(W.FULL | flag, sh, q, kn, vn, [n], ws, paged=desc), out, lse)
+    native()
+    t_nat = pct(_timed(native, reps))["median"]
+    rk = torch.zeros((1, Hk, S + Wn + R, D), dtype=torch.bfloat16, device=dev)
+    rv = torch.zeros_like(rk)
+    tags = torch.full((1, S + Wn + R), -1, dtype=torch.int32, device=dev)
+    ring = W.make_ring(rk, rv, tags, S, Wn, R)
+    W.ring_append(sh, ring, synth.normal((1, S, Hk, D), wl.seed, "ring_sink_k", wl.kv_scale, "bf16", dev),
+                  synth.normal((1, S, Hk, D), wl.seed, "ring_sink_v", wl.kv_scale, "bf16", dev), [0])
+    W.ring_append(sh, ring, synth.normal((1, Wn, Hk, D), wl.seed, "ring_tail_k", wl.kv_scale, "bf16", dev),
+                  synth.normal((1, Wn, Hk, D), wl.seed, "ring_tail_v", wl.kv_scale, "bf16", dev), [n0 - Wn])
+    wsw = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, [n], 0, S, Wn, R), dev)
+
+    def window():
+        W.combine(W.draft_attn_append(W.SINK_WINDOW | flag, sh, q, kn, vn, [n], wsw, ring=ring), out, lse)
+    window()
+    t_win = pct(_timed(window, reps))["median"]
+    res = {"shape": "4 q heads / 1 KV head, d=64, bf16", "context": n0,
+           "native_draft_step_us": t_nat,
+           "native_gbps": round(draft_launch_bytes(n, wl, True) / (t_nat * 1e-6) / 1e9, 1),
+           "window_draft_step_us": t_win}
+    del pool, ws, wsw, rk, rv, tags
+    torch.cuda.empty_cache()
+    return res
+
+
 def mixed_batch(flag, reps, dev):
     """Four sequences of mixed length in one call: native draft, then the window draft at three W."""
     wl = synth.workload("mixed_4seq_bf16")
@@ -418,7 +465,8 @@ def mixed_batch(flag, reps, dev):
     B = len(lens)
     bt, total = synth.block_table(wl.seed, [synth.blocks_for(n, 16) for n in lens], permuted=True)
     pool = synth.normal((total, Hk, 2, 16, D), wl.seed, "pool_kv", wl.kv_scale, "bf16", dev)   # K|V runs
-    desc = W.make_paged_interleaved(pool, torch.from_numpy(bt).to(dev))
+    btd = torch.from_numpy(bt).to(dev)
+    desc = W.make_paged_interleaved(pool, btd)
     q = synth.normal((B, Hq, D), wl.seed, "q_draft", 1.0, "bf16", dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
@@ -656,6 +704,8 @@ def main():
         torch.cuda.empty_cache()
         log("mixed batch (4 sequences)")
         details["mixed_batch"] = mixed_batch(flag, reps, dev)
+        log("1M draft step, 4 q heads / 1 KV head / d=64")
+        details["draft_1m_4q_1kv_d64"] = other_head_reading(flag, reps, dev)
 
     g = wl.gamma
     bytes_win, bytes_nat = step_bytes(n0, wl, True), step_bytes(n0, wl, False)

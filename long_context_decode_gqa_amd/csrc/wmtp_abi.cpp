@@ -25,7 +25,8 @@ constexpr int kVerifyTile = 32;    // keys per verify tile
 // that holds one item per sequence and head), so no item waits for a second
 // round.  Full-context launches target 256 slots, one item per MI355X compute
 // unit: each CU streams one long run of blocks, measured faster than two
-// co-resident items per CU at 1M keys.  The window draft is latency-bound and
+// co-resident items per CU at 1M keys (rows of 512 bytes or more; narrower
+// rows target twice as many, see draft_plan).  The window draft is latency-bound and
 // its items fit two per CU (512-thread dot-product or 256-thread matrix-core
 // items), so it targets 512 slots with splits of at least 64 entries: longer
 // items add a memory round trip of latency per 64 entries.
@@ -148,9 +149,15 @@ int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, i
     bound[b] = std::min<int64_t>(seq_lens[b], ring_slots);
     vis[b] = upper_bound ? bound[b] : std::min<int64_t>(seq_lens[b], sb + wb);
   }
-  if (chunk == 0)
-    chunk = base_mode == WMTP_FULL ? default_split(bound, batch, shape->num_kv_heads, kFullSlots, kFullMinSplit)
+  if (chunk == 0) {
+    // Rows under 512 bytes run on the dot-product kernel with 4 waves per work item;
+    // two items per CU then keep enough loads in flight (measured at 1M keys: 4/1/64
+    // 137 -> 84 us, 8/1/128 175 -> 130 us, 4/2/128 244 -> 194 us).
+    const int64_t row_bytes = (int64_t)shape->head_dim * elem_bytes(shape->dtype);
+    const int64_t full_slots = row_bytes < 512 ? 2 * kFullSlots : kFullSlots;
+    chunk = base_mode == WMTP_FULL ? default_split(bound, batch, shape->num_kv_heads, full_slots, kFullMinSplit)
                                    : default_split(bound, batch, shape->num_kv_heads, kWindowSlots, kWindowMinSplit);
+  }
   if (chunk < kDraftTile || chunk % kDraftTile != 0) return WMTP_EINVAL;
   *chunk_out = chunk;
   return make_plan(vis, batch, chunk, shape->num_q_heads, shape->head_dim, shape->num_kv_heads, p);

@@ -160,34 +160,47 @@ def make_shape(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.
     return Shape(num_q_heads, num_kv_heads, head_dim, head_dim ** -0.5 if scale is None else scale, dtype_code(dtype))
 
 
+# The descriptors hold raw device pointers; each keeps a reference to the tensors it
+# points into, so that a temporary (say a block table built inline) is not freed and
+# its memory reused by torch's allocator while the descriptor is still in use.
 def make_paged(k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor) -> Paged:
-    """Separate pools k, v: [num_blocks][H_kv][16][D]; block_table: int32 [batch][max_blocks] (device)."""
+    """Separate pools k, v: [num_blocks][H_kv][16][D]; block_table: int32 [batch][max_blocks] (device).
+    The descriptor keeps k, v and block_table alive."""
     assert block_table.dtype == torch.int32 and block_table.dim() == 2
     assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
-    return Paged(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), BLOCK_SIZE, block_table.shape[1], k.shape[0],
-                 BLOCK_SIZE)
+    p = Paged(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), BLOCK_SIZE, block_table.shape[1], k.shape[0],
+              BLOCK_SIZE)
+    p._tensors = (k, v, block_table)
+    return p
 
 
 def make_paged_interleaved(pool: torch.Tensor, block_table: torch.Tensor) -> Paged:
     """One pool [num_blocks][H_kv][2][16][D] holding K (index 0) and V (index 1) of each (block, head)
-    as one contiguous run of 32 rows; k and v views are pool[:, :, 0] and pool[:, :, 1]."""
+    as one contiguous run of 32 rows; k and v views are pool[:, :, 0] and pool[:, :, 1].  The
+    descriptor keeps pool and block_table alive."""
     assert block_table.dtype == torch.int32 and block_table.dim() == 2
     assert pool.is_contiguous() and pool.dim() == 5 and pool.shape[2] == 2 and pool.shape[3] == BLOCK_SIZE
-    return Paged(pool[:, :, 0].data_ptr(), pool[:, :, 1].data_ptr(), block_table.data_ptr(), BLOCK_SIZE,
-                 block_table.shape[1], pool.shape[0], 2 * BLOCK_SIZE)
+    p = Paged(pool[:, :, 0].data_ptr(), pool[:, :, 1].data_ptr(), block_table.data_ptr(), BLOCK_SIZE,
+              block_table.shape[1], pool.shape[0], 2 * BLOCK_SIZE)
+    p._tensors = (pool, block_table)
+    return p
 
 
 def make_ring(k: torch.Tensor, v: torch.Tensor, slot_pos: torch.Tensor, sink: int, window: int,
               headroom: int = 0) -> Ring:
-    """k, v: [batch][H_kv][S+W+R][D]; slot_pos: int32 [batch][S+W+R] (device); R = headroom."""
+    """k, v: [batch][H_kv][S+W+R][D]; slot_pos: int32 [batch][S+W+R] (device); R = headroom.  The
+    descriptor keeps k, v and slot_pos alive."""
     assert slot_pos.dtype == torch.int32
-    return Ring(k.data_ptr(), v.data_ptr(), slot_pos.data_ptr(), int(sink), int(window), int(headroom), None, None)
+    r = Ring(k.data_ptr(), v.data_ptr(), slot_pos.data_ptr(), int(sink), int(window), int(headroom), None, None)
+    r._tensors = (k, v, slot_pos)
+    return r
 
 
 def with_policy(ring: Ring, seq_sink: Optional[Sequence[int]] = None,
                 seq_window: Optional[Sequence[int]] = None) -> Ring:
     """A copy of `ring` whose draft queries use per-sequence sinks / windows (host arrays kept alive)."""
     r = Ring(ring.k, ring.v, ring.slot_pos, ring.sink, ring.window, ring.headroom, None, None)
+    r._tensors = getattr(ring, "_tensors", None)
     if seq_sink is not None:
         r._seq_sink = _lens(seq_sink)
         r.seq_sink = ctypes.cast(r._seq_sink, ctypes.c_void_p)

@@ -416,3 +416,46 @@ def test_memory_plan_checks():
     assert lib.wmtp_plan_memory(ctypes.byref(sh), 10, 10, 4, 64, 0, 0, None) == W.EINVAL
     assert lib.wmtp_plan_memory(ctypes.byref(sh), 1 << 30, 1 << 60, 4, 64, 0, 0, ctypes.byref(out)) == W.EINVAL
     assert lib.wmtp_plan_memory(None, 10, 10, 4, 64, 0, 0, ctypes.byref(out)) == W.EINVAL
+
+
+def test_descriptors_keep_their_tensors_alive():
+    """A descriptor holds raw pointers; it must keep the tensors behind them alive, so that a
+    block table or ring built inline is not freed (and its memory reused) while it is in use,
+    and let them go with it."""
+    import gc
+    import weakref
+
+    def pools():
+        return torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16)
+
+    def table():
+        return torch.zeros((1, 4), dtype=torch.int32)
+
+    def tags():
+        return torch.full((1, 12), -1, dtype=torch.int32)
+
+    def ring_kv():
+        return torch.zeros((1, 2, 12, 64), dtype=torch.bfloat16)
+
+    builds = [
+        lambda t: W.make_paged(t[0], t[1], t[2]),
+        lambda t: W.make_paged_interleaved(t[0], t[1]),
+        lambda t: W.make_ring(t[0], t[1], t[2], 4, 8),
+        lambda t: W.with_policy(W.make_ring(t[0], t[1], t[2], 4, 8), [2], [8]),
+    ]
+    inputs = [
+        lambda: (pools(), pools(), table()),
+        lambda: (torch.zeros((4, 2, 2, 16, 64), dtype=torch.bfloat16), table()),
+        lambda: (ring_kv(), ring_kv(), tags()),
+        lambda: (ring_kv(), ring_kv(), tags()),
+    ]
+    for build, make_inputs in zip(builds, inputs):
+        temporaries = make_inputs()
+        refs = [weakref.ref(t) for t in temporaries]
+        desc = build(temporaries)
+        del temporaries
+        gc.collect()
+        assert all(r() is not None for r in refs)
+        del desc
+        gc.collect()
+        assert all(r() is None for r in refs)

@@ -675,6 +675,48 @@ def test_draft_full_1m_paged_sampled_head():
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+def test_draft_1m_other_head_reading(mode):
+    """The 1M paged draft workload under the other reading of its head shapes (4 query heads on
+    1 KV head, d = 64, bf16), in the launch configuration the benchmark times: bf16 PV weights,
+    default splits, the step's token appended inside the launch.  Native over a K|V-run pool with
+    a random block permutation, window over a ring with headroom; all heads checked against the
+    oracle over the whole context."""
+    n0, Hq, Hk, D, S, Wn, R = 1 << 20, 4, 1, 64, 4, 4096, 2
+    scale = D ** -0.5
+    say("draft 1M 4q/1kv/64", mode)
+    sh = W.make_shape(Hq, Hk, D, torch.bfloat16, scale)
+    kc = synth.normal((1, n0, Hk, D), 7, "ctx_k_4q", 0.5, "bf16", DEV)
+    vc = synth.normal((1, n0, Hk, D), 7, "ctx_v_4q", 0.5, "bf16", DEV)
+    kn = synth.normal((1, 1, Hk, D), 7, "kn_4q", 0.5, "bf16", DEV)
+    vn = synth.normal((1, 1, Hk, D), 7, "vn_4q", 0.5, "bf16", DEV)
+    q = synth.normal((1, Hq, D), 7, "q_4q", 1.0, "bf16", DEV)
+    n = n0 + 1
+    flag = W.DRAFT_FAST_PV
+    if mode == O.FULL:
+        bt, total = synth.block_table(7, [synth.blocks_for(n, 16)], permuted=True)
+        pool = torch.zeros((total, Hk, 2, 16, D), dtype=torch.bfloat16, device=DEV)
+        btd = torch.from_numpy(bt).to(DEV)
+        desc = W.make_paged_interleaved(pool, btd)
+        W.paged_append(sh, desc, kc, vc, [0])
+        ws = W.workspace(W.draft_workspace_bytes(W.FULL, sh, [n], 0), DEV)
+        parts = W.draft_attn_append(W.FULL | flag, sh, q, kn, vn, [n], ws, paged=desc)
+    else:
+        ring = RingCache(1, Hk, D, S, Wn, torch.bfloat16, headroom=R)
+        W.ring_append(sh, ring.desc, kc, vc, [0])
+        ws = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, [n], 0, S, Wn, R), DEV)
+        parts = W.draft_attn_append(W.SINK_WINDOW | flag, sh, q, kn, vn, [n], ws, ring=ring.desc)
+    out, lse = run_combine(parts, Hq, D, 1)
+    torch.cuda.synchronize()
+    sk = O.ConcatKV(O.LogicalKV(synth.bf16_bits(kc[0]), "bf16"), O.LogicalKV(synth.bf16_bits(kn[0]), "bf16"))
+    sv = O.ConcatKV(O.LogicalKV(synth.bf16_bits(vc[0]), "bf16"), O.LogicalKV(synth.bf16_bits(vn[0]), "bf16"))
+    o_ref, l_ref = O.draft_attention(O.to_f64(synth.bf16_bits(q[0]), "bf16"), sk, sv, n, mode, S, Wn, scale)
+    eo, el = max_err(out[0], o_ref), max_err(lse[0], l_ref)
+    say("draft 1M 4q/1kv/64 errors", eo, el)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
+@pytest.mark.slow
 def test_verify_1m_paged_sampled_head():
     """One target layer's verify at 1M context in the benchmark's launch configuration (default
     splits): 4 causal queries over 1,048,580 keys, two query tokens checked on one KV head."""
