@@ -189,9 +189,10 @@ int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const 
  *  chunk_tokens: entries per split (a multiple of 64).  0 = library default:
  *  the smallest multiple of 64 (at least 256 in WMTP_FULL mode, 64 in
  *  WMTP_SINK_WINDOW mode, at most 65536) for which the work items
- *  (sequence, KV head, split) fit one round of 256 (WMTP_FULL: one per MI355X
- *  compute unit) or 512 (WMTP_SINK_WINDOW) items, or of the smallest multiple
- *  of that holding one item per sequence and KV head.
+ *  (sequence, KV head, split) fit one round of 256 (WMTP_FULL with rows of at
+ *  least 512 bytes: one per MI355X compute unit) or 512 (WMTP_FULL with
+ *  narrower rows, and WMTP_SINK_WINDOW) items, or of the smallest multiple of
+ *  that holding one item per sequence and KV head.
  *  The call writes split partials into `workspace` (device, >= the size from
  *  wmtp_draft_workspace_bytes, 256-byte aligned) and describes them in
  *  *parts (host).  Finish with wmtp_combine. */
