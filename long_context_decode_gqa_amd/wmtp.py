@@ -238,6 +238,7 @@ def draft_attn(mode: int, shape: Shape, q: torch.Tensor, seq_lens: Sequence[int]
         ctypes.byref(ring) if ring is not None else None, ctypes.cast(_lens(seq_lens), ctypes.c_void_p),
         len(seq_lens), chunk_tokens, ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(parts),
         _stream(stream)))
+    parts._workspace = ws   # the partials live in ws: keep it alive with them
     return parts
 
 
@@ -248,6 +249,7 @@ def verify_attn(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, seq_lens:
         ctypes.byref(shape), q.data_ptr(), t_q, ctypes.byref(paged), ctypes.cast(_lens(seq_lens), ctypes.c_void_p),
         len(seq_lens), split_tokens, ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(parts),
         _stream(stream)))
+    parts._workspace = ws   # the partials live in ws: keep it alive with them
     return parts
 
 
@@ -271,6 +273,7 @@ def draft_attn_append(mode: int, shape: Shape, q: torch.Tensor, k_new: torch.Ten
         ctypes.byref(ring) if ring is not None else None, k_new.data_ptr(), v_new.data_ptr(),
         ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), chunk_tokens, ws.data_ptr(),
         ws.numel() * ws.element_size(), ctypes.byref(parts), _stream(stream)))
+    parts._workspace = ws   # the partials live in ws: keep it alive with them
     return parts
 
 
@@ -284,6 +287,7 @@ def verify_attn_append(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, k_
         ctypes.byref(shape), q.data_ptr(), t_q, ctypes.byref(paged), k_new.data_ptr(), v_new.data_ptr(),
         ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), split_tokens, ws.data_ptr(),
         ws.numel() * ws.element_size(), ctypes.byref(parts), _stream(stream)))
+    parts._workspace = ws   # the partials live in ws: keep it alive with them
     return parts
 
 

@@ -459,3 +459,4 @@ def test_descriptors_keep_their_tensors_alive():
         del desc
         gc.collect()
         assert all(r() is None for r in refs)
+

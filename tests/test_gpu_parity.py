@@ -426,6 +426,34 @@ def test_draft_mixed_batch_paged_permuted(mode):
     assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
 
 
+def test_partials_keep_their_workspace_alive():
+    """The partials a call returns point into its workspace and keep it alive: a workspace made
+    inline in the call stays valid until the combine, and is freed with the partials."""
+    import gc
+    import weakref
+    wl = synth.workload("draft_131k_bf16", window=256)
+    case = synth.draft_case(wl, (700,))
+    sh = W.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16, wl.scale)
+    cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=1, seed=wl.seed)
+    q = case.q[0].contiguous().to(DEV)
+    lens = [case.n0[0]]
+    parts = W.draft_attn(W.FULL, sh, q, lens, W.workspace(W.draft_workspace_bytes(W.FULL, sh, lens, 64), DEV),
+                         paged=cache.desc, chunk_tokens=64)
+    ref = weakref.ref(parts._workspace)
+    gc.collect()
+    torch.empty(1 << 22, dtype=torch.uint8, device=DEV).fill_(255)      # would reuse a freed workspace
+    out, lse = run_combine(parts, wl.num_q_heads, wl.head_dim, 1)
+    torch.cuda.synchronize()
+    qf = O.to_f64(host_array(case.q[0], wl.dtype), wl.dtype)
+    k, v = host_array(case.k_ctx, wl.dtype), host_array(case.v_ctx, wl.dtype)
+    o_ref, l_ref = O.draft_attention(qf[0], O.LogicalKV(k[0], wl.dtype, lens[0]), O.LogicalKV(v[0], wl.dtype, lens[0]),
+                                     lens[0], O.FULL, wl.sink, wl.window, wl.scale)
+    assert max_err(out[0], o_ref) <= TOL["bf16"] and max_err(lse[0], l_ref) <= TOL["bf16"]
+    del parts
+    gc.collect()
+    assert ref() is None
+
+
 @pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
 @pytest.mark.parametrize("hq,hk", [(2, 2), (4, 2), (8, 2), (4, 1)])
 def test_draft_matrix_core_groupings(mode, hq, hk):
