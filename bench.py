@@ -41,8 +41,8 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "41065a3cb1ef6b9f0d5a70a39e9b8f6566888964e91cee57220987d36632d98c",
-                  "fetch_kib": 1049665.86, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_TRAFFIC = {"sources_sha256": "e3f2bf4045493ba208765ea5b877571c06f9d230321984a9aeac131d2b083e42",
+                  "fetch_kib": 1049671.18, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_row_tile.hpp",
                   "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
@@ -748,7 +748,7 @@ def main():
             "draft_native_per_step": round(dnat_ms * 1e3, 2),
         },
         "roofline": {
-            "kernel": "mfma_attn_kernel<8, false, false> (verify, 10 launches per step)",
+            "kernel": "mfma_attn_kernel<256, 8, false, false> (verify, 10 launches per step)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -78,10 +78,10 @@ extern "C" {
 /* Optional flag OR-ed into the draft mode (bf16 only): the PV product takes the
  * softmax weights rounded to bf16 (bf16 x bf16 products, fp32 sums) instead of
  * fp32 weights.  The normaliser is summed from the same rounded weights.  With
- * this flag and head_dim 256, both modes run on the matrix-core kernel of
- * wmtp_verify_attn with one query token (the same arithmetic), over the paged
- * pool or over the ring's visible entries; other shapes use v_dot2_f32_bf16
- * over key pairs.  Without it the PV product uses the fp32 weights. */
+ * this flag both modes run on the matrix-core kernel of wmtp_verify_attn with
+ * one query token (the same arithmetic), over the paged pool or over the
+ * ring's visible entries.  Without it the PV product uses the fp32 weights, on
+ * a kernel of vector dot products. */
 #define WMTP_DRAFT_FAST_PV 0x10
 
 #define WMTP_MAX_BATCH   64     /* sequences per call                                         */
@@ -189,10 +189,12 @@ int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const 
  *  chunk_tokens: entries per split (a multiple of 64).  0 = library default:
  *  the smallest multiple of 64 (at least 256 in WMTP_FULL mode, 64 in
  *  WMTP_SINK_WINDOW mode, at most 65536) for which the work items
- *  (sequence, KV head, split) fit one round of 256 (WMTP_FULL with rows of at
- *  least 512 bytes: one per MI355X compute unit) or 512 (WMTP_FULL with
- *  narrower rows, and WMTP_SINK_WINDOW) items, or of the smallest multiple of
- *  that holding one item per sequence and KV head.
+ *  (sequence, KV head, split) fit one round of 256 x max(1, 512 / row bytes)
+ *  items in WMTP_FULL mode (one per MI355X compute unit at head_dim 256 in
+ *  bf16; narrower rows run fewer waves per item, so more items) or 512 items
+ *  in WMTP_SINK_WINDOW mode, or of the smallest multiple of that holding one
+ *  item per sequence and KV head.  The count depends on the shape and mode
+ *  only, not on WMTP_DRAFT_FAST_PV.
  *  The call writes split partials into `workspace` (device, >= the size from
  *  wmtp_draft_workspace_bytes, 256-byte aligned) and describes them in
  *  *parts (host).  Finish with wmtp_combine. */
@@ -205,10 +207,11 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
  * (Windowed-MTP summary, Abstract: verification stays full-context).
  *  q: device [batch][t_q][H_q][D].  n_b = seq_lens_host[b] includes the t_q
  *  query tokens' own entries; query token i attends causally to positions
- *  0..n_b-t_q+i.  Requires t_q * G <= WMTP_MAX_VERIFY_ROWS, dtype bf16 and
- *  head_dim 256 (other shapes return WMTP_EUNSUPPORTED).
+ *  0..n_b-t_q+i.  Requires dtype bf16 and t_q * G <= WMTP_MAX_VERIFY_ROWS at
+ *  head_dim 256, t_q * G <= 32 at head_dim 64 and 128 (otherwise
+ *  WMTP_EUNSUPPORTED).
  *  split_tokens: entries per split (a multiple of 32; 0 = the WMTP_FULL draft
- *  default: one round of one work item per compute unit).
+ *  default for the shape: 256 x 256 / head_dim work items).
  *  Workspace and *parts as for wmtp_draft_attn. */
 int wmtp_verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv,
                      const int32_t* seq_lens_host, int32_t batch, int32_t split_tokens,

@@ -5,6 +5,7 @@
 // GPU.  Nothing here allocates, synchronises or keeps state between calls.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -150,11 +151,14 @@ int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, i
     vis[b] = upper_bound ? bound[b] : std::min<int64_t>(seq_lens[b], sb + wb);
   }
   if (chunk == 0) {
-    // Rows under 512 bytes run on the dot-product kernel with 4 waves per work item;
-    // two items per CU then keep enough loads in flight (measured at 1M keys: 4/1/64
-    // 137 -> 84 us, 8/1/128 175 -> 130 us, 4/2/128 244 -> 194 us).
+    // Narrower rows mean fewer waves per work item (one per 64 bf16 elements on the
+    // matrix-core kernel, 4 instead of 8 on the dot-product kernel below 512-byte
+    // rows): target proportionally more items, so a CU holds as many waves' loads
+    // (measured at 1M keys on the dot-product kernel: 4/1/64 137 -> 87 us, 8/1/128
+    // 175 -> 130 us, 4/2/128 244 -> 194 us).  The count depends on the shape only,
+    // so the workspace size does not depend on the PV flag.
     const int64_t row_bytes = (int64_t)shape->head_dim * elem_bytes(shape->dtype);
-    const int64_t full_slots = row_bytes < 512 ? 2 * kFullSlots : kFullSlots;
+    const int64_t full_slots = kFullSlots * std::max<int64_t>(1, 512 / row_bytes);
     chunk = base_mode == WMTP_FULL ? default_split(bound, batch, shape->num_kv_heads, full_slots, kFullMinSplit)
                                    : default_split(bound, batch, shape->num_kv_heads, kWindowSlots, kWindowMinSplit);
   }
@@ -167,17 +171,22 @@ int verify_plan(const wmtp_shape* shape, int32_t t_q, const int32_t* seq_lens, i
                 Plan* p, int32_t* split_out) {
   int st = check_shape(shape);
   if (st) return st;
-  if (shape->dtype != WMTP_BF16 || shape->head_dim != 256) return WMTP_EUNSUPPORTED;
+  if (shape->dtype != WMTP_BF16) return WMTP_EUNSUPPORTED;
   if (!seq_lens || batch < 1 || batch > WMTP_MAX_BATCH) return WMTP_EINVAL;
   if (t_q < 1) return WMTP_EINVAL;
   const int g = shape->num_q_heads / shape->num_kv_heads;
-  if ((int64_t)t_q * g > WMTP_MAX_VERIFY_ROWS) return WMTP_EUNSUPPORTED;
+  // head_dim 256: up to three row tiles of 32 packed rows; 64 and 128: one
+  const int64_t max_rows = shape->head_dim == 256 ? WMTP_MAX_VERIFY_ROWS : 32;
+  if ((int64_t)t_q * g > max_rows) return WMTP_EUNSUPPORTED;
   int64_t vis[WMTP_MAX_BATCH];
   for (int b = 0; b < batch; ++b) {
     if (seq_lens[b] < t_q) return WMTP_EINVAL;   // the queries' own keys are in the cache
     vis[b] = seq_lens[b];
   }
-  if (split == 0) split = default_split(vis, batch, shape->num_kv_heads, kFullSlots, kFullMinSplit);
+  // A work item runs one wave per 64 elements of head_dim: narrower heads get
+  // proportionally more items, so a CU still holds four waves' loads.
+  if (split == 0)
+    split = default_split(vis, batch, shape->num_kv_heads, kFullSlots * (256 / shape->head_dim), kFullMinSplit);
   if (split < kVerifyTile || split % kVerifyTile != 0) return WMTP_EINVAL;
   *split_out = split;
   return make_plan(vis, batch, split, t_q * shape->num_q_heads, shape->head_dim, shape->num_kv_heads, p);
@@ -310,7 +319,7 @@ int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_
   }
   const int grid = p.total * shape->num_kv_heads;
   const bool fast_pv = (mode & WMTP_DRAFT_FAST_PV) != 0 && shape->dtype == WMTP_BF16;
-  if (fast_pv && shape->head_dim == 256) {
+  if (fast_pv) {
     // A draft step is attention of a single query token, i.e. the verify
     // contraction with t_q = 1; both round p to bf16 before PV, so the G packed
     // rows run on the matrix-core kernel, which spends fewer vector instructions
@@ -319,8 +328,11 @@ int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_
     a.t_q = 1;
     const int group = shape->num_q_heads / shape->num_kv_heads;
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    return launch_status(base_mode == WMTP_FULL ? launch_verify(shape->head_dim, group, true, a, grid, st)
-                                                : launch_window_mfma(shape->head_dim, group, a, grid, st));
+    const bool window = base_mode == WMTP_SINK_WINDOW;
+    if (shape->head_dim != 256)
+      return launch_status(launch_row_tile_small(shape->head_dim, group, true, window, a, grid, st));
+    return launch_status(window ? launch_window_mfma(shape->head_dim, group, a, grid, st)
+                                : launch_verify(shape->head_dim, group, true, a, grid, st));
   }
   return launch_status(launch_draft(shape->dtype, shape->head_dim, shape->num_q_heads / shape->num_kv_heads,
                                     base_mode == WMTP_SINK_WINDOW, fast_pv, a, grid,
@@ -362,8 +374,11 @@ int verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_
   a.run_rows = run_rows_of(kv);
   a.t_q = t_q;
   const int grid = p.total * shape->num_kv_heads;
-  return launch_status(launch_verify(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, false, a, grid,
-                                     static_cast<hipStream_t>(stream)));
+  const int group = shape->num_q_heads / shape->num_kv_heads;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (shape->head_dim != 256)
+    return launch_status(launch_row_tile_small(shape->head_dim, group, false, false, a, grid, hs));
+  return launch_status(launch_verify(shape->head_dim, group, false, a, grid, hs));
 }
 
 }  // namespace

@@ -47,6 +47,10 @@ hipError_t launch_draft(int dtype, int head_dim, int group, bool window, bool pv
 hipError_t launch_verify(int head_dim, int group, bool single_query, const SplitArgs& a, int grid, hipStream_t st);
 // The same kernel for one query token over the ring's visible entries (window mode).
 hipError_t launch_window_mfma(int head_dim, int group, const SplitArgs& a, int grid, hipStream_t st);
+// The one-row-tile kernel at head_dim 64 or 128 (one or two waves per work item):
+// verify of up to 32 packed rows, or a draft step over the paged pool or the ring.
+hipError_t launch_row_tile_small(int head_dim, int group, bool single_query, bool ring, const SplitArgs& a, int grid,
+                                 hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_ring_append(const AppendArgs& a, int batch, hipStream_t st);
 hipError_t launch_paged_append(const AppendArgs& a, int batch, hipStream_t st);

@@ -71,10 +71,10 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 // k-step s -> piece 2s + kh of the row's quarter; zero for padding rows.  The
 // loads are settled here, so none is still pending at the header of the main
 // loop (which would force a full drain per tile).
-template <int G>
+template <int D, int G>
 __device__ __forceinline__ void load_q_quarter(u32x4 (&qreg)[kVKS], const SplitArgs& a, int b, int h, int tq,
                                                int rows, int wave, int c32, int kh) {
-  constexpr int ROWB = kVD * 2;
+  constexpr int ROWB = D * 2;
   const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
   const int j = c32;
   const int i = j / G, g = j % G;
@@ -95,14 +95,16 @@ __device__ __forceinline__ void load_q_quarter(u32x4 (&qreg)[kVKS], const SplitA
 // visible entries of the compact ring (sinks, then the window) instead of a
 // paged context; each lane addresses its keys by ring slot, and a key whose
 // slot tag does not hold its position (a hole) is masked.
-template <int G, bool SINGLE, bool RING>
-__global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
+template <int D, int G, bool SINGLE, bool RING>
+__global__ __launch_bounds__(D / kVQ * 64, 8 / (D / kVQ)) void mfma_attn_kernel(const SplitArgs a) {
   static_assert(!RING || SINGLE, "the ring serves the one-query draft step");
-  constexpr int ROWB = kVD * 2;
+  static_assert(D == 64 || D == 128 || D == 256, "head_dim: one, two or four 64-element wave slices");
+  constexpr int ROWB = D * 2;
+  constexpr int NW = D / kVQ;                // waves, one 64-element slice of D each
   constexpr float TAU = 8.0f;
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[4 * kVStage];
-  __shared__ __attribute__((aligned(16))) float sc_lds[2 * 4 * 16 * 64];   // [buf][wave][4][lane][4]
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[NW * kVStage];
+  __shared__ __attribute__((aligned(16))) float sc_lds[2 * NW * 16 * 64];   // [buf][wave][4][lane][4]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
       const u32x4 ka = *reinterpret_cast<const u32x4*>(my_k + vpiece(c32, 2 * s + kh) * 16);
       sacc = mfma32(ka, qreg[s], sacc);
     }
-    float* sc = sc_lds + (it & 1) * (4 * 16 * 64);
+    float* sc = sc_lds + (it & 1) * (NW * 16 * 64);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 w4 = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
     for (int q = 0; q < 4; ++q) {
       f32x4 x = *reinterpret_cast<const f32x4*>(sc + (q * 64 + lane) * 4);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) x += *reinterpret_cast<const f32x4*>(sc + ((w * 4 + q) * 64 + lane) * 4);
+      for (int w = 1; w < NW; ++w) x += *reinterpret_cast<const f32x4*>(sc + ((w * 4 + q) * 64 + lane) * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) s2[4 * q + e] = x[e];
     }
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
     }
     tile_runs(kRing - 1, run_next);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (RING) load_q_quarter<G>(qreg, a, b, h, tq, rows, wave, c32, kh);
+    if constexpr (RING) load_q_quarter<D, G>(qreg, a, b, h, tq, rows, wave, c32, kh);
     int it = 0;
     for (; it + 3 <= ntiles; it += 3) {
       body(it, 0);
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(const SplitArgs a) {
       float2 w2;
       w2.x = O[0][x] * inv;
       w2.y = O[1][x] * inv;
-      *reinterpret_cast<float2*>(a.part_o + orow * kVD + wave * kVQ + 2 * c32) = w2;
+      *reinterpret_cast<float2*>(a.part_o + orow * D + wave * kVQ + 2 * c32) = w2;
     }
   }
   if (wave == 0 && lane < rows && lane < 32) {

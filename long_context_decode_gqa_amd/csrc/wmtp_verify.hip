@@ -399,10 +399,10 @@ __global__ __launch_bounds__(512, 1) void mfma_attn_teams_kernel(const SplitArgs
 template <int G>
 static hipError_t launch_rt(int rt, bool single, const SplitArgs& a, int grid, hipStream_t st) {
   if (single) {
-    mfma_attn_kernel<G, true, false><<<grid, 256, 0, st>>>(a);
+    mfma_attn_kernel<kVD, G, true, false><<<grid, 256, 0, st>>>(a);
   } else {
     switch (rt) {
-      case 1: mfma_attn_kernel<G, false, false><<<grid, 256, 0, st>>>(a); break;
+      case 1: mfma_attn_kernel<kVD, G, false, false><<<grid, 256, 0, st>>>(a); break;
       case 2: mfma_attn_teams_kernel<G, 2><<<grid, 512, 0, st>>>(a); break;
       case 3: mfma_attn_teams_kernel<G, 3><<<grid, 512, 0, st>>>(a); break;
       default: return hipErrorInvalidValue;

@@ -11,7 +11,7 @@ namespace wmtp {
 
 template <int G>
 static hipError_t launch_ring(const SplitArgs& a, int grid, hipStream_t st) {
-  mfma_attn_kernel<G, true, true><<<grid, 256, 0, st>>>(a);
+  mfma_attn_kernel<kVD, G, true, true><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -455,13 +455,14 @@ def test_partials_keep_their_workspace_alive():
 
 
 @pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
-@pytest.mark.parametrize("hq,hk", [(2, 2), (4, 2), (8, 2), (4, 1)])
-def test_draft_matrix_core_groupings(mode, hq, hk):
-    """bf16 PV weights at d = 256 run the draft step on the matrix-core kernel in both modes
-    (paged pool or ring); every query-head grouping G = 1, 2, 4 it is built for, beside the
-    benchmark's G = 8, with fused appends, several splits and a wrapped ring."""
-    wl = synth.workload("draft_131k_bf16", num_q_heads=hq, num_kv_heads=hk, head_dim=256, window=300)
-    say("draft matrix-core groupings", mode, hq, hk)
+@pytest.mark.parametrize("hq,hk,d", [(2, 2, 256), (4, 2, 256), (8, 2, 256), (4, 1, 256),
+                                     (4, 2, 128), (8, 1, 128), (2, 2, 128), (4, 1, 64), (8, 8, 64), (16, 2, 64)])
+def test_draft_matrix_core_groupings(mode, hq, hk, d):
+    """bf16 PV weights run the draft step on the matrix-core kernel in both modes (paged pool or
+    ring): every query-head grouping G = 1, 2, 4, 8 at head_dim 256, 128 and 64 (four, two or one
+    wave per work item), with fused appends, several splits and a wrapped ring."""
+    wl = synth.workload("draft_131k_bf16", num_q_heads=hq, num_kv_heads=hk, head_dim=d, window=300)
+    say("draft matrix-core groupings", mode, hq, hk, d)
     eo, el = draft_steps(wl, (1500, 77), mode, chunk=128, fast_pv=True, fused=True, headroom=2)
     assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
 
@@ -540,6 +541,22 @@ def test_verify_row_packings(t_q, hq, hk):
     wl = synth.workload("step_1m_bf16", num_q_heads=hq, num_kv_heads=hk)
     say("verify rows", t_q, hq, hk)
     eo, el = verify_run(wl, (1234,), t_q, 128)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("t_q,hq,hk,contexts,split,fused,interleaved", [
+    (4, 16, 2, (1234,), 64, False, False),          # G = 8: one full row tile
+    (1, 8, 2, (0, 777), 0, True, False),            # G = 4, a sequence with no context
+    (3, 4, 4, (300, 5000), 32, False, True),        # G = 1, K|V runs
+    (8, 8, 2, (2044, 17), 256, True, True),         # G = 4, 32 rows, tokens across a split boundary
+    (2, 16, 2, (200000,), 0, False, False),         # a long context, default splits
+])
+def test_verify_small_head_dims(d, t_q, hq, hk, contexts, split, fused, interleaved):
+    """Verify at head_dim 64 and 128 (one or two waves per work item, up to 32 packed rows)."""
+    wl = synth.workload("step_1m_bf16", num_q_heads=hq, num_kv_heads=hk, head_dim=d)
+    say("verify small d", d, t_q, hq, hk, contexts, split, fused, interleaved)
+    eo, el = verify_run(wl, contexts, t_q, split, fused=fused, interleaved=interleaved)
     assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
 
 
