@@ -61,6 +61,14 @@ def verify_sources_sha256() -> str:
     return h.hexdigest()
 
 
+def verify_kernel_name(t_q, group):
+    """The kernel a verify launch of t_q queries at G = group, head_dim 256, runs on."""
+    row_tiles = (t_q * group + 31) // 32
+    if row_tiles == 1:
+        return f"mfma_attn_kernel<256, {group}, false, false>"
+    return f"mfma_attn_teams_kernel<{group}, {row_tiles}>"
+
+
 def verify_traffic_bytes():
     t = VERIFY_TRAFFIC
     if t["fetch_kib"] is None or t["sources_sha256"] != verify_sources_sha256():
@@ -627,6 +635,7 @@ def main():
     # slow for a few ms, and settle after ~20 ms of load; the warmup absorbs that
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--context", type=int, default=1 << 20)
+    ap.add_argument("--gamma", type=int, default=3, help="draft steps per decode step (verify takes gamma + 1 queries)")
     ap.add_argument("--chunk-full", type=int, default=0, help="draft split size, native mode (0 = library default)")
     ap.add_argument("--chunk-window", type=int, default=0, help="draft split size, window mode (0 = default)")
     ap.add_argument("--split", type=int, default=0, help="verify split size (0 = library default)")
@@ -666,7 +675,7 @@ def main():
                           "data": "synthetic", "dtype": "bf16", "n_gpus": 1, "steps": args.steps,
                           "warmup": args.warmup, "rows": rows}), flush=True)
         return
-    wl = synth.workload("step_1m_bf16", contexts=(args.context,))
+    wl = synth.workload("step_1m_bf16", contexts=(args.context,), gamma=args.gamma)
     n0 = args.context
     log("streaming-read ceiling")
     ceiling = stream_ceiling_gbps(dev)
@@ -748,13 +757,14 @@ def main():
             "draft_native_per_step": round(dnat_ms * 1e3, 2),
         },
         "roofline": {
-            "kernel": "mfma_attn_kernel<256, 8, false, false> (verify, 10 launches per step)",
+            "kernel": (f"{verify_kernel_name(g + 1, wl.group)} (verify, {wl.target_layers} launches per step)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": verify_traffic_bytes(),
+            # counters were taken on the default workload (1M keys, gamma 3, K|V-run pools)
+            "traffic": (verify_traffic_bytes() if (n0, g, args.pool_layout) == (1 << 20, 3, "kv_runs") else None),
             "algorithmic_bytes": ver_bytes,
             "measured_read_ceiling": round(ceiling, 1),
             "frac_of_measured_ceiling": round(achieved / ceiling, 4),
