@@ -41,10 +41,10 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "e3f2bf4045493ba208765ea5b877571c06f9d230321984a9aeac131d2b083e42",
+VERIFY_TRAFFIC = {"sources_sha256": "e542efdf8b92e7ab8428e1eb3f0a9892f34bc4018ae41bbf558931851ecb7d3d",
                   "fetch_kib": 1049671.18, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_row_tile.hpp",
-                  "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
+                  "long_context_decode_gqa_amd/csrc/wmtp_teams.hpp", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
 
 def verify_sources_sha256() -> str:
@@ -66,7 +66,7 @@ def verify_kernel_name(t_q, group):
     row_tiles = (t_q * group + 31) // 32
     if row_tiles == 1:
         return f"mfma_attn_kernel<256, {group}, false, false>"
-    return f"mfma_attn_teams_kernel<{group}, {row_tiles}>"
+    return f"mfma_attn_teams_kernel<256, {group}, {row_tiles}>"
 
 
 def verify_traffic_bytes():

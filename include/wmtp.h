@@ -207,9 +207,8 @@ int wmtp_draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const 
  * (Windowed-MTP summary, Abstract: verification stays full-context).
  *  q: device [batch][t_q][H_q][D].  n_b = seq_lens_host[b] includes the t_q
  *  query tokens' own entries; query token i attends causally to positions
- *  0..n_b-t_q+i.  Requires dtype bf16 and t_q * G <= WMTP_MAX_VERIFY_ROWS at
- *  head_dim 256, t_q * G <= 32 at head_dim 64 and 128 (otherwise
- *  WMTP_EUNSUPPORTED).
+ *  0..n_b-t_q+i.  Requires dtype bf16 and t_q * G <= WMTP_MAX_VERIFY_ROWS
+ *  (otherwise WMTP_EUNSUPPORTED).
  *  split_tokens: entries per split (a multiple of 32; 0 = the WMTP_FULL draft
  *  default for the shape: 256 x 256 / head_dim work items).
  *  Workspace and *parts as for wmtp_draft_attn. */

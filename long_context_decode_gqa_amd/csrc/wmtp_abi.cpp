@@ -175,9 +175,8 @@ int verify_plan(const wmtp_shape* shape, int32_t t_q, const int32_t* seq_lens, i
   if (!seq_lens || batch < 1 || batch > WMTP_MAX_BATCH) return WMTP_EINVAL;
   if (t_q < 1) return WMTP_EINVAL;
   const int g = shape->num_q_heads / shape->num_kv_heads;
-  // head_dim 256: up to three row tiles of 32 packed rows; 64 and 128: one
-  const int64_t max_rows = shape->head_dim == 256 ? WMTP_MAX_VERIFY_ROWS : 32;
-  if ((int64_t)t_q * g > max_rows) return WMTP_EUNSUPPORTED;
+  // up to three row tiles of 32 packed rows
+  if ((int64_t)t_q * g > WMTP_MAX_VERIFY_ROWS) return WMTP_EUNSUPPORTED;
   int64_t vis[WMTP_MAX_BATCH];
   for (int b = 0; b < batch; ++b) {
     if (seq_lens[b] < t_q) return WMTP_EINVAL;   // the queries' own keys are in the cache

@@ -195,8 +195,8 @@ def test_workspace_sizes_follow_the_split_plan():
 
 @pytest.mark.parametrize("args,status", [
     (dict(sh=shape(dt=W.F32)), W.EUNSUPPORTED),
-    (dict(sh=shape(d=128), t_q=5), W.EUNSUPPORTED),                # d < 256: one row tile, 5 x 8 rows > 32
-    (dict(sh=shape(d=64), t_q=5), W.EUNSUPPORTED),
+    (dict(sh=shape(d=128), t_q=13), W.EUNSUPPORTED),               # 13 x 8 rows > 96 at every head_dim
+    (dict(sh=shape(d=64), t_q=13), W.EUNSUPPORTED),
     (dict(t_q=0), W.EINVAL),
     (dict(t_q=13), W.EUNSUPPORTED),                              # 13 x 8 rows > 96
     (dict(seq=(3,)), W.EINVAL),                                  # fewer keys than queries

@@ -551,9 +551,16 @@ def test_verify_row_packings(t_q, hq, hk):
     (3, 4, 4, (300, 5000), 32, False, True),        # G = 1, K|V runs
     (8, 8, 2, (2044, 17), 256, True, True),         # G = 4, 32 rows, tokens across a split boundary
     (2, 16, 2, (200000,), 0, False, False),         # a long context, default splits
+    (6, 16, 2, (29, 300), 32, True, False),         # G = 8, 48 rows: two row tiles (two wave teams)
+    (9, 16, 2, (2044, 17), 256, True, True),        # 72 rows: three row tiles, straddling a split
+    (12, 8, 1, (5000,), 0, False, False),           # 96 rows, the maximum
+    (33, 1, 1, (100, 40), 32, True, False),         # G = 1, 33 rows: a second row tile of one row
+    (40, 4, 2, (3000, 41), 64, False, True),        # G = 2, 80 rows, a ragged third row tile
 ])
 def test_verify_small_head_dims(d, t_q, hq, hk, contexts, split, fused, interleaved):
-    """Verify at head_dim 64 and 128 (one or two waves per work item, up to 32 packed rows)."""
+    """Verify at head_dim 64 and 128: one or two waves per work item up to 32 packed
+    rows; two wave teams (one loader wave per slice of D, one compute wave per row
+    tile) for 33..96 rows."""
     wl = synth.workload("step_1m_bf16", num_q_heads=hq, num_kv_heads=hk, head_dim=d)
     say("verify small d", d, t_q, hq, hk, contexts, split, fused, interleaved)
     eo, el = verify_run(wl, contexts, t_q, split, fused=fused, interleaved=interleaved)
