@@ -9,12 +9,14 @@ namespace wmtp {
 // (o_i, lse_i); the result over the union is
 //   L = log sum_i exp(lse_i),  o = sum_i exp(lse_i - L) o_i.
 // Workgroup = (sequence b, row r, 32-float slice of D: one 128-byte line per
-// split).  Its 256 threads are 8 lanes across the slice (16 bytes each) x 32
+// split).  Its NW waves are 8 lanes across the slice (16 bytes each) x 8 NW
 // split lanes.  Every thread merges its own splits (all loads independent),
-// then the 8 split lanes of a wave are merged with a shuffle tree and the 4
-// waves through LDS.
+// then the 8 split lanes of a wave are merged with a shuffle tree and the NW
+// waves through LDS.  A thread merges up to PER (4 or 8) splits per round of
+// loads, and NW grows with the splits of the longest sequence, so up to 1,024
+// splits take one round: with a fixed 4 waves the 1,024 splits of a
+// one-KV-head draft at head_dim 64 over 1M keys gave each thread 32 splits.
 constexpr int kCombineDL = 8;                     // lanes across a D slice (128 bytes)
-constexpr int kCombineSL = 256 / kCombineDL;      // split lanes
 
 struct MergeState {
   float m, w;
@@ -29,8 +31,10 @@ __device__ __forceinline__ MergeState merge_state(const MergeState& x, const Mer
   return {m, x.w * fx + y.w * fy, x.acc * fx + y.acc * fy};
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  __shared__ MergeState sm[4][kCombineDL];
+template <int NW, int PER>
+__global__ __launch_bounds__(NW * 64) void combine_kernel(const CombineArgs a) {
+  constexpr int SL = NW * 64 / kCombineDL;        // split lanes
+  __shared__ MergeState sm[NW][kCombineDL];
   const int slices = a.head_dim / (4 * kCombineDL);
   const int slice = blockIdx.x % slices;
   const int br = blockIdx.x / slices;             // b * rows + r
@@ -42,21 +46,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int d0 = slice * 4 * kCombineDL + dl * 4;
 
   // One pass over this thread's splits, merging each (lse, o) into a running
-  // (m, w, acc) in log2 units: the lse and o loads of all the thread's splits
-  // are independent, so they are in flight together.  An empty split carries
-  // lse = -inf and o = 0 and is skipped.
+  // (m, w, acc) in log2 units.  The loads of up to PER splits
+  // are issued before any of them is used: indexes past the sequence's last
+  // split are clamped to its first and weighted out, and the merge has no
+  // branch, so the loads of a round are in flight together (a branch per split
+  // made each split one memory round trip of its own).  An empty split carries
+  // lse = -inf and o = 0 and gets weight 0.
   MergeState st;
   st.m = kNegInf;
   st.w = 0.f;
   st.acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = s0 + sl; s < s1; s += kCombineSL) {
-    const float l = a.part_lse[(int64_t)s * a.rows + r] * kLog2e;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)s * a.rows + r) * a.head_dim + d0);
-    if (l != kNegInf) {
-      const float mn = fmaxf(st.m, l);
-      const float fa = exp2f(st.m - mn), fb = exp2f(l - mn);   // st.m = -inf gives fa = 0
-      st.acc = st.acc * fa + fb * x;
+  for (int base = s0 + sl; base < s1; base += PER * SL) {
+    float l[PER];
+    f32x4 x[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int s = base + k * SL;
+      const int sc = s < s1 ? s : s0;
+      const float ls = a.part_lse[(int64_t)sc * a.rows + r];
+      l[k] = s < s1 ? ls * kLog2e : kNegInf;
+      x[k] = *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)sc * a.rows + r) * a.head_dim + d0);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const float mn = fmaxf(st.m, l[k]);
+      const float ref = mn == kNegInf ? 0.f : mn;       // both -inf: fa = fb = 0
+      const float fa = exp2f(st.m - ref), fb = exp2f(l[k] - ref);
+      st.acc = st.acc * fa + fb * x[k];
       st.w = st.w * fa + fb;
       st.m = mn;
     }
@@ -81,7 +97,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   if (threadIdx.x >= kCombineDL) return;
   MergeState t = sm[0][dl];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) t = merge_state(t, sm[w][dl]);
+  for (int w = 1; w < NW; ++w) t = merge_state(t, sm[w][dl]);
   const float inv = t.w > 0.f ? 1.f / t.w : 0.f;
   const int64_t orow = ((int64_t)b * a.rows + r) * a.head_dim + d0;
   if (a.out_bf16) {
@@ -99,7 +115,17 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int slices = a.head_dim / (4 * kCombineDL);
   const int grid = a.batch * a.rows * slices;
   if (grid <= 0) return hipSuccess;
-  combine_kernel<<<grid, 256, 0, st>>>(a);
+  int most = 0;
+  for (int b = 0; b < a.batch; ++b) most = std::max(most, a.split_base[b + 1] - a.split_base[b]);
+  constexpr int L = 64 / kCombineDL;   // split lanes per wave
+  if (most <= 4 * L * 4)
+    combine_kernel<4, 4><<<grid, 4 * 64, 0, st>>>(a);
+  else if (most <= 4 * L * 8)
+    combine_kernel<4, 8><<<grid, 4 * 64, 0, st>>>(a);
+  else if (most <= 8 * L * 8)
+    combine_kernel<8, 8><<<grid, 8 * 64, 0, st>>>(a);
+  else
+    combine_kernel<16, 8><<<grid, 16 * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
