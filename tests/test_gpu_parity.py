@@ -6,6 +6,7 @@ accumulation).  Inputs come from `synth` with the workloads' shapes at context
 lengths the oracle finishes in seconds, spanning several tiles and splits with
 ragged tails; the 1M-token cases compare sampled KV heads.
 """
+import math
 import sys
 
 import numpy as np
@@ -949,6 +950,45 @@ def test_mixed_batch_full_sizes():
         eo, el = max_err(out[b, rows], o_ref), max_err(lse[b, rows], l_ref)
         assert eo <= TOL["bf16"] and el <= TOL["bf16"], ("full", b, eo, el)
 
+
+
+# ============================================================== LSE combine alone
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("counts", [(1, 5, 0, 100), (200,), (400, 3), (700,), (1500, 1)])
+def test_combine_synthetic_partials(counts, D):
+    """wmtp_combine on seeded partials whose split counts reach every workgroup shape the
+    launch picks (4 waves x 4 splits per thread up to 128 splits, 4 x 8 up to 256, 8 x 8 up
+    to 512, 16 x 8 beyond, two rounds of loads at 1,500), with a sequence of no splits and
+    about 10% empty splits (lse = -inf, o = 0); lse spread over N(0, 5^2).  Checked against
+    the oracle's float64 merge within the fp32 tolerance."""
+    rows, B = 3, len(counts)
+    say(f"combine counts={counts} D={D}")
+    base = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    P = int(base[-1])
+    o = synth.normal((P, rows, D), 7, ("comb_o", D, P), 1.0, "f32")
+    lse = synth.normal((P, rows), 7, ("comb_lse", D, P), 5.0, "f32")
+    empty = synth.normal((P, rows), 7, ("comb_empty", D, P), 1.0, "f32") > 1.2816   # ~10%
+    lse[empty] = -math.inf
+    o[empty] = 0.0
+    parts = W.Partials()
+    od, ld = o.to(DEV), lse.to(DEV)
+    parts.o, parts.lse = od.data_ptr(), ld.data_ptr()
+    parts.batch, parts.rows_per_seq, parts.head_dim, parts.total_splits = B, rows, D, P
+    for b in range(B + 1):
+        parts.split_base[b] = int(base[b])
+    out, lse_out = run_combine(parts, rows, D, B)
+    torch.cuda.synchronize()
+    on, ln = o.double().numpy(), lse.double().numpy()
+    for b in range(B):
+        o_ref, l_ref = O.lse_combine(on[base[b]:base[b + 1]], ln[base[b]:base[b + 1]])
+        got_o, got_l = out[b].double().cpu().numpy(), lse_out[b].double().cpu().numpy()
+        if counts[b] == 0:
+            assert np.all(got_o == 0.0) and np.all(np.isneginf(got_l))
+            continue
+        fin = np.isfinite(l_ref)
+        assert np.array_equal(np.isfinite(got_l), fin), (b, got_l, l_ref)
+        assert np.abs(got_o - o_ref).max() <= TOL["f32"], (b, np.abs(got_o - o_ref).max())
+        assert np.abs(got_l[fin] - l_ref[fin]).max(initial=0.0) <= TOL["f32"] * max(1.0, np.abs(l_ref[fin]).max(initial=0.0))
 
 
 # ============================================================== HIP graph capture
