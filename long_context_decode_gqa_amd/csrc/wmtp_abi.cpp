@@ -27,13 +27,16 @@ constexpr int kVerifyTile = 32;    // keys per verify tile
 // round.  Full-context launches target 256 slots, one item per MI355X compute
 // unit: each CU streams one long run of blocks, measured faster than two
 // co-resident items per CU at 1M keys (rows of 512 bytes or more; narrower
-// rows target twice as many, see draft_plan).  The window draft is latency-bound and
-// its items fit two per CU (512-thread dot-product or 256-thread matrix-core
-// items), so it targets 512 slots with splits of at least 64 entries: longer
-// items add a memory round trip of latency per 64 entries.
+// rows target twice as many, see draft_plan).  Below about 32K keys the
+// items are short and the launch is latency-bound: there the smallest split
+// (64 entries) halves verify's launch at 2K keys against a floor of 256
+// (8.1 against 14.4 us).  The window draft is latency-bound and its items fit
+// two per CU (512-thread dot-product or 256-thread matrix-core items), so it
+// targets 512 slots: longer items add a memory round trip of latency per 64
+// entries.
 constexpr int64_t kFullSlots = 256;
 constexpr int64_t kWindowSlots = 512;
-constexpr int64_t kFullMinSplit = 256;
+constexpr int64_t kFullMinSplit = 64;
 constexpr int64_t kWindowMinSplit = 64;
 constexpr int64_t kMaxDefaultSplit = 65536;
 

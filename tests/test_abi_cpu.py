@@ -144,23 +144,27 @@ def _rule(vis, hk, slots, lo):
 @pytest.mark.parametrize("lens", [[1048577], [1048580], [262144] * 4, [32769, 131073, 524289, 1048577], [1000],
                                   [5, 70000, 3, 9000, 1 << 20]])
 def test_default_split_fits_one_round_of_work_items(lens):
-    # 0 = library default: the smallest split (multiple of 64, >= 256) whose work
-    # items (sequence, KV head, split) fit one round of 256 (one per compute unit)
+    # 0 = library default: the smallest split (multiple of 64) whose work items
+    # (sequence, KV head, split) fit one round of 256 (one per compute unit)
     sh = shape()                                                   # 2 KV heads
-    s = _rule(lens, 2, 256, 256)
+    s = _rule(lens, 2, 256, 64)
     assert W.draft_workspace_bytes(W.FULL, sh, lens, 0) == W.draft_workspace_bytes(W.FULL, sh, lens, s)
     if min(lens) >= 4:
         assert W.verify_workspace_bytes(sh, 4, lens, 0) == W.verify_workspace_bytes(sh, 4, lens, s)
     total = _splits_of(W.draft_workspace_bytes(W.FULL, sh, lens, 0), 16, 256)
     assert total * 2 <= 256
-    if s > 256:                                                    # minimal: one tile less does not fit
+    if s > 64:                                                     # minimal: one tile less does not fit
         assert 2 * sum(-(-v // (s - 64)) for v in lens) > 256
 
 
 def test_default_split_values():
     sh = shape()
-    assert _rule([1048577], 2, 256, 256) == 8256                   # 128 splits x 2 heads = 256 items
-    assert _rule([32769, 131073, 524289, 1048577], 2, 256, 256) > 13568   # plain division would give 260 items
+    assert _rule([1048577], 2, 256, 64) == 8256                    # 128 splits x 2 heads = 256 items
+    assert _rule([32769, 131073, 524289, 1048577], 2, 256, 64) > 13568    # plain division would give 260 items
+    # short contexts: splits of 64 entries (two verify tiles), not a floor of 256
+    assert _rule([2052], 2, 256, 64) == 64
+    assert W.verify_workspace_bytes(sh, 4, [2052], 0) == W.verify_workspace_bytes(sh, 4, [2052], 64)
+    assert W.draft_workspace_bytes(W.FULL, sh, [8193], 0) == W.draft_workspace_bytes(W.FULL, sh, [8193], 128)
     # very long contexts hit the 65536 cap
     big = shape(hq=64, hk=8)
     assert W.draft_workspace_bytes(W.FULL, big, [8 << 20], 0) == W.draft_workspace_bytes(W.FULL, big, [8 << 20], 65536)
