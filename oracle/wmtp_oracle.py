@@ -392,8 +392,12 @@ def memory_plan(num_kv_heads: int, head_dim: int, elem_bytes: int, target_layers
     Reading: every full-attention layer, target or native draft, keeps a paged
     pool of ceil(context / block_size) blocks of K and V; one int32 block table
     per sequence serves all of them; the windowed draft keeps only its ring
-    (S + W + R slots of K and V plus an int32 tag per slot).
+    (S + W + R slots of K and V plus an int32 tag per slot).  The reclaimed
+    share is a fraction of the sequence's KV, so a sequence must hold some:
+    context >= 1, else ValueError.
     """
+    if context < 1:
+        raise ValueError("the reclaimed share is defined for a context of at least one token")
     blocks = -(-context // block_size)
     layer = blocks * block_size * num_kv_heads * head_dim * elem_bytes * 2
     table = blocks * 4
@@ -401,12 +405,11 @@ def memory_plan(num_kv_heads: int, head_dim: int, elem_bytes: int, target_layers
     target = target_layers * layer
     native = target + layer + table
     windowed = target + ring + table
-    # a sequence that needs no bytes (no context and no target layer) is reported as 0, not infinity
     return {
         "layer_bytes": layer, "block_table_bytes": table, "ring_bytes": ring,
         "native_seq_bytes": native, "windowed_seq_bytes": windowed,
-        "reclaimed_fraction": (native - windowed) / native if native else 0.0,
-        "native_sequences": budget_bytes // native if native else 0,
-        "windowed_sequences": budget_bytes // windowed if windowed else 0,
+        "reclaimed_fraction": (native - windowed) / native,
+        "native_sequences": budget_bytes // native,
+        "windowed_sequences": budget_bytes // windowed,
     }
 
