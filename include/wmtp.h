@@ -86,6 +86,10 @@ extern "C" {
 
 #define WMTP_MAX_BATCH   64     /* sequences per call                                         */
 #define WMTP_BLOCK_SIZE  16     /* tokens per paged block                                     */
+/* Longest sequence (cache length, and first position + new tokens of an append) a
+ * call accepts: 2^30 tokens keeps every position, split end and block index of the
+ * kernels inside 32-bit arithmetic.  Longer lengths give WMTP_EINVAL. */
+#define WMTP_MAX_SEQ_LEN (1 << 30)
 #define WMTP_MAX_VERIFY_ROWS 96 /* t_q * G per KV head in one verify call (3 tiles of 32 rows) */
 
 /* ---------------------------------------------------------------- descriptors */
@@ -253,7 +257,7 @@ int wmtp_verify_attn_append(const wmtp_shape* shape, const void* q, int32_t t_q,
  *  out: device [batch][rows_per_seq][D], dtype out_dtype (WMTP_F32 or
  *  WMTP_BF16, round-to-nearest-even).  lse_out: device [batch][rows_per_seq]
  *  fp32, or NULL. */
-int wmtp_combine(const wmtp_partials* parts, void* out, int32_t out_dtype, float* lse_out, void* stream);
+int wmtp_combine(const wmtp_partials* parts, void* out, float* lse_out, int32_t out_dtype, void* stream);
 
 /* Append t_new tokens per sequence to the compact ring (Windowed-MTP summary,
  * Abstract: the ring holds the draft's window).  Token i of sequence b has
@@ -324,10 +328,10 @@ typedef struct wmtp_memory_plan {
   int64_t windowed_sequences;   /* floor(budget / windowed_seq_bytes)           */
 } wmtp_memory_plan;
 
-/* Fill *out (host).  context >= 0, target_layers >= 0, budget_bytes >= 0,
- * sink/window/headroom as in wmtp_ring.  A sequence that needs no bytes (no
- * context and no target layer) gets fraction 0 and 0 sequences.  Makes no HIP
- * call; WMTP_EINVAL on invalid arguments or int64 overflow. */
+/* Fill *out (host).  context >= 1 (the reclaimed share is a fraction of a
+ * sequence's KV, undefined for a sequence that holds none), target_layers >= 0,
+ * budget_bytes >= 0, sink/window/headroom as in wmtp_ring.  Makes no HIP call;
+ * WMTP_EINVAL on invalid arguments or int64 overflow. */
 int wmtp_plan_memory(const wmtp_shape* shape, int32_t target_layers, int64_t context, int32_t sink,
                      int32_t window, int32_t headroom, int64_t budget_bytes, wmtp_memory_plan* out);
 

@@ -142,7 +142,7 @@ int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, i
   const int64_t ring_slots = (int64_t)sink + window + headroom;
   int64_t vis[WMTP_MAX_BATCH], bound[WMTP_MAX_BATCH];
   for (int b = 0; b < batch; ++b) {
-    if (seq_lens[b] < 0) return WMTP_EINVAL;
+    if (seq_lens[b] < 0 || seq_lens[b] > WMTP_MAX_SEQ_LEN) return WMTP_EINVAL;
     if (base_mode == WMTP_FULL) {
       vis[b] = bound[b] = seq_lens[b];
       continue;
@@ -182,7 +182,7 @@ int verify_plan(const wmtp_shape* shape, int32_t t_q, const int32_t* seq_lens, i
   if ((int64_t)t_q * g > WMTP_MAX_VERIFY_ROWS) return WMTP_EUNSUPPORTED;
   int64_t vis[WMTP_MAX_BATCH];
   for (int b = 0; b < batch; ++b) {
-    if (seq_lens[b] < t_q) return WMTP_EINVAL;   // the queries' own keys are in the cache
+    if (seq_lens[b] < t_q || seq_lens[b] > WMTP_MAX_SEQ_LEN) return WMTP_EINVAL;   // the queries' keys are cached
     vis[b] = seq_lens[b];
   }
   // A work item runs one wave per 64 elements of head_dim: narrower heads get
@@ -280,7 +280,7 @@ int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_
     st = check_paged(kv, true);
     if (st) return st;
     for (int b = 0; b < batch; ++b)
-      if ((int64_t)(seq_lens_host[b] + WMTP_BLOCK_SIZE - 1) / WMTP_BLOCK_SIZE > kv->max_blocks_per_seq)
+      if (((int64_t)seq_lens_host[b] + WMTP_BLOCK_SIZE - 1) / WMTP_BLOCK_SIZE > kv->max_blocks_per_seq)
         return WMTP_EINVAL;
   }
   if (base_mode == WMTP_SINK_WINDOW &&
@@ -353,7 +353,7 @@ int verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_
   st = check_paged(kv, true);
   if (st) return st;
   for (int b = 0; b < batch; ++b)
-    if ((int64_t)(seq_lens_host[b] + WMTP_BLOCK_SIZE - 1) / WMTP_BLOCK_SIZE > kv->max_blocks_per_seq)
+    if (((int64_t)seq_lens_host[b] + WMTP_BLOCK_SIZE - 1) / WMTP_BLOCK_SIZE > kv->max_blocks_per_seq)
       return WMTP_EINVAL;
   if (!workspace && p.bytes > 0) return WMTP_EINVAL;
   if (!aligned(workspace, 256)) return WMTP_EALIGN;
@@ -419,7 +419,7 @@ int wmtp_verify_attn_append(const wmtp_shape* shape, const void* q, int32_t t_q,
                      workspace_bytes, parts, stream);
 }
 
-int wmtp_combine(const wmtp_partials* parts, void* out, int32_t out_dtype, float* lse_out, void* stream) {
+int wmtp_combine(const wmtp_partials* parts, void* out, float* lse_out, int32_t out_dtype, void* stream) {
   if (!parts || !out) return WMTP_EINVAL;
   if (out_dtype != WMTP_F32 && out_dtype != WMTP_BF16) return WMTP_EINVAL;
   if (parts->batch < 1 || parts->batch > WMTP_MAX_BATCH || parts->rows_per_seq < 1) return WMTP_EINVAL;
@@ -453,7 +453,7 @@ static int append_common(const wmtp_shape* shape, const void* k_new, const void*
   if ((int64_t)batch * t_new > INT32_MAX) return WMTP_EINVAL;
   std::memset(a, 0, sizeof(*a));
   for (int b = 0; b < batch; ++b) {
-    if (pos_host[b] < 0 || (int64_t)pos_host[b] + t_new > INT32_MAX) return WMTP_EINVAL;
+    if (pos_host[b] < 0 || (int64_t)pos_host[b] + t_new > WMTP_MAX_SEQ_LEN) return WMTP_EINVAL;
     a->pos[b] = pos_host[b];
   }
   a->k_new = k_new;
@@ -487,7 +487,7 @@ int wmtp_ring_rollback(const wmtp_ring* ring, const int32_t* seq_lens_host, int3
   AppendArgs a;
   std::memset(&a, 0, sizeof(a));
   for (int b = 0; b < batch; ++b) {
-    if (seq_lens_host[b] < 0) return WMTP_EINVAL;
+    if (seq_lens_host[b] < 0 || seq_lens_host[b] > WMTP_MAX_SEQ_LEN) return WMTP_EINVAL;
     a.pos[b] = seq_lens_host[b];
   }
   a.slot_pos = ring->slot_pos;
@@ -550,7 +550,7 @@ int wmtp_plan_memory(const wmtp_shape* shape, int32_t target_layers, int64_t con
                      int32_t window, int32_t headroom, int64_t budget_bytes, wmtp_memory_plan* out) {
   const int st = check_shape(shape);
   if (st) return st;
-  if (!out || target_layers < 0 || context < 0 || budget_bytes < 0) return WMTP_EINVAL;
+  if (!out || target_layers < 0 || context < 1 || budget_bytes < 0) return WMTP_EINVAL;
   if (sink < 0 || window < 1 || headroom < 0 || (int64_t)sink + window + headroom > (int64_t)INT32_MAX / 2)
     return WMTP_EINVAL;
   const int64_t row = (int64_t)shape->num_kv_heads * shape->head_dim * elem_bytes(shape->dtype) * 2;   // K+V
@@ -564,10 +564,10 @@ int wmtp_plan_memory(const wmtp_shape* shape, int32_t target_layers, int64_t con
   out->ring_bytes = ring;
   out->native_seq_bytes = (int64_t)target_layers * layer + layer + table;
   out->windowed_seq_bytes = (int64_t)target_layers * layer + ring + table;
-  out->reclaimed_fraction =
-      out->native_seq_bytes > 0 ? 1.0 - (double)out->windowed_seq_bytes / (double)out->native_seq_bytes : 0.0;
-  out->native_sequences = out->native_seq_bytes > 0 ? budget_bytes / out->native_seq_bytes : 0;
-  out->windowed_sequences = out->windowed_seq_bytes > 0 ? budget_bytes / out->windowed_seq_bytes : 0;
+  // context >= 1 gives native_seq_bytes >= one block of K and V, and the ring at least one slot
+  out->reclaimed_fraction = 1.0 - (double)out->windowed_seq_bytes / (double)out->native_seq_bytes;
+  out->native_sequences = budget_bytes / out->native_seq_bytes;
+  out->windowed_sequences = budget_bytes / out->windowed_seq_bytes;
   return WMTP_OK;
 }
 

@@ -24,7 +24,8 @@ FULL, SINK_WINDOW = 0, 1
 DRAFT_FAST_PV = 0x10
 MAX_BATCH = 64
 BLOCK_SIZE = 16
-MAX_VERIFY_ROWS = 32
+MAX_SEQ_LEN = 1 << 30
+MAX_VERIFY_ROWS = 96
 
 
 class WmtpError(RuntimeError):
@@ -101,7 +102,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.wmtp_draft_attn_append.restype = ctypes.c_int
     lib.wmtp_verify_attn_append.argtypes = [sp, P, I32, pp, P, P, P, I32, I32, P, SZ, tp, P]
     lib.wmtp_verify_attn_append.restype = ctypes.c_int
-    lib.wmtp_combine.argtypes = [tp, P, I32, P, P]
+    lib.wmtp_combine.argtypes = [tp, P, P, I32, P]
     lib.wmtp_combine.restype = ctypes.c_int
     lib.wmtp_ring_append.argtypes = [sp, rp, P, P, P, I32, I32, P]
     lib.wmtp_ring_append.restype = ctypes.c_int
@@ -155,6 +156,26 @@ def dtype_code(dt: torch.dtype) -> int:
     return {torch.float32: F32, torch.bfloat16: BF16}[dt]
 
 
+def _device_tensor(name: str, t: torch.Tensor, numel: int, dtypes, on_gpu: bool = True) -> None:
+    """The C ABI sees a raw pointer only: check here that `t` is a contiguous device tensor of one of
+    `dtypes` holding exactly `numel` elements, so a mis-sized buffer fails on the host.  on_gpu=False
+    leaves the device check to the caller."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {tuple(dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()} (shape {tuple(t.shape)})")
+    if on_gpu and not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor, got device {t.device}")
+
+
+def _shape_dtype(shape: Shape) -> torch.dtype:
+    return torch.bfloat16 if shape.dtype == BF16 else torch.float32
+
+
 def make_shape(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
                scale: Optional[float] = None) -> Shape:
     return Shape(num_q_heads, num_kv_heads, head_dim, head_dim ** -0.5 if scale is None else scale, dtype_code(dtype))
@@ -190,7 +211,13 @@ def make_ring(k: torch.Tensor, v: torch.Tensor, slot_pos: torch.Tensor, sink: in
               headroom: int = 0) -> Ring:
     """k, v: [batch][H_kv][S+W+R][D]; slot_pos: int32 [batch][S+W+R] (device); R = headroom.  The
     descriptor keeps k, v and slot_pos alive."""
-    assert slot_pos.dtype == torch.int32
+    slots = int(sink) + int(window) + int(headroom)
+    if slot_pos.dtype != torch.int32 or slot_pos.dim() != 2 or not slot_pos.is_contiguous():
+        raise ValueError("slot_pos: expected a contiguous int32 [batch][S+W+R] tensor")
+    if k.dim() != 4 or k.shape != v.shape or k.dtype != v.dtype or not (k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("k, v: expected two contiguous [batch][H_kv][S+W+R][D] tensors of one dtype")
+    if k.shape[2] != slots or tuple(slot_pos.shape) != (k.shape[0], slots):
+        raise ValueError(f"ring of S+W+R = {slots} slots: k is {tuple(k.shape)}, slot_pos {tuple(slot_pos.shape)}")
     r = Ring(k.data_ptr(), v.data_ptr(), slot_pos.data_ptr(), int(sink), int(window), int(headroom), None, None)
     r._tensors = (k, v, slot_pos)
     return r
@@ -232,6 +259,7 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 def draft_attn(mode: int, shape: Shape, q: torch.Tensor, seq_lens: Sequence[int], ws: torch.Tensor,
                paged: Optional[Paged] = None, ring: Optional[Ring] = None, chunk_tokens: int = 0,
                stream=None) -> Partials:
+    _device_tensor("q", q, len(seq_lens) * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
     parts = Partials()
     _check("wmtp_draft_attn", load().wmtp_draft_attn(
         mode, ctypes.byref(shape), q.data_ptr(), ctypes.byref(paged) if paged is not None else None,
@@ -244,6 +272,7 @@ def draft_attn(mode: int, shape: Shape, q: torch.Tensor, seq_lens: Sequence[int]
 
 def verify_attn(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, seq_lens: Sequence[int], ws: torch.Tensor,
                 split_tokens: int = 0, stream=None) -> Partials:
+    _device_tensor("q", q, len(seq_lens) * t_q * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
     parts = Partials()
     _check("wmtp_verify_attn", load().wmtp_verify_attn(
         ctypes.byref(shape), q.data_ptr(), t_q, ctypes.byref(paged), ctypes.cast(_lens(seq_lens), ctypes.c_void_p),
@@ -257,15 +286,18 @@ def _new_tokens(shape: Shape, k_new: torch.Tensor, v_new: torch.Tensor, batch: i
     """The fused calls read [batch][t_new][H_kv][D] from k_new and v_new: check that much is there."""
     want = batch * t_new * shape.num_kv_heads * shape.head_dim
     for name, x in (("k_new", k_new), ("v_new", v_new)):
-        if x.numel() != want or dtype_code(x.dtype) != shape.dtype or not x.is_contiguous():
+        if x.numel() != want or x.dtype != _shape_dtype(shape) or not x.is_contiguous():
             raise ValueError(f"{name}: expected a contiguous [{batch}][{t_new}][{shape.num_kv_heads}]"
                              f"[{shape.head_dim}] tensor of the cache dtype, got {tuple(x.shape)} {x.dtype}")
+        if not x.is_cuda:
+            raise ValueError(f"{name}: expected a GPU tensor, got device {x.device}")
 
 
 def draft_attn_append(mode: int, shape: Shape, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                       seq_lens: Sequence[int], ws: torch.Tensor, paged: Optional[Paged] = None,
                       ring: Optional[Ring] = None, chunk_tokens: int = 0, stream=None) -> Partials:
     """Append one token per sequence at position seq_lens[b] - 1 (paged or ring) and attend, in one launch."""
+    _device_tensor("q", q, len(seq_lens) * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
     _new_tokens(shape, k_new, v_new, len(seq_lens), 1)
     parts = Partials()
     _check("wmtp_draft_attn_append", load().wmtp_draft_attn_append(
@@ -281,6 +313,7 @@ def verify_attn_append(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, k_
                        v_new: torch.Tensor, seq_lens: Sequence[int], ws: torch.Tensor, split_tokens: int = 0,
                        stream=None) -> Partials:
     """Append the t_q query tokens' K/V at positions seq_lens[b] - t_q .. seq_lens[b] - 1 and verify, in one launch."""
+    _device_tensor("q", q, len(seq_lens) * t_q * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
     _new_tokens(shape, k_new, v_new, len(seq_lens), t_q)
     parts = Partials()
     _check("wmtp_verify_attn_append", load().wmtp_verify_attn_append(
@@ -292,13 +325,24 @@ def verify_attn_append(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, k_
 
 
 def combine(parts: Partials, out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
-    _check("wmtp_combine", load().wmtp_combine(ctypes.byref(parts), out.data_ptr(), dtype_code(out.dtype),
-                                               _ptr(lse), _stream(stream)))
+    """out: [batch][rows_per_seq][D] fp32 or bf16; lse: fp32 [batch][rows_per_seq] or None (device)."""
+    rows = parts.batch * parts.rows_per_seq
+    _device_tensor("out", out, rows * parts.head_dim, (torch.float32, torch.bfloat16), on_gpu=False)
+    if lse is not None:
+        _device_tensor("lse", lse, rows, (torch.float32,), on_gpu=False)
+    for name, t in (("out", out), ("lse", lse)):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name}: expected a GPU tensor, got device {t.device}")
+    _check("wmtp_combine", load().wmtp_combine(ctypes.byref(parts), out.data_ptr(), _ptr(lse),
+                                               dtype_code(out.dtype), _stream(stream)))
 
 
 def ring_append(shape: Shape, ring: Ring, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
                 stream=None) -> None:
     """k_new, v_new: [batch][t_new][H_kv][D]; pos[b]: absolute position of the first new token."""
+    if k_new.dim() != 4:
+        raise ValueError(f"k_new: expected [batch][t_new][H_kv][D], got shape {tuple(k_new.shape)}")
+    _new_tokens(shape, k_new, v_new, len(pos), k_new.shape[1])
     _check("wmtp_ring_append", load().wmtp_ring_append(
         ctypes.byref(shape), ctypes.byref(ring), k_new.data_ptr(), v_new.data_ptr(),
         ctypes.cast(_lens(pos), ctypes.c_void_p), len(pos), k_new.shape[1], _stream(stream)))
@@ -312,6 +356,9 @@ def ring_rollback(ring: Ring, seq_lens: Sequence[int], stream=None) -> None:
 
 def paged_append(shape: Shape, paged: Paged, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
                  stream=None) -> None:
+    if k_new.dim() != 4:
+        raise ValueError(f"k_new: expected [batch][t_new][H_kv][D], got shape {tuple(k_new.shape)}")
+    _new_tokens(shape, k_new, v_new, len(pos), k_new.shape[1])
     _check("wmtp_paged_append", load().wmtp_paged_append(
         ctypes.byref(shape), ctypes.byref(paged), k_new.data_ptr(), v_new.data_ptr(),
         ctypes.cast(_lens(pos), ctypes.c_void_p), len(pos), k_new.shape[1], _stream(stream)))

@@ -240,18 +240,20 @@ def test_combine_checks():
     p = W.Partials()
     p.o, p.lse, p.batch, p.rows_per_seq, p.head_dim, p.total_splits = FAKE, FAKE, 1, 16, 256, 3
     p.split_base[0], p.split_base[1] = 0, 3
-    assert lib.wmtp_combine(None, FAKE, W.F32, None, None) == W.EINVAL
-    assert lib.wmtp_combine(ctypes.byref(p), None, W.F32, None, None) == W.EINVAL
-    assert lib.wmtp_combine(ctypes.byref(p), FAKE, 9, None, None) == W.EINVAL
-    assert lib.wmtp_combine(ctypes.byref(p), FAKE_ODD, W.F32, None, None) == W.EALIGN
+    # argument order: parts, out, lse_out, out_dtype, stream
+    assert lib.wmtp_combine(None, FAKE, None, W.F32, None) == W.EINVAL
+    assert lib.wmtp_combine(ctypes.byref(p), None, None, W.F32, None) == W.EINVAL
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE, None, 9, None) == W.EINVAL
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE_ODD, None, W.F32, None) == W.EALIGN
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE, FAKE + 2, W.F32, None) == W.EALIGN   # lse_out not 4-byte aligned
     p.split_base[1] = 2
-    assert lib.wmtp_combine(ctypes.byref(p), FAKE, W.F32, None, None) == W.EINVAL   # inconsistent total
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE, None, W.F32, None) == W.EINVAL   # inconsistent total
     p.split_base[1] = 3
     p.head_dim = 80
-    assert lib.wmtp_combine(ctypes.byref(p), FAKE, W.F32, None, None) == W.EUNSUPPORTED
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE, None, W.F32, None) == W.EUNSUPPORTED
     p.head_dim = 256
     p.batch = 0
-    assert lib.wmtp_combine(ctypes.byref(p), FAKE, W.F32, None, None) == W.EINVAL
+    assert lib.wmtp_combine(ctypes.byref(p), FAKE, None, W.F32, None) == W.EINVAL
 
 
 def test_append_checks():
@@ -399,6 +401,8 @@ def test_memory_plan_matches_the_oracle():
         for L in (0, 1, 10):
             for ctx in (0, 1, 15, 16, 17, 131072, 1 << 20, 3_000_001):
                 for S, Wn, R in ((4, 4096, 2), (0, 1, 0), (16, 16384, 7)):
+                    if ctx == 0:
+                        continue
                     budget = 288 * 10 ** 9
                     got = W.plan_memory(sh, L, ctx, S, Wn, R, budget)
                     want = O.memory_plan(hk, d, eb, L, ctx, S, Wn, R, budget)
@@ -421,6 +425,78 @@ def test_memory_plan_checks():
     assert lib.wmtp_plan_memory(ctypes.byref(sh), 10, 10, 4, 64, 0, 0, None) == W.EINVAL
     assert lib.wmtp_plan_memory(ctypes.byref(sh), 1 << 30, 1 << 60, 4, 64, 0, 0, ctypes.byref(out)) == W.EINVAL
     assert lib.wmtp_plan_memory(None, 10, 10, 4, 64, 0, 0, ctypes.byref(out)) == W.EINVAL
+    # a sequence with no KV has no reclaimed share: both sides reject it
+    for L in (0, 10):
+        assert lib.wmtp_plan_memory(ctypes.byref(sh), L, 0, 4, 64, 0, 0, ctypes.byref(out)) == W.EINVAL
+    assert lib.wmtp_plan_memory(ctypes.byref(sh), 10, 1, 4, 64, 0, 0, ctypes.byref(out)) == W.OK
+
+
+def test_memory_plan_oracle_rejects_an_empty_sequence():
+    import oracle as O
+    for L in (0, 10):
+        with pytest.raises(ValueError):
+            O.memory_plan(2, 256, 2, L, 0, 4, 4096, 2, 1 << 40)
+    one = O.memory_plan(2, 256, 2, 0, 1, 4, 4096, 2, 1 << 40)
+    assert one["native_seq_bytes"] == 16 * 2 * 256 * 2 * 2 + 4      # one block of K and V, one table entry
+
+
+def test_lengths_past_the_maximum_are_rejected():
+    """Lengths near INT32_MAX would overflow the kernels' 32-bit position arithmetic and the
+    planner's block count: every entry point that takes lengths or positions rejects anything past
+    WMTP_MAX_SEQ_LEN (2^30) before any HIP call, and accepts the maximum itself."""
+    lib = W.load()
+    sh = shape()
+    big, top = 2 ** 31 - 1, W.MAX_SEQ_LEN
+    for n in (big, top + 1):
+        assert lib.wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(n), 1, 0, 0, 1, 0) == W.EINVAL
+        assert lib.wmtp_draft_workspace_bytes(W.SINK_WINDOW, ctypes.byref(sh), lens(n), 1, 0, 4, 64, 0) == W.EINVAL
+        assert lib.wmtp_verify_workspace_bytes(ctypes.byref(sh), 4, lens(n), 1, 0) == W.EINVAL
+        kv = paged(mb=1 << 27)                                    # a table row long enough for any length
+        assert draft(kv=kv, seq=(n,)) == W.EINVAL
+        assert draft(mode=W.SINK_WINDOW, seq=(n,)) == W.EINVAL
+        p = W.Partials()
+        assert lib.wmtp_verify_attn(ctypes.byref(sh), FAKE, 4, ctypes.byref(kv), lens(n), 1, 0, FAKE, 1 << 40,
+                                    ctypes.byref(p), None) == W.EINVAL
+        assert lib.wmtp_ring_rollback(ctypes.byref(ring()), lens(n), 1, None) == W.EINVAL
+        pos = lens(n - 1)
+        assert lib.wmtp_ring_append(ctypes.byref(sh), ctypes.byref(ring()), FAKE, FAKE, pos, 1, 2, None) == W.EINVAL
+        assert lib.wmtp_paged_append(ctypes.byref(sh), ctypes.byref(kv), FAKE, FAKE, pos, 1, 2, None) == W.EINVAL
+    # the maximum itself plans
+    assert lib.wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(top), 1, 0, 0, 1, 0) > 0
+    assert lib.wmtp_verify_workspace_bytes(ctypes.byref(sh), 4, lens(top), 1, 0) > 0
+
+
+def test_binding_checks_buffers_before_the_call():
+    """The binding passes raw pointers to the C ABI, so it checks sizes, dtypes and contiguity of the
+    tensors first: a mis-sized buffer raises on the host instead of reaching a kernel."""
+    sh = W.make_shape(16, 2, 256, torch.bfloat16, 1 / 16)
+    p = W.Partials()
+    p.batch, p.rows_per_seq, p.head_dim, p.total_splits = 2, 16, 256, 4
+    with pytest.raises(ValueError, match="out"):
+        W.combine(p, torch.empty((2, 15, 256)))                        # one row short
+    with pytest.raises(ValueError, match="lse"):
+        W.combine(p, torch.empty((2, 16, 256)), torch.empty((2, 17)))
+    with pytest.raises(ValueError, match="dtype"):
+        W.combine(p, torch.empty((2, 16, 256), dtype=torch.float16))
+    with pytest.raises(ValueError, match="GPU"):
+        W.combine(p, torch.empty((2, 16, 256)))                        # right size, but host memory
+    ws = torch.empty(1 << 12, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="q"):
+        W.draft_attn(W.FULL, sh, torch.empty((1, 8, 256), dtype=torch.bfloat16), [100], ws)
+    with pytest.raises(ValueError, match="q"):
+        W.verify_attn(sh, torch.empty((1, 3, 16, 256), dtype=torch.bfloat16), 4, W.Paged(), [100], ws)
+    with pytest.raises(ValueError, match="contiguous"):
+        W.draft_attn(W.FULL, sh, torch.empty((1, 256, 16), dtype=torch.bfloat16).transpose(1, 2), [100], ws)
+    with pytest.raises(ValueError, match="k_new"):
+        W.ring_append(sh, W.Ring(), torch.empty((1, 3, 2, 256)), torch.empty((1, 3, 2, 256)), [0])
+    kr = torch.zeros((1, 2, 12, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="slots"):
+        W.make_ring(kr, kr.clone(), torch.full((1, 12), -1, dtype=torch.int32), 4, 8, 1)   # 13 slots wanted
+    with pytest.raises(ValueError, match="slot_pos"):
+        W.make_ring(kr, kr.clone(), torch.full((1, 12), -1, dtype=torch.int64), 4, 8)
+    with pytest.raises(ValueError, match="k, v"):
+        W.make_ring(kr, torch.zeros((1, 2, 12, 128), dtype=torch.bfloat16), torch.full((1, 12), -1, dtype=torch.int32),
+                    4, 8)
 
 
 def test_descriptors_keep_their_tensors_alive():
