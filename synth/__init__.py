@@ -17,7 +17,14 @@ and a 1M-token context):
   * a block table is a seeded random permutation of the physical block ids,
     split into consecutive runs, one per sequence;
   * small cases are drawn on the CPU; the multi-GiB paged pools of the 1M-token
-    workloads are drawn on the GPU with torch's counter-based generator.
+    workloads are drawn on the GPU with torch's counter-based generator;
+  * "needles" give a long context structure a parity check can see: at seeded
+    positions, keys parallel to chosen query rows (scaled so that the row's
+    scaled dot product with its key is a seeded value in [21.5, 22.5]) and
+    freshly drawn values.  Each such row's softmax then rests on its few dozen
+    needles instead of spreading evenly over a million keys, so its output is
+    of order one and changes if any of those value rows is read from the
+    wrong place.
 """
 from __future__ import annotations
 
@@ -31,6 +38,7 @@ import torch
 __all__ = [
     "Workload", "WORKLOADS", "workload", "stream_seed", "normal", "block_table",
     "blocks_for", "bf16_bits", "DraftCase", "draft_case", "VerifyCase", "verify_case",
+    "needle_positions", "needle_logits", "needle_keys", "NEEDLE_LOGITS",
 ]
 
 
@@ -151,6 +159,49 @@ def block_table(seed: int, blocks_per_seq: Sequence[int], permuted: bool = True,
         bt[b, :nb] = ids[at:at + nb]
         at += nb
     return bt, total
+
+
+# --------------------------------------------------------------------------- needles
+NEEDLE_LOGITS = (21.5, 22.5)
+
+
+def needle_positions(seed: int, stream, count: int, lo: int, hi: int,
+                     include: Sequence[int] = ()) -> np.ndarray:
+    """`count` distinct positions in [lo, hi): the `include` positions first (in order, duplicates
+    dropped), then seeded uniform draws without replacement from the rest."""
+    stream = stream if isinstance(stream, tuple) else (stream,)
+    first = list(dict.fromkeys(int(p) for p in include))
+    if len(first) > count or any(not lo <= p < hi for p in first) or count > hi - lo:
+        raise ValueError("needle positions do not fit the range")
+    rng = np.random.default_rng(stream_seed(seed, "needle_positions", *stream))
+    taken = set(first)
+    out = list(first)
+    while len(out) < count:
+        for p in rng.integers(lo, hi, size=2 * (count - len(out)) + 8):
+            p = int(p)
+            if p not in taken:
+                taken.add(p)
+                out.append(p)
+                if len(out) == count:
+                    break
+    return np.asarray(out, dtype=np.int64)
+
+
+def needle_logits(seed: int, stream, count: int) -> torch.Tensor:
+    """Seeded target values of scale * q.k for `count` needles, uniform in NEEDLE_LOGITS (float32)."""
+    stream = stream if isinstance(stream, tuple) else (stream,)
+    g = torch.Generator()
+    g.manual_seed(stream_seed(seed, "needle_logits", *stream))
+    lo, hi = NEEDLE_LOGITS
+    return lo + (hi - lo) * torch.rand(count, generator=g, dtype=torch.float32)
+
+
+def needle_keys(q_rows: torch.Tensor, logits: torch.Tensor, scale: float, dtype: str) -> torch.Tensor:
+    """Key rows parallel to query rows: row j is c_j * q_rows[j] with c_j = logits[j] / (scale |q_j|^2),
+    so scale * q_j . key_j is logits[j] before the key is rounded to `dtype` (bf16: RNE)."""
+    qf = q_rows.float()
+    c = logits.to(qf.device).float() / (scale * (qf * qf).sum(dim=-1))
+    return (c[:, None] * qf).to(_torch_dtype(dtype))
 
 
 # --------------------------------------------------------------------------- cases

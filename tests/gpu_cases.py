@@ -83,6 +83,60 @@ class RingCache:
         self.desc = W.make_ring(self.k, self.v, self.tags, sink, window, headroom)
 
 
+def needles(q_rows: torch.Tensor, heads, lo: int, hi: int, seed: int, stream: tuple, scale: float,
+            per_row: int = 32, include=()):
+    """Needle inputs (synth's recipe) aimed at query rows q_rows [R][D] (device), row r on KV head
+    heads[r]: per row, `per_row` keys parallel to it at positions in [lo, hi), distinct within
+    each KV head, and fresh values.  Every position in `include` is given to each KV head, as
+    needle 0 of that head's first rows (one forced position per row), so chosen blocks (the
+    start, the sinks, the highest addresses of a pool) hold needles of both heads.
+    Returns (positions [R * per_row], heads [R * per_row], k rows, v rows), row r's needles at
+    r * per_row ...."""
+    heads = np.asarray(heads)
+    R, D = q_rows.shape
+    pos = np.empty(R * per_row, dtype=np.int64)
+    for h in np.unique(heads):
+        rows = np.nonzero(heads == h)[0]
+        inc = list(include)[:len(rows)]
+        p = synth.needle_positions(seed, stream + (int(h),), len(rows) * per_row, lo, hi, inc)
+        for i in range(len(inc)):                          # forced position i -> needle 0 of row i
+            p[[i, i * per_row]] = p[[i * per_row, i]]
+        for j, r in enumerate(rows):
+            pos[r * per_row:(r + 1) * per_row] = p[j * per_row:(j + 1) * per_row]
+    logits = synth.needle_logits(seed, stream, R * per_row)
+    k = synth.needle_keys(q_rows.repeat_interleave(per_row, 0), logits, scale, "bf16")
+    v = synth.normal((R * per_row, D), seed, ("needle_v",) + stream, 0.5, "bf16", str(q_rows.device))
+    return pos, np.repeat(heads, per_row), k, v
+
+
+def plant_paged(kpool: torch.Tensor, vpool: torch.Tensor, bt_row: np.ndarray, needle) -> None:
+    """Write needle K/V rows into paged pools [blocks][H_kv][16][D] (or K|V views of one pool) of one
+    sequence: token p of head h sits at [bt_row[p // 16], h, p % 16] (plain tensor indexing)."""
+    pos, heads, k, v = needle
+    blk = torch.from_numpy(bt_row[pos // 16].astype(np.int64)).to(kpool.device)
+    off = torch.from_numpy(pos % 16).to(kpool.device)
+    hh = torch.from_numpy(heads.astype(np.int64)).to(kpool.device)
+    kpool[blk, hh, off] = k.to(kpool.device)
+    vpool[blk, hh, off] = v.to(vpool.device)
+
+
+def plant_logical(k_ctx: torch.Tensor, v_ctx: torch.Tensor, b: int, needle) -> None:
+    """Write needle K/V rows into position-ordered tokens [batch][n][H_kv][D] of sequence b."""
+    pos, heads, k, v = needle
+    p = torch.from_numpy(pos).to(k_ctx.device)
+    hh = torch.from_numpy(heads.astype(np.int64)).to(k_ctx.device)
+    k_ctx[b, p, hh] = k.to(k_ctx.device)
+    v_ctx[b, p, hh] = v.to(v_ctx.device)
+
+
+def top_block_positions(bt_row: np.ndarray, n0: int, top: int, count: int = 16) -> list:
+    """The first `count` token positions of the logical block that maps to physical block `top`
+    (the pool's highest addresses), which must lie inside the n0-token context."""
+    j = int(np.nonzero(bt_row == top)[0][0])
+    assert (j + 1) * 16 <= n0, "the top block holds no context token"
+    return [j * 16 + t for t in range(count)]
+
+
 def max_err(gpu: torch.Tensor, ref: np.ndarray) -> float:
     g = gpu.detach().cpu().double().numpy()
     if g.size == 0:
