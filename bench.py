@@ -19,6 +19,7 @@ Prints one JSON line on stdout.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -203,6 +204,7 @@ class Step:
         self.lse_d = torch.empty((1, Hq), dtype=torch.float32, device=dev)
         self.out_v = torch.empty((1, (g + 1) * Hq, D), dtype=torch.float32, device=dev)
         self.lse_v = torch.empty((1, (g + 1) * Hq), dtype=torch.float32, device=dev)
+        self._calls = {}
 
     def draft(self, mode, flag, ev=None, fused=True):
         """gamma draft steps.  fused: each step's append runs inside its attention launch
@@ -250,6 +252,53 @@ class Step:
             W.combine(parts, self.out_v, self.lse_v)
 
 
+    def calls(self, mode, flag, fused=True):
+        """The launches of one decode step as prepared C-ABI calls, in launch order: a list of
+        (kind, index, call) with kind in draft / draft_combine / verify / verify_combine (and append
+        for the unfused step).  The calls run once here, which fills each attention call's partials
+        before the combine that reads them is prepared."""
+        key = (mode, flag, fused)
+        if key in self._calls:
+            return self._calls[key]
+        g, n0 = self.wl.gamma, self.n0
+        out = []
+        for j in range(g):
+            pos, n = n0 + j, n0 + j + 1
+            full = mode == W.FULL
+            kw = dict(paged=self.layers[0][1], chunk_tokens=self.chunk_full) if full else \
+                dict(ring=self.ring, chunk_tokens=self.chunk_win)
+            ws = self.ws_full if full else self.ws_win
+            if fused:
+                a = W.prepare_draft_attn_append(mode | flag, self.sh, self.q_draft[j], self.k_draft[j],
+                                                self.v_draft[j], [n], ws, **kw)
+            else:
+                app = (W.prepare_paged_append(self.sh, self.layers[0][1], self.k_draft[j], self.v_draft[j], [pos])
+                       if full else W.prepare_ring_append(self.sh, self.ring, self.k_draft[j], self.v_draft[j], [pos]))
+                app()
+                out.append(("append", j, app))
+                a = W.prepare_draft_attn(mode | flag, self.sh, self.q_draft[j], [n], ws, **kw)
+            a()
+            c = W.prepare_combine(a.parts, self.out_d, self.lse_d)
+            c()
+            out += [("draft", j, a), ("draft_combine", j, c)]
+        for l in range(len(self.layers) - 1):
+            desc = self.layers[l + 1][1]
+            if fused:
+                a = W.prepare_verify_attn_append(self.sh, self.q_ver[l], g + 1, desc, self.k_ver, self.v_ver,
+                                                 [n0 + g + 1], self.ws_ver, self.split)
+            else:
+                app = W.prepare_paged_append(self.sh, desc, self.k_ver, self.v_ver, [n0])
+                app()
+                out.append(("append", 100 + l, app))
+                a = W.prepare_verify_attn(self.sh, self.q_ver[l], g + 1, desc, [n0 + g + 1], self.ws_ver, self.split)
+            a()
+            c = W.prepare_combine(a.parts, self.out_v, self.lse_v)
+            c()
+            out += [("verify", l, a), ("verify_combine", l, c)]
+        self._calls[key] = out
+        return out
+
+
 def kv_bytes(tokens, wl):
     return tokens * wl.num_kv_heads * wl.head_dim * 2 * 2
 
@@ -268,42 +317,64 @@ def draft_launch_bytes(entries, wl, paged):
 
 
 def time_steps(step, mode, flag, steps, warmup, fused=True):
-    """Warmup, then time `steps` decode steps; per-launch events on the dominant kernels."""
+    """Warmup, then `steps` decode steps with an event on the launch stream before the step and after
+    every launch: the interval ending at a launch's event is that launch's time on the device's
+    timeline (any idle gap before it included).  The launches are prepared C-ABI calls and the
+    garbage collector is off in the timed loop, so no host pause lands between them.
+    Returns {"step": [ms per step], kind: [[ms per launch of that kind] per step]}."""
+    calls = step.calls(mode, flag, fused)
     torch.cuda.synchronize()
     for _ in range(warmup):
-        step.draft(mode, flag, fused=fused)
-        step.verify(fused=fused)
+        for _, _, c in calls:
+            c()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
-    L = len(step.layers) - 1
-    ev_v = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-            for _ in range(steps)]
-    ev_d = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
-    ev_s[0].record()
-    for s in range(steps):
-        step.draft(mode, flag, ev_d[s], fused=fused)
-        step.verify(ev_v[s], fused=fused)
-        ev_s[s + 1].record()
-    torch.cuda.synchronize()
-    total_ms = ev_s[0].elapsed_time(ev_s[-1])
-    step_ms = [ev_s[s].elapsed_time(ev_s[s + 1]) for s in range(steps)]
-    ver_ms = [a.elapsed_time(b) for row in ev_v for a, b in row]
-    draft_ms = [a.elapsed_time(b) for a, b in ev_d]
-    return total_ms / steps, float(np.mean(ver_ms)), float(np.mean(draft_ms)), step_ms
+    gc_was = gc.isenabled()
+    gc.disable()
+    try:
+        for s in range(steps):
+            ev = evs[s]
+            ev[0].record()
+            for i, (_, _, c) in enumerate(calls):
+                c()
+                ev[i + 1].record()
+        torch.cuda.synchronize()
+    finally:
+        if gc_was:
+            gc.enable()
+    res = {"step": [ev[0].elapsed_time(ev[-1]) for ev in evs]}
+    for i, (kind, _, _) in enumerate(calls):
+        res.setdefault(kind, [[] for _ in range(steps)])
+        for s in range(steps):
+            res[kind][s].append(evs[s][i].elapsed_time(evs[s][i + 1]))
+    return res
 
 
-def pct(ms):
-    """median / p10 / p90 of a list of milliseconds, in microseconds."""
+def flat(per_step):
+    return [x for row in per_step for x in row]
+
+
+def med(ms):
+    return float(np.median(np.asarray(ms, dtype=np.float64)))
+
+
+def pct(ms, full=False):
+    """median / p10 / p90 (and with full=True mean, max and the count above 1.1 x median) of a list of
+    milliseconds, in microseconds."""
     a = np.asarray(ms, dtype=np.float64) * 1e3
-    return {"median": round(float(np.median(a)), 1), "p10": round(float(np.percentile(a, 10)), 1),
-            "p90": round(float(np.percentile(a, 90)), 1), "n": int(a.size)}
+    m = float(np.median(a))
+    out = {"median": round(m, 1), "p10": round(float(np.percentile(a, 10)), 1),
+           "p90": round(float(np.percentile(a, 90)), 1), "n": int(a.size)}
+    if full:
+        out.update(mean=round(float(a.mean()), 1), max=round(float(a.max()), 1),
+                   above_1_1x_median=int((a > 1.1 * m).sum()))
+    return out
 
 
-def _hold():
+def _hold(cycles=100000):
     """Keep the GPU busy for a bounded spin (tens of µs) while the host queues the timed launches,
     so the events measure device time rather than Python launch overhead."""
-    torch.cuda._sleep(100000)
+    torch.cuda._sleep(cycles)
 
 
 def _timed(fn, reps, before=_hold):
@@ -522,6 +593,95 @@ def mixed_batch(flag, reps, dev):
     return res
 
 
+def draft_131k_measurements(flag, reps, dev):
+    """The single-draft-layer workload at 131,072 tokens: gamma = 3 draft steps (each the append inside
+    the attention launch, then the combine) in native mode over a contiguous K|V pool and in
+    sink_window mode (S = 4, W = 4,096) over a ring of S + W slots.  Timed cold (1 GiB written
+    between repetitions, as a real step's verify evicts the draft's KV) and warm."""
+    wl = synth.workload("draft_131k_bf16")
+    Hq, Hk, D, S, Wn, g = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.sink, wl.window, wl.gamma
+    n0 = wl.contexts[0]
+    sh = W.make_shape(Hq, Hk, D, torch.bfloat16, wl.scale)
+    nb = synth.blocks_for(n0 + g, 16)
+    bt, total = synth.block_table(wl.seed, [nb], permuted=False)
+    pool = synth.normal((total, Hk, 2, 16, D), wl.seed, "c2kv", wl.kv_scale, "bf16", dev)
+    desc = W.make_paged_interleaved(pool, torch.from_numpy(bt).to(dev))
+    rk = torch.zeros((1, Hk, S + Wn, D), dtype=torch.bfloat16, device=dev)
+    rv = torch.zeros_like(rk)
+    tags = torch.full((1, S + Wn), -1, dtype=torch.int32, device=dev)
+    ring = W.make_ring(rk, rv, tags, S, Wn)
+    W.ring_append(sh, ring, synth.normal((1, S, Hk, D), wl.seed, "c2_sink_k", wl.kv_scale, "bf16", dev),
+                  synth.normal((1, S, Hk, D), wl.seed, "c2_sink_v", wl.kv_scale, "bf16", dev), [0])
+    W.ring_append(sh, ring, synth.normal((1, Wn, Hk, D), wl.seed, "c2_tail_k", wl.kv_scale, "bf16", dev),
+                  synth.normal((1, Wn, Hk, D), wl.seed, "c2_tail_v", wl.kv_scale, "bf16", dev), [n0 - Wn])
+    q = synth.normal((g, 1, Hq, D), wl.seed, "c2q", 1.0, "bf16", dev)
+    kn = synth.normal((g, 1, 1, Hk, D), wl.seed, "c2kn", wl.kv_scale, "bf16", dev)
+    vn = synth.normal((g, 1, 1, Hk, D), wl.seed, "c2vn", wl.kv_scale, "bf16", dev)
+    out = torch.empty((1, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, Hq), dtype=torch.float32, device=dev)
+    lens = [n0 + g]
+    ws_full = W.workspace(W.draft_workspace_bytes(W.FULL, sh, lens, 0), dev)
+    ws_win = W.workspace(W.draft_workspace_bytes(W.SINK_WINDOW, sh, lens, 0, S, Wn, 0), dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    res = {"context": n0, "gamma": g, "sink": S, "window": Wn, "pool": "contiguous K|V runs (identity table)"}
+    for mode, name in ((W.FULL, "native"), (W.SINK_WINDOW, "windowed")):
+        calls = []
+        for j in range(g):
+            kw = dict(paged=desc) if mode == W.FULL else dict(ring=ring)
+            a = W.prepare_draft_attn_append(mode | flag, sh, q[j], kn[j], vn[j], [n0 + j + 1],
+                                            ws_full if mode == W.FULL else ws_win, **kw)
+            a()
+            c = W.prepare_combine(a.parts, out, lse)
+            c()
+            calls += [a, c]
+
+        def run():
+            for c in calls:
+                c()
+        run()
+        torch.cuda.synchronize()
+        cold = pct(_timed(run, reps, lambda: (flush.fill_(1), _hold(400000))))
+        warm = pct(_timed(run, reps, lambda: _hold(400000)))
+        nbytes = sum(draft_launch_bytes(min(n0 + j + 1, S + Wn) if mode == W.SINK_WINDOW else n0 + j + 1, wl,
+                                        mode == W.FULL) for j in range(g))
+        gbps = nbytes / (cold["median"] * 1e-6) / 1e9
+        res[name] = {"cold_us": cold, "warm_us_median": warm["median"], "algorithmic_bytes": nbytes,
+                     "gbps": round(gbps, 1), "pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+    res["ratio_native_over_windowed"] = round(res["native"]["cold_us"]["median"] /
+                                              res["windowed"]["cold_us"]["median"], 3)
+    res["launches"] = (f"{g} x (draft attention with the append inside + combine); host launches queued behind "
+                       f"a spin (and the flush when cold)")
+    del pool, flush, rk, rv, tags, ws_full, ws_win
+    torch.cuda.empty_cache()
+    return res
+
+
+def native_draft_pv_measurements(step, reps):
+    """The 1M native draft step (append inside the attention launch, then the combine) with fp32 softmax
+    weights in the PV product (the vector dot-product kernel) beside bf16 weight pairs (the matrix-core
+    kernel), in the main step's launch configuration.  Every launch streams the 2 GiB pool, far past
+    the caches, so each repetition reads it from HBM."""
+    n = step.n0 + 1
+    res = {}
+    for flag, name in ((0, "fp32_weights_dot_product_kernel"), (W.DRAFT_FAST_PV, "bf16_weights_matrix_core_kernel")):
+        a = W.prepare_draft_attn_append(W.FULL | flag, step.sh, step.q_draft[0], step.k_draft[0], step.v_draft[0],
+                                        [n], step.ws_full, paged=step.layers[0][1], chunk_tokens=step.chunk_full)
+        a()
+        c = W.prepare_combine(a.parts, step.out_d, step.lse_d)
+
+        def run():
+            a()
+            c()
+        run()
+        torch.cuda.synchronize()
+        t = pct(_timed(run, reps, lambda: _hold(400000)), full=True)
+        nbytes = draft_launch_bytes(n, step.wl, True)
+        gbps = nbytes / (t["median"] * 1e-6) / 1e9
+        res[name] = {"us": t, "gbps": round(gbps, 1), "pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+    res["algorithmic_bytes"] = draft_launch_bytes(n, step.wl, True)
+    return res
+
+
 def _per_rep(fn, budget_s):
     """Mean seconds per call of fn(rep), repeating until `budget_s` has passed (at least once)."""
     reps, t0 = 0, time.perf_counter()
@@ -544,11 +704,12 @@ def cpu_baseline(wl, n0, budget_s=12.0):
     draft steps.  Keys and values are synthetic bf16.
     """
     import oracle as O
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+        from threadpoolctl import threadpool_limits
+        limits = threadpool_limits(limits=cores)          # BLAS threads = the cores this process may use
+    except ImportError:
+        limits = None
     rng = np.random.default_rng(0)
     D, G, g = wl.head_dim, wl.group, wl.gamma
     n = n0 + g + 1
@@ -568,6 +729,8 @@ def cpu_baseline(wl, n0, budget_s=12.0):
         lambda r: O.attention_over(qs[r % 4, 0], src_k, src_v, np.arange(n0 + 1), 0, wl.scale), 0.2 * budget_s)
     t_win, r_w, e_w = _per_rep(
         lambda r: O.attention_over(qs[r % 4, 0], src_k, src_v, win, 0, wl.scale), 0.05 * budget_s)
+    if limits is not None:
+        limits.restore_original_limits()
     Hk, L = wl.num_kv_heads, wl.target_layers
     verify_step = t_verify * Hk * L
     win_s, nat_s = verify_step + t_win * Hk * g, verify_step + t_native * Hk * g
@@ -578,7 +741,7 @@ def cpu_baseline(wl, n0, budget_s=12.0):
         # oracle-equivalent rate: the step's algorithmic K/V bytes over the oracle's time
         "gbps": round(step_bytes(n0, wl, True) / win_s / 1e9, 3),
         "native_gbps": round(step_bytes(n0, wl, False) / nat_s / 1e9, 3),
-        "cores": int(threads),
+        "cores": int(cores),
         "kind": "oracle",
         "sample": (f"float64 oracle on 1 KV head: {r_v} verify layer(s) ({g + 1} causal queries x {G} heads over "
                    f"{n} keys), {r_n} native draft step(s) ({n0 + 1} keys), {r_w} windowed draft step(s) "
@@ -606,8 +769,10 @@ def sweep(flag, steps, warmup, dev, contexts, gammas):
             wl = synth.workload("step_1m_bf16", contexts=(n0,), gamma=g)
             log(f"sweep n0={n0} gamma={g}")
             step = Step(wl, n0, wl.target_layers, 0, 0, 0, dev)
-            win_ms, ver_ms, dwin_ms, _ = time_steps(step, W.SINK_WINDOW, flag, steps, warmup)
-            nat_ms, _, dnat_ms, _ = time_steps(step, W.FULL, flag, steps, warmup)
+            rw = time_steps(step, W.SINK_WINDOW, flag, steps, warmup)
+            rn = time_steps(step, W.FULL, flag, steps, warmup)
+            win_ms, nat_ms = med(rw["step"]), med(rn["step"])
+            ver_ms, dwin_ms, dnat_ms = med(flat(rw["verify"])), med(flat(rw["draft"])), med(flat(rn["draft"]))
             # the same steps replayed from a HIP graph: no host launch cost (small contexts are host-bound eagerly)
             gw, okw = graph_step(step, W.SINK_WINDOW, flag, 5)
             gn, okn = graph_step(step, W.FULL, flag, 5)
@@ -686,20 +851,43 @@ def main():
     log("paged streaming-read ceiling")
     paged_ceiling = paged_ceiling_gbps(step)
     log("timing windowed step")
-    win_ms, ver_ms, dwin_ms, win_steps = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup)
+    rw = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup)
     log("timing native step")
-    nat_ms, ver_ms2, dnat_ms, nat_steps = time_steps(step, W.FULL, flag, args.steps, args.warmup)
-    details = {"step_us": {"windowed": pct(win_steps), "native": pct(nat_steps)}}
+    rn = time_steps(step, W.FULL, flag, args.steps, args.warmup)
+    win_ms, nat_ms = med(rw["step"]), med(rn["step"])
+    ver_ms = med(flat(rw["verify"]))                  # verify launches of the windowed (headline) step
+    ver_ms_nat = med(flat(rn["verify"]))
+    dwin_ms, dnat_ms = med(flat(rw["draft"])), med(flat(rn["draft"]))
+    L = wl.target_layers
+    details = {
+        "step_us": {"windowed": pct(rw["step"], True), "native": pct(rn["step"], True)},
+        "launch_us": {arm: {kind: pct(flat(r[kind]), True) for kind in ("draft", "draft_combine", "verify",
+                                                                          "verify_combine")}
+                      for arm, r in (("windowed", rw), ("native", rn))},
+        "verify_us_by_layer": [round(med([r[l] for r in rw["verify"]]) * 1e3, 1) for l in range(L)],
+        "self_check": {
+            # the step contains its verify launches: L x their median cannot exceed the step's median
+            "verify_layers_within_step": bool(L * ver_ms <= win_ms and L * ver_ms_nat <= nat_ms),
+            # the launches' medians add up to the step's median within 2% (nothing else is timed)
+            "launch_sum_over_step": {arm: round(sum(med(flat(r[k])) * len(r[k][0]) for k in r if k != "step")
+                                                / med(r["step"]), 4) for arm, r in (("windowed", rw), ("native", rn))},
+        },
+        "timing": ("median over the timed steps; an event after every launch on the launch stream; prepared "
+                   "C-ABI calls with the garbage collector off"),
+    }
+    if not details["self_check"]["verify_layers_within_step"]:
+        log("WARNING: verify launches exceed their step")
     if not args.no_details:
         reps = 20
         log("unfused steps (append calls before the attention calls)")
         uw = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup, fused=False)
         un = time_steps(step, W.FULL, flag, args.steps, args.warmup, fused=False)
-        details["unfused_step_us"] = {"windowed": pct(uw[3]), "native": pct(un[3])}
+        details["unfused_step_us"] = {"windowed": pct(uw["step"]), "native": pct(un["step"])}
         log("graph-captured steps")
         gw, okw = graph_step(step, W.SINK_WINDOW, flag, 20)
         gn, okn = graph_step(step, W.FULL, flag, 20)
-        details["graph_step_us"] = {"windowed": pct(gw), "native": pct(gn), "replays_match_eager": bool(okw and okn)}
+        details["graph_step_us"] = {"windowed": pct(gw), "native": pct(gn), "replays_match_eager": bool(okw and okn),
+                                    "ratio": round(med(gn) / med(gw), 4)}
         log("window draft: warm, cold, across contexts")
         details["window_draft_step_us"] = window_measurements(
             step, flag, reps, dev, (32768, 131072, 524288, n0))
@@ -709,8 +897,12 @@ def main():
                                       budget="the GPU's whole memory", budget_bytes=int(total_mem))
         log("native draft launch: literal 256-key splits vs default")
         details["native_draft_launch_us"] = native_split_measurements(step, flag, 10, dev)
+        log("native draft step: fp32 vs bf16 PV weights")
+        details["native_draft_step_1m_pv"] = native_draft_pv_measurements(step, reps)
         del step
         torch.cuda.empty_cache()
+        log("131K draft layer: native vs windowed, 3 steps")
+        details["draft_131k_3_steps"] = draft_131k_measurements(flag, reps, dev)
         log("mixed batch (4 sequences)")
         details["mixed_batch"] = mixed_batch(flag, reps, dev)
         log("1M draft step, 4 q heads / 1 KV head / d=64")
@@ -719,8 +911,8 @@ def main():
     g = wl.gamma
     bytes_win, bytes_nat = step_bytes(n0, wl, True), step_bytes(n0, wl, False)
     ver_bytes = verify_launch_bytes(n0 + g + 1, wl, g + 1)
-    ver_avg_ms = (ver_ms + ver_ms2) / 2
-    achieved = ver_bytes / (ver_avg_ms * 1e-3) / 1e9
+    achieved = ver_bytes / (ver_ms * 1e-3) / 1e9
+    ver_all = np.asarray(flat(rw["verify"]), dtype=np.float64)
     res = {
         "metric": METRIC,
         "value": round(win_ms * 1e3, 1),
@@ -743,6 +935,7 @@ def main():
             "draft_pv": "fp32 weights" if args.exact_pv else "bf16 weight pairs",
             "pool_layout": ("[blocks][H_kv][K|V][16][D]" if args.pool_layout == "kv_runs"
                             else "[blocks][H_kv][16][D] per K and V"),
+            "statistic": "median of the timed steps",
         },
         "windowed_us_per_step": round(win_ms * 1e3, 1),
         "native_us_per_step": round(nat_ms * 1e3, 1),
@@ -752,9 +945,12 @@ def main():
         "windowed_pct_peak": round(100 * bytes_win / (win_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "native_pct_peak": round(100 * bytes_nat / (nat_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "kernels_us": {
-            "verify_per_layer": round(ver_avg_ms * 1e3, 2),
+            "verify_per_layer": round(ver_ms * 1e3, 2),
+            "verify_per_layer_native_arm": round(ver_ms_nat * 1e3, 2),
             "draft_window_per_step": round(dwin_ms * 1e3, 2),
             "draft_native_per_step": round(dnat_ms * 1e3, 2),
+            "verify_combine": round(med(flat(rw["verify_combine"])) * 1e3, 2),
+            "draft_combine_window": round(med(flat(rw["draft_combine"])) * 1e3, 2),
         },
         "roofline": {
             "kernel": (f"{verify_kernel_name(g + 1, wl.group)} (verify, {wl.target_layers} launches per step)"),
@@ -766,6 +962,9 @@ def main():
             # counters were taken on the default workload (1M keys, gamma 3, K|V-run pools)
             "traffic": (verify_traffic_bytes() if (n0, g, args.pool_layout) == (1 << 20, 3, "kv_runs") else None),
             "algorithmic_bytes": ver_bytes,
+            "launch_us_median": round(ver_ms * 1e3, 2),
+            "launch_us_mean": round(float(ver_all.mean()) * 1e3, 2),
+            "launches": int(ver_all.size),
             "measured_read_ceiling": round(ceiling, 1),
             "frac_of_measured_ceiling": round(achieved / ceiling, 4),
             "measured_paged_read_ceiling": round(paged_ceiling, 1),
@@ -774,6 +973,7 @@ def main():
     }
     native_draft_bytes = draft_launch_bytes(n0 + 1, wl, True)
     res["draft_native_gbps"] = round(native_draft_bytes / (dnat_ms * 1e-3) / 1e9, 1)
+    res["draft_native_pct_peak"] = round(100 * native_draft_bytes / (dnat_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)
     res["details"] = details
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")

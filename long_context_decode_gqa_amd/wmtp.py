@@ -256,30 +256,65 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 
 # ---------------------------------------------------------------- hot path
+class Prepared:
+    """One C-ABI call whose ctypes arguments were built once: calling it launches the same work again
+    (same pointers, sizes and stream), with no argument marshalling on the host.  An attention call
+    fills `parts` (the split partials it writes into its workspace) each time it runs."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple = (), parts: Optional["Partials"] = None):
+        self.name, self.parts = name, parts
+        self._fn, self._args, self._keep = getattr(load(), name), args, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st < 0:
+            _check(self.name, st)
+
+
+def _attn_call(name: str, lead: tuple, seq_lens: Sequence[int], tail_before_ws: tuple, ws: torch.Tensor,
+               stream, keep: tuple) -> Prepared:
+    """Arguments of the four attention entry points: lead..., seq_lens_host, batch, split size, workspace,
+    workspace bytes, parts, stream."""
+    parts = Partials()
+    parts._workspace = ws   # the partials live in ws: keep it alive with them
+    lens = _lens(seq_lens)
+    args = lead + (ctypes.cast(lens, ctypes.c_void_p), len(seq_lens)) + tail_before_ws + (
+        ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(parts), _stream(stream))
+    return Prepared(name, args, keep + (lens, ws), parts)
+
+
+def _ref(x):
+    return ctypes.byref(x) if x is not None else None
+
+
+def prepare_draft_attn(mode: int, shape: Shape, q: torch.Tensor, seq_lens: Sequence[int], ws: torch.Tensor,
+                       paged: Optional[Paged] = None, ring: Optional[Ring] = None, chunk_tokens: int = 0,
+                       stream=None) -> Prepared:
+    _device_tensor("q", q, len(seq_lens) * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
+    return _attn_call("wmtp_draft_attn", (mode, ctypes.byref(shape), q.data_ptr(), _ref(paged), _ref(ring)),
+                      seq_lens, (chunk_tokens,), ws, stream, (shape, q, paged, ring))
+
+
 def draft_attn(mode: int, shape: Shape, q: torch.Tensor, seq_lens: Sequence[int], ws: torch.Tensor,
                paged: Optional[Paged] = None, ring: Optional[Ring] = None, chunk_tokens: int = 0,
                stream=None) -> Partials:
-    _device_tensor("q", q, len(seq_lens) * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
-    parts = Partials()
-    _check("wmtp_draft_attn", load().wmtp_draft_attn(
-        mode, ctypes.byref(shape), q.data_ptr(), ctypes.byref(paged) if paged is not None else None,
-        ctypes.byref(ring) if ring is not None else None, ctypes.cast(_lens(seq_lens), ctypes.c_void_p),
-        len(seq_lens), chunk_tokens, ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(parts),
-        _stream(stream)))
-    parts._workspace = ws   # the partials live in ws: keep it alive with them
-    return parts
+    call = prepare_draft_attn(mode, shape, q, seq_lens, ws, paged, ring, chunk_tokens, stream)
+    call()
+    return call.parts
+
+
+def prepare_verify_attn(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, seq_lens: Sequence[int],
+                        ws: torch.Tensor, split_tokens: int = 0, stream=None) -> Prepared:
+    _device_tensor("q", q, len(seq_lens) * t_q * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
+    return _attn_call("wmtp_verify_attn", (ctypes.byref(shape), q.data_ptr(), t_q, _ref(paged)),
+                      seq_lens, (split_tokens,), ws, stream, (shape, q, paged))
 
 
 def verify_attn(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, seq_lens: Sequence[int], ws: torch.Tensor,
                 split_tokens: int = 0, stream=None) -> Partials:
-    _device_tensor("q", q, len(seq_lens) * t_q * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
-    parts = Partials()
-    _check("wmtp_verify_attn", load().wmtp_verify_attn(
-        ctypes.byref(shape), q.data_ptr(), t_q, ctypes.byref(paged), ctypes.cast(_lens(seq_lens), ctypes.c_void_p),
-        len(seq_lens), split_tokens, ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(parts),
-        _stream(stream)))
-    parts._workspace = ws   # the partials live in ws: keep it alive with them
-    return parts
+    call = prepare_verify_attn(shape, q, t_q, paged, seq_lens, ws, split_tokens, stream)
+    call()
+    return call.parts
 
 
 def _new_tokens(shape: Shape, k_new: torch.Tensor, v_new: torch.Tensor, batch: int, t_new: int) -> None:
@@ -293,39 +328,47 @@ def _new_tokens(shape: Shape, k_new: torch.Tensor, v_new: torch.Tensor, batch: i
             raise ValueError(f"{name}: expected a GPU tensor, got device {x.device}")
 
 
+def prepare_draft_attn_append(mode: int, shape: Shape, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                              seq_lens: Sequence[int], ws: torch.Tensor, paged: Optional[Paged] = None,
+                              ring: Optional[Ring] = None, chunk_tokens: int = 0, stream=None) -> Prepared:
+    _device_tensor("q", q, len(seq_lens) * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
+    _new_tokens(shape, k_new, v_new, len(seq_lens), 1)
+    return _attn_call("wmtp_draft_attn_append",
+                      (mode, ctypes.byref(shape), q.data_ptr(), _ref(paged), _ref(ring), k_new.data_ptr(),
+                       v_new.data_ptr()), seq_lens, (chunk_tokens,), ws, stream, (shape, q, paged, ring, k_new, v_new))
+
+
 def draft_attn_append(mode: int, shape: Shape, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                       seq_lens: Sequence[int], ws: torch.Tensor, paged: Optional[Paged] = None,
                       ring: Optional[Ring] = None, chunk_tokens: int = 0, stream=None) -> Partials:
     """Append one token per sequence at position seq_lens[b] - 1 (paged or ring) and attend, in one launch."""
-    _device_tensor("q", q, len(seq_lens) * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
-    _new_tokens(shape, k_new, v_new, len(seq_lens), 1)
-    parts = Partials()
-    _check("wmtp_draft_attn_append", load().wmtp_draft_attn_append(
-        mode, ctypes.byref(shape), q.data_ptr(), ctypes.byref(paged) if paged is not None else None,
-        ctypes.byref(ring) if ring is not None else None, k_new.data_ptr(), v_new.data_ptr(),
-        ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), chunk_tokens, ws.data_ptr(),
-        ws.numel() * ws.element_size(), ctypes.byref(parts), _stream(stream)))
-    parts._workspace = ws   # the partials live in ws: keep it alive with them
-    return parts
+    call = prepare_draft_attn_append(mode, shape, q, k_new, v_new, seq_lens, ws, paged, ring, chunk_tokens, stream)
+    call()
+    return call.parts
+
+
+def prepare_verify_attn_append(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, k_new: torch.Tensor,
+                               v_new: torch.Tensor, seq_lens: Sequence[int], ws: torch.Tensor, split_tokens: int = 0,
+                               stream=None) -> Prepared:
+    _device_tensor("q", q, len(seq_lens) * t_q * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
+    _new_tokens(shape, k_new, v_new, len(seq_lens), t_q)
+    return _attn_call("wmtp_verify_attn_append",
+                      (ctypes.byref(shape), q.data_ptr(), t_q, _ref(paged), k_new.data_ptr(), v_new.data_ptr()),
+                      seq_lens, (split_tokens,), ws, stream, (shape, q, paged, k_new, v_new))
 
 
 def verify_attn_append(shape: Shape, q: torch.Tensor, t_q: int, paged: Paged, k_new: torch.Tensor,
                        v_new: torch.Tensor, seq_lens: Sequence[int], ws: torch.Tensor, split_tokens: int = 0,
                        stream=None) -> Partials:
     """Append the t_q query tokens' K/V at positions seq_lens[b] - t_q .. seq_lens[b] - 1 and verify, in one launch."""
-    _device_tensor("q", q, len(seq_lens) * t_q * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
-    _new_tokens(shape, k_new, v_new, len(seq_lens), t_q)
-    parts = Partials()
-    _check("wmtp_verify_attn_append", load().wmtp_verify_attn_append(
-        ctypes.byref(shape), q.data_ptr(), t_q, ctypes.byref(paged), k_new.data_ptr(), v_new.data_ptr(),
-        ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), split_tokens, ws.data_ptr(),
-        ws.numel() * ws.element_size(), ctypes.byref(parts), _stream(stream)))
-    parts._workspace = ws   # the partials live in ws: keep it alive with them
-    return parts
+    call = prepare_verify_attn_append(shape, q, t_q, paged, k_new, v_new, seq_lens, ws, split_tokens, stream)
+    call()
+    return call.parts
 
 
-def combine(parts: Partials, out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
-    """out: [batch][rows_per_seq][D] fp32 or bf16; lse: fp32 [batch][rows_per_seq] or None (device)."""
+def prepare_combine(parts: Partials, out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+    """out: [batch][rows_per_seq][D] fp32 or bf16; lse: fp32 [batch][rows_per_seq] or None (device).  `parts`
+    must already describe its partials (the attention call that fills it has run)."""
     rows = parts.batch * parts.rows_per_seq
     _device_tensor("out", out, rows * parts.head_dim, (torch.float32, torch.bfloat16), on_gpu=False)
     if lse is not None:
@@ -333,19 +376,35 @@ def combine(parts: Partials, out: torch.Tensor, lse: Optional[torch.Tensor] = No
     for name, t in (("out", out), ("lse", lse)):
         if t is not None and not t.is_cuda:
             raise ValueError(f"{name}: expected a GPU tensor, got device {t.device}")
-    _check("wmtp_combine", load().wmtp_combine(ctypes.byref(parts), out.data_ptr(), _ptr(lse),
-                                               dtype_code(out.dtype), _stream(stream)))
+    return Prepared("wmtp_combine", (ctypes.byref(parts), out.data_ptr(), _ptr(lse), dtype_code(out.dtype),
+                                     _stream(stream)), (parts, out, lse))
+
+
+def combine(parts: Partials, out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """out: [batch][rows_per_seq][D] fp32 or bf16; lse: fp32 [batch][rows_per_seq] or None (device)."""
+    prepare_combine(parts, out, lse, stream)()
+
+
+def _append_call(name: str, shape: Shape, desc, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
+                 stream) -> Prepared:
+    if k_new.dim() != 4:
+        raise ValueError(f"k_new: expected [batch][t_new][H_kv][D], got shape {tuple(k_new.shape)}")
+    _new_tokens(shape, k_new, v_new, len(pos), k_new.shape[1])
+    lens = _lens(pos)
+    return Prepared(name, (ctypes.byref(shape), ctypes.byref(desc), k_new.data_ptr(), v_new.data_ptr(),
+                           ctypes.cast(lens, ctypes.c_void_p), len(pos), k_new.shape[1], _stream(stream)),
+                    (shape, desc, k_new, v_new, lens))
+
+
+def prepare_ring_append(shape: Shape, ring: Ring, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
+                        stream=None) -> Prepared:
+    return _append_call("wmtp_ring_append", shape, ring, k_new, v_new, pos, stream)
 
 
 def ring_append(shape: Shape, ring: Ring, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
                 stream=None) -> None:
     """k_new, v_new: [batch][t_new][H_kv][D]; pos[b]: absolute position of the first new token."""
-    if k_new.dim() != 4:
-        raise ValueError(f"k_new: expected [batch][t_new][H_kv][D], got shape {tuple(k_new.shape)}")
-    _new_tokens(shape, k_new, v_new, len(pos), k_new.shape[1])
-    _check("wmtp_ring_append", load().wmtp_ring_append(
-        ctypes.byref(shape), ctypes.byref(ring), k_new.data_ptr(), v_new.data_ptr(),
-        ctypes.cast(_lens(pos), ctypes.c_void_p), len(pos), k_new.shape[1], _stream(stream)))
+    prepare_ring_append(shape, ring, k_new, v_new, pos, stream)()
 
 
 def ring_rollback(ring: Ring, seq_lens: Sequence[int], stream=None) -> None:
@@ -354,14 +413,14 @@ def ring_rollback(ring: Ring, seq_lens: Sequence[int], stream=None) -> None:
         ctypes.byref(ring), ctypes.cast(_lens(seq_lens), ctypes.c_void_p), len(seq_lens), _stream(stream)))
 
 
+def prepare_paged_append(shape: Shape, paged: Paged, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
+                         stream=None) -> Prepared:
+    return _append_call("wmtp_paged_append", shape, paged, k_new, v_new, pos, stream)
+
+
 def paged_append(shape: Shape, paged: Paged, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
                  stream=None) -> None:
-    if k_new.dim() != 4:
-        raise ValueError(f"k_new: expected [batch][t_new][H_kv][D], got shape {tuple(k_new.shape)}")
-    _new_tokens(shape, k_new, v_new, len(pos), k_new.shape[1])
-    _check("wmtp_paged_append", load().wmtp_paged_append(
-        ctypes.byref(shape), ctypes.byref(paged), k_new.data_ptr(), v_new.data_ptr(),
-        ctypes.cast(_lens(pos), ctypes.c_void_p), len(pos), k_new.shape[1], _stream(stream)))
+    prepare_paged_append(shape, paged, k_new, v_new, pos, stream)()
 
 
 # ---------------------------------------------------------------- index resolution hooks
