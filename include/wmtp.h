@@ -25,7 +25,8 @@
  *    WMTP_E* code.  Argument checks run before any HIP call; on an error no
  *    work is enqueued.  No call aborts, prints, or throws across the boundary.
  *    WMTP_ELAUNCH reports a failed kernel launch (hipGetLastError).
- *  - Thread safety: the library has no mutable global state.
+ *  - Thread safety: the library has no mutable global state, except the fixed
+ *    scratch of wmtp_draft_attn_noalloc (see there).
  *
  * Numbers
  * -------
@@ -258,6 +259,31 @@ int wmtp_verify_attn_append(const wmtp_shape* shape, const void* q, int32_t t_q,
  *  WMTP_BF16, round-to-nearest-even).  lse_out: device [batch][rows_per_seq]
  *  fp32, or NULL. */
 int wmtp_combine(const wmtp_partials* parts, void* out, float* lse_out, int32_t out_dtype, void* stream);
+
+/* For callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  One draft step into final outputs:
+ * wmtp_draft_attn (k_new and v_new NULL) or wmtp_draft_attn_append (both set), then
+ * wmtp_combine into out / lse_out, with the same arguments, kernels and results,
+ * except that the split partials go to a fixed device array of
+ * WMTP_NOALLOC_SCRATCH_BYTES inside the library instead of a caller workspace.
+ *  out: device [batch][H_q][D] of out_dtype (WMTP_F32 or WMTP_BF16), 16-byte
+ *  aligned; lse_out: device [batch][H_q] fp32 or NULL.
+ *  Allocates nothing: no hipMalloc, hipFree or allocating library call.  Each GPU
+ *  that runs the call holds its own copy of the array until the process ends; its
+ *  device address is resolved on the first call on that GPU (make that first call
+ *  outside any graph capture).  A plan whose partials need more than
+ *  WMTP_NOALLOC_SCRATCH_BYTES (wmtp_draft_workspace_bytes gives the size) returns
+ *  WMTP_EWORKSPACE; with the default split sizes, batch x H_kv <= 256 and
+ *  contexts up to 4M tokens need at most 4.3 MB.
+ *  All calls on one GPU share the array, which keeps the last call's partials
+ *  (every split writes all of its rows, so nothing needs clearing): calls that
+ *  overlap on one GPU (other streams, other host threads) race; calls in order
+ *  on one stream do not. */
+#define WMTP_NOALLOC_SCRATCH_BYTES (16 << 20)
+int wmtp_draft_attn_noalloc(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv,
+                            const wmtp_ring* ring, const void* k_new, const void* v_new,
+                            const int32_t* seq_lens_host, int32_t batch, int32_t chunk_tokens, void* out,
+                            float* lse_out, int32_t out_dtype, void* stream);
 
 /* Append t_new tokens per sequence to the compact ring (Windowed-MTP summary,
  * Abstract: the ring holds the draft's window).  Token i of sequence b has

@@ -10,10 +10,40 @@
 #include <cstdint>
 #include <cstring>
 
+#include <mutex>
+
 #include "wmtp.h"
 #include "wmtp_launch.hpp"
 
 using namespace wmtp;
+
+// Split partials of wmtp_draft_attn_noalloc, for callers that cannot allocate: one array per GPU
+// that loads the library, held until the process ends.  Host code never names it except in the
+// hipGetSymbolAddress call below; it uses the device address that call returns.
+static __device__ __align__(256) uint8_t scratch[WMTP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, resolved once per device with that device current.
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return WMTP_ELAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return WMTP_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return WMTP_ELAUNCH;
+    scratch_dev_ptr[dev] = p;
+  }
+  *out = scratch_dev_ptr[dev];
+  return WMTP_OK;
+}
+
+}  // namespace
 
 namespace {
 
@@ -221,6 +251,14 @@ void fill_split_args(SplitArgs& a, const wmtp_shape* s, const Plan& p, const int
 
 int launch_status(hipError_t e) { return e == hipSuccess ? WMTP_OK : WMTP_ELAUNCH; }
 
+// The output side of a combine: out (16-byte aligned), optional lse_out (4-byte aligned), dtype.
+int check_combine_out(const void* out, const float* lse_out, int32_t out_dtype) {
+  if (!out) return WMTP_EINVAL;
+  if (out_dtype != WMTP_F32 && out_dtype != WMTP_BF16) return WMTP_EINVAL;
+  if (!aligned(out, 16) || !aligned(lse_out, 4)) return WMTP_EALIGN;
+  return WMTP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,9 +294,11 @@ int check_new_tokens(const void* k_new, const void* v_new, int32_t t_new, const 
   return WMTP_OK;
 }
 
+// check_only: run every argument check and the plan, then return before touching *parts or the GPU.
 int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv, const wmtp_ring* ring,
                const void* k_new, const void* v_new, int32_t t_new, const int32_t* seq_lens_host, int32_t batch,
-               int32_t chunk_tokens, void* workspace, size_t workspace_bytes, wmtp_partials* parts, void* stream) {
+               int32_t chunk_tokens, void* workspace, size_t workspace_bytes, wmtp_partials* parts, void* stream,
+               bool check_only = false) {
   const int base_mode = mode & 0xF;
   int32_t sink = 0, window = 1, headroom = 0;
   if (base_mode == WMTP_SINK_WINDOW) {
@@ -291,7 +331,7 @@ int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_
   if (!aligned(workspace, 256)) return WMTP_EALIGN;
   if ((int64_t)workspace_bytes < p.bytes) return WMTP_EWORKSPACE;
   st = check_new_tokens(k_new, v_new, t_new, seq_lens_host, batch);
-  if (st) return st;
+  if (st || check_only) return st;
 
   fill_parts(p, workspace, batch, shape->head_dim, parts);
   SplitArgs a;
@@ -420,7 +460,9 @@ int wmtp_verify_attn_append(const wmtp_shape* shape, const void* q, int32_t t_q,
 }
 
 int wmtp_combine(const wmtp_partials* parts, void* out, float* lse_out, int32_t out_dtype, void* stream) {
-  if (!parts || !out) return WMTP_EINVAL;
+  if (!parts) return WMTP_EINVAL;
+  const int st = check_combine_out(out, lse_out, out_dtype);
+  if (st) return st;
   if (out_dtype != WMTP_F32 && out_dtype != WMTP_BF16) return WMTP_EINVAL;
   if (parts->batch < 1 || parts->batch > WMTP_MAX_BATCH || parts->rows_per_seq < 1) return WMTP_EINVAL;
   if (parts->head_dim != 64 && parts->head_dim != 128 && parts->head_dim != 256) return WMTP_EUNSUPPORTED;
@@ -428,7 +470,7 @@ int wmtp_combine(const wmtp_partials* parts, void* out, float* lse_out, int32_t 
   for (int b = 0; b < parts->batch; ++b)
     if (parts->split_base[b + 1] < parts->split_base[b]) return WMTP_EINVAL;
   if (parts->total_splits > 0 && (!parts->o || !parts->lse)) return WMTP_EINVAL;
-  if (!aligned(parts->o, 16) || !aligned(out, 16) || !aligned(lse_out, 4)) return WMTP_EALIGN;
+  if (!aligned(parts->o, 16)) return WMTP_EALIGN;
   CombineArgs a;
   std::memset(&a, 0, sizeof(a));
   a.part_o = parts->o;
@@ -588,13 +630,35 @@ int wmtp_stream_read_paged(const void* k, const void* v, int64_t pool_bytes, con
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int wmtp_draft_attn_noalloc(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_paged* kv,
+                            const wmtp_ring* ring, const void* k_new, const void* v_new,
+                            const int32_t* seq_lens_host, int32_t batch, int32_t chunk_tokens, void* out,
+                            float* lse_out, int32_t out_dtype, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return WMTP_EINVAL;
+  const int32_t t_new = k_new ? 1 : 0;
+  // Every check, including the plan's size against the fixed scratch, before any HIP call.
+  wmtp_partials parts;
+  int st = draft_attn(mode, shape, q, kv, ring, k_new, v_new, t_new, seq_lens_host, batch, chunk_tokens,
+                      reinterpret_cast<void*>(uintptr_t{256}), WMTP_NOALLOC_SCRATCH_BYTES, &parts, stream, true);
+  if (st) return st;
+  st = check_combine_out(out, lse_out, out_dtype);
+  if (st) return st;
+  void* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st) return st;
+  st = draft_attn(mode, shape, q, kv, ring, k_new, v_new, t_new, seq_lens_host, batch, chunk_tokens, ws,
+                  WMTP_NOALLOC_SCRATCH_BYTES, &parts, stream);
+  if (st) return st;
+  return wmtp_combine(&parts, out, lse_out, out_dtype, stream);
+}
+
 const char* wmtp_status_str(int status) {
   switch (status) {
     case WMTP_OK: return "ok";
     case WMTP_EINVAL: return "invalid argument";
     case WMTP_EUNSUPPORTED: return "unsupported shape or dtype";
     case WMTP_EALIGN: return "pointer not aligned";
-    case WMTP_EWORKSPACE: return "workspace too small";
+    case WMTP_EWORKSPACE: return "workspace too small (or the plan exceeds the fixed scratch of the no-allocation call)";
     case WMTP_ELAUNCH: return "kernel launch failed";
   }
   return "unknown status";

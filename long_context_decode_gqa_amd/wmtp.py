@@ -25,6 +25,7 @@ DRAFT_FAST_PV = 0x10
 MAX_BATCH = 64
 BLOCK_SIZE = 16
 MAX_SEQ_LEN = 1 << 30
+NOALLOC_SCRATCH_BYTES = 16 << 20
 MAX_VERIFY_ROWS = 96
 
 
@@ -73,7 +74,7 @@ EXPORTS = (
     "wmtp_draft_attn_append", "wmtp_verify_attn_append", "wmtp_combine", "wmtp_ring_append", "wmtp_ring_rollback", "wmtp_paged_append", "wmtp_debug_resolve_paged",
     "wmtp_debug_resolve_ring", "wmtp_debug_window_positions", "wmtp_plan_memory", "wmtp_stream_read",
     "wmtp_stream_read_paged", "wmtp_status_str",
-    "wmtp_version",
+    "wmtp_version", "wmtp_draft_attn_noalloc",
 )
 
 _lib = None
@@ -103,6 +104,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.wmtp_verify_attn_append.argtypes = [sp, P, I32, pp, P, P, P, I32, I32, P, SZ, tp, P]
     lib.wmtp_verify_attn_append.restype = ctypes.c_int
     lib.wmtp_combine.argtypes = [tp, P, P, I32, P]
+    lib.wmtp_draft_attn_noalloc.argtypes = [I32, sp, P, pp, rp, P, P, P, I32, I32, P, P, I32, P]
+    lib.wmtp_draft_attn_noalloc.restype = ctypes.c_int
     lib.wmtp_combine.restype = ctypes.c_int
     lib.wmtp_ring_append.argtypes = [sp, rp, P, P, P, I32, I32, P]
     lib.wmtp_ring_append.restype = ctypes.c_int
@@ -399,6 +402,30 @@ def _append_call(name: str, shape: Shape, desc, k_new: torch.Tensor, v_new: torc
 def prepare_ring_append(shape: Shape, ring: Ring, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],
                         stream=None) -> Prepared:
     return _append_call("wmtp_ring_append", shape, ring, k_new, v_new, pos, stream)
+
+
+def draft_attn_noalloc(mode: int, shape: Shape, q: torch.Tensor, seq_lens: Sequence[int], out: torch.Tensor,
+                       lse: Optional[torch.Tensor] = None, paged: Optional[Paged] = None, ring: Optional[Ring] = None,
+                       k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                       chunk_tokens: int = 0, stream=None) -> None:
+    """A draft step (with the append inside when k_new / v_new are given) and its combine into out
+    [batch][H_q][D] (fp32 or bf16) and lse [batch][H_q], using the library's fixed scratch: no
+    workspace, and nothing allocated by the library."""
+    batch = len(seq_lens)
+    _device_tensor("q", q, batch * shape.num_q_heads * shape.head_dim, (_shape_dtype(shape),))
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new: give both or neither")
+    if k_new is not None:
+        _new_tokens(shape, k_new, v_new, batch, 1)
+    rows = batch * shape.num_q_heads
+    _device_tensor("out", out, rows * shape.head_dim, (torch.float32, torch.bfloat16))
+    if lse is not None:
+        _device_tensor("lse", lse, rows, (torch.float32,))
+    lens = _lens(seq_lens)
+    _check("wmtp_draft_attn_noalloc", load().wmtp_draft_attn_noalloc(
+        mode, ctypes.byref(shape), q.data_ptr(), _ref(paged), _ref(ring), _ptr(k_new), _ptr(v_new),
+        ctypes.cast(lens, ctypes.c_void_p), batch, chunk_tokens, out.data_ptr(), _ptr(lse), dtype_code(out.dtype),
+        _stream(stream)))
 
 
 def ring_append(shape: Shape, ring: Ring, k_new: torch.Tensor, v_new: torch.Tensor, pos: Sequence[int],

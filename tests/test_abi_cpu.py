@@ -541,3 +541,35 @@ def test_descriptors_keep_their_tensors_alive():
         gc.collect()
         assert all(r() is None for r in refs)
 
+
+
+def test_noalloc_draft_checks_before_any_hip_call():
+    """wmtp_draft_attn_noalloc runs every check of the draft and combine calls, and sizes its plan
+    against the fixed scratch, before its first HIP call: each invalid call here returns on a
+    machine without a GPU."""
+    lib = W.load()
+    sh = shape()
+    kv, rg = paged(mb=1 << 17), ring()
+
+    def call(mode=W.FULL | W.DRAFT_FAST_PV, q=FAKE, k_new=None, v_new=None, seq=(1000,), chunk=0, out=FAKE, lse=None,
+             dt=W.F32, kvp=kv, rgp=rg):
+        return lib.wmtp_draft_attn_noalloc(mode, ctypes.byref(sh), q, ctypes.byref(kvp) if kvp else None,
+                                           ctypes.byref(rgp) if rgp else None, k_new, v_new, lens(*seq), len(seq),
+                                           chunk, out, lse, dt, None)
+    assert call(q=None) == W.EINVAL
+    assert call(k_new=FAKE) == W.EINVAL                         # k_new without v_new
+    assert call(out=None) == W.EINVAL
+    assert call(out=FAKE_ODD) == W.EALIGN
+    assert call(lse=FAKE + 2) == W.EALIGN
+    assert call(dt=5) == W.EINVAL
+    assert call(kvp=None) == W.EINVAL
+    assert call(mode=W.SINK_WINDOW, rgp=None) == W.EINVAL
+    assert call(seq=(2 ** 31 - 1,)) == W.EINVAL
+    # 64-key splits over 1M keys: 16,384 splits x 16 rows x 1,028 bytes, past the 16 MiB scratch
+    n = 1 << 20
+    need = lib.wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(n), 1, 64, 0, 1, 0)
+    assert need > W.NOALLOC_SCRATCH_BYTES
+    assert call(seq=(n,), chunk=64) == W.EWORKSPACE
+    assert "scratch" in lib.wmtp_status_str(W.EWORKSPACE).decode()
+    # the default splits at the same length fit
+    assert lib.wmtp_draft_workspace_bytes(W.FULL, ctypes.byref(sh), lens(n), 1, 0, 0, 1, 0) <= W.NOALLOC_SCRATCH_BYTES
