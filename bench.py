@@ -103,10 +103,11 @@ def stream_ceiling_gbps(dev, nbytes=2 << 30):
     return best
 
 
-def paged_ceiling_gbps(step):
+def paged_ceiling_gbps(step, run_kib=16):
     """Best rate of the paged streaming-read probe over one verify layer's pool, read in the
     block table's order, one head's blocks after another: per (block, head) the 8 KiB of K and
-    the 8 KiB of V after it, i.e. the verify's own access pattern without its arithmetic."""
+    the 8 KiB of V after it, i.e. the verify's own access pattern without its arithmetic.
+    run_kib=32 (K|V pools): per block the 32 KiB of both heads instead."""
     wl, n = step.wl, step.n0 + step.wl.gamma + 1
     pool = step.layers[1][0]
     nb = synth.blocks_for(n, 16)
@@ -114,7 +115,13 @@ def paged_ceiling_gbps(step):
     run_bytes = 16 * wl.head_dim * 2                       # one (block, head) half: K or V
     bt = step.bt[0, :nb].to(torch.int64)
     runs = torch.cat([bt * Hk + h for h in range(Hk)])
-    if step.kv_runs:
+    if step.kv_runs and run_kib == 32:
+        # both heads of a block, 32 KiB in the K|V pool: halves of 16 KiB read back to back
+        flat = pool.view(-1)
+        run_bytes = Hk * run_bytes
+        k, v = flat, flat[run_bytes // 2:]
+        runs = 2 * bt
+    elif step.kv_runs:
         flat = pool.view(-1)
         k, v = flat, flat[run_bytes // 2:]                 # V of a run starts 8 KiB after its K
         runs = 2 * runs
@@ -316,37 +323,48 @@ def draft_launch_bytes(entries, wl, paged):
     return b + (synth.blocks_for(entries, 16) * 4 if paged else entries * 4)
 
 
-def time_steps(step, mode, flag, steps, warmup, fused=True):
-    """Warmup, then `steps` decode steps with an event on the launch stream before the step and after
-    every launch: the interval ending at a launch's event is that launch's time on the device's
-    timeline (any idle gap before it included).  The launches are prepared C-ABI calls and the
-    garbage collector is off in the timed loop, so no host pause lands between them.
-    Returns {"step": [ms per step], kind: [[ms per launch of that kind] per step]}."""
+def time_steps(step, mode, flag, steps, warmup, fused=True, per_launch=True):
+    """Warmup, then `steps` decode steps of prepared C-ABI calls with the garbage collector off.
+
+    Two timed passes over the same launches: the first records events only at step boundaries
+    (the step times: an event recorded between two launches costs device time, 2-5 us each at
+    this size); the second records an event after every launch as well, and the interval ending
+    at a launch's event is that launch's time on the device's timeline, any idle gap before it
+    included.  Returns {"step": [ms per step], kind: [[ms per launch of that kind] per step]}
+    (launch kinds from the second pass, or none with per_launch=False)."""
     calls = step.calls(mode, flag, fused)
     torch.cuda.synchronize()
     for _ in range(warmup):
         for _, _, c in calls:
             c()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    gc_was = gc.isenabled()
-    gc.disable()
-    try:
-        for s in range(steps):
-            ev = evs[s]
-            ev[0].record()
-            for i, (_, _, c) in enumerate(calls):
-                c()
-                ev[i + 1].record()
+    res = {}
+    for every in ((False, True) if per_launch else (False,)):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
         torch.cuda.synchronize()
-    finally:
-        if gc_was:
-            gc.enable()
-    res = {"step": [ev[0].elapsed_time(ev[-1]) for ev in evs]}
-    for i, (kind, _, _) in enumerate(calls):
-        res.setdefault(kind, [[] for _ in range(steps)])
-        for s in range(steps):
-            res[kind][s].append(evs[s][i].elapsed_time(evs[s][i + 1]))
+        gc_was = gc.isenabled()
+        gc.disable()
+        try:
+            for s in range(steps):
+                ev = evs[s]
+                ev[0].record()
+                for i, (_, _, c) in enumerate(calls):
+                    c()
+                    if every:
+                        ev[i + 1].record()
+                if not every:
+                    ev[-1].record()
+            torch.cuda.synchronize()
+        finally:
+            if gc_was:
+                gc.enable()
+        if not every:
+            res["step"] = [ev[0].elapsed_time(ev[-1]) for ev in evs]
+            continue
+        res["step_with_launch_events"] = [ev[0].elapsed_time(ev[-1]) for ev in evs]
+        for i, (kind, _, _) in enumerate(calls):
+            res.setdefault(kind, [[] for _ in range(steps)])
+            for s in range(steps):
+                res[kind][s].append(evs[s][i].elapsed_time(evs[s][i + 1]))
     return res
 
 
@@ -471,6 +489,29 @@ def window_measurements(step, flag, reps, dev, contexts):
     res["cold_median_by_context"] = by_ctx
     # rollback after a partial acceptance: forget the drafts past n0 + 1
     res["ring_rollback_us"] = pct(_timed(lambda: W.ring_rollback(step.ring, [n0 + 1]), reps))["median"]
+    # The step is two short launches, so latency sets its cost.  Queued back to back (the device's
+    # throughput for them) beside a one-block torch kernel as the floor of any launch; the figures
+    # above, one step between two events, add the events' own cost (compare the empty launch).
+    a = W.prepare_draft_attn_append(W.SINK_WINDOW | flag, step.sh, step.q_draft[0], step.k_draft[0],
+                                    step.v_draft[0], [n0 + 1], step.ws_win, ring=step.ring, chunk_tokens=step.chunk_win)
+    a()
+    c = W.prepare_combine(a.parts, step.out_d, step.lse_d)
+    x = torch.zeros(64, device=dev)
+
+    def back_to_back(fn, count=20):
+        fn()
+        torch.cuda.synchronize()
+        _hold(2000000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(count):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / count * 1e3, 2)
+    res["back_to_back_us"] = {"step": back_to_back(lambda: (a(), c())), "attention": back_to_back(a),
+                              "combine": back_to_back(c), "empty_launch": back_to_back(lambda: x.add_(1))}
+    res["empty_launch_between_events_us"] = pct(_timed(lambda: x.add_(1), reps))["median"]
     return res
 
 
@@ -850,6 +891,7 @@ def main():
 
     log("paged streaming-read ceiling")
     paged_ceiling = paged_ceiling_gbps(step)
+    paged_ceiling_32k = paged_ceiling_gbps(step, 32) if args.pool_layout == "kv_runs" else None
     log("timing windowed step")
     rw = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup)
     log("timing native step")
@@ -869,19 +911,24 @@ def main():
             # the step contains its verify launches: L x their median cannot exceed the step's median
             "verify_layers_within_step": bool(L * ver_ms <= win_ms and L * ver_ms_nat <= nat_ms),
             # the launches' medians add up to the step's median within 2% (nothing else is timed)
-            "launch_sum_over_step": {arm: round(sum(med(flat(r[k])) * len(r[k][0]) for k in r if k != "step")
-                                                / med(r["step"]), 4) for arm, r in (("windowed", rw), ("native", rn))},
+            "launch_sum_over_step": {arm: round(sum(med(flat(r[k])) * len(r[k][0]) for k in r if k.islower()
+                                                    and not k.startswith("step")) / med(r["step_with_launch_events"]),
+                                                4) for arm, r in (("windowed", rw), ("native", rn))},
+            # device time the per-launch events add to a step (the step times above have none)
+            "launch_events_cost_us": {arm: round((med(r["step_with_launch_events"]) - med(r["step"])) * 1e3, 1)
+                                      for arm, r in (("windowed", rw), ("native", rn))},
         },
-        "timing": ("median over the timed steps; an event after every launch on the launch stream; prepared "
-                   "C-ABI calls with the garbage collector off"),
+        "timing": ("median over the timed steps, events at step boundaries only; per-launch times from a second "
+                   "pass with an event after every launch on the launch stream; prepared C-ABI calls with the "
+                   "garbage collector off"),
     }
     if not details["self_check"]["verify_layers_within_step"]:
         log("WARNING: verify launches exceed their step")
     if not args.no_details:
         reps = 20
         log("unfused steps (append calls before the attention calls)")
-        uw = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup, fused=False)
-        un = time_steps(step, W.FULL, flag, args.steps, args.warmup, fused=False)
+        uw = time_steps(step, W.SINK_WINDOW, flag, args.steps, args.warmup, fused=False, per_launch=False)
+        un = time_steps(step, W.FULL, flag, args.steps, args.warmup, fused=False, per_launch=False)
         details["unfused_step_us"] = {"windowed": pct(uw["step"]), "native": pct(un["step"])}
         log("graph-captured steps")
         gw, okw = graph_step(step, W.SINK_WINDOW, flag, 20)
@@ -969,6 +1016,9 @@ def main():
             "frac_of_measured_ceiling": round(achieved / ceiling, 4),
             "measured_paged_read_ceiling": round(paged_ceiling, 1),
             "frac_of_paged_ceiling": round(achieved / paged_ceiling, 4),
+            # the same probe over runs of both heads of a block (32 KiB), what one work item per
+            # block covering both heads would read
+            "measured_paged_read_ceiling_32k_runs": (round(paged_ceiling_32k, 1) if paged_ceiling_32k else None),
         },
     }
     native_draft_bytes = draft_launch_bytes(n0 + 1, wl, True)

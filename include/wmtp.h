@@ -191,7 +191,7 @@ int64_t wmtp_verify_workspace_bytes(const wmtp_shape* shape, int32_t t_q, const 
  *                            seq_window), and the cost follows min(n, S_b + W_b).
  *  n_b = seq_lens_host[b] (host) is the length after this step's own entry was
  *  appended, so the query attends to itself.  q: device [batch][H_q][D].
- *  chunk_tokens: entries per split (a multiple of 64).  0 = library default:
+ *  chunk_tokens: entries per split (a multiple of 32).  0 = library default:
  *  the smallest multiple of 64 (at most 65536) for which the work items
  *  (sequence, KV head, split) fit one round of 256 x max(1, 512 / row bytes)
  *  items in WMTP_FULL mode (one per MI355X compute unit at head_dim 256 in

@@ -195,7 +195,7 @@ int draft_plan(int32_t mode, const wmtp_shape* shape, const int32_t* seq_lens, i
     chunk = base_mode == WMTP_FULL ? default_split(bound, batch, shape->num_kv_heads, full_slots, kFullMinSplit)
                                    : default_split(bound, batch, shape->num_kv_heads, kWindowSlots, kWindowMinSplit);
   }
-  if (chunk < kDraftTile || chunk % kDraftTile != 0) return WMTP_EINVAL;
+  if (chunk < kVerifyTile || chunk % kVerifyTile != 0) return WMTP_EINVAL;   // whole 32-key tiles
   *chunk_out = chunk;
   return make_plan(vis, batch, chunk, shape->num_q_heads, shape->head_dim, shape->num_kv_heads, p);
 }

@@ -90,7 +90,8 @@ def draft(mode=W.FULL, sh=None, q=FAKE, kv="default", rg="default", seq=(1000,),
     (dict(kv=paged(rr=8)), W.EINVAL),                           # runs closer than 16 rows overlap
     (dict(kv=paged(rr=-16)), W.EINVAL),
     (dict(seq=(-1,)), W.EINVAL),
-    (dict(chunk=100), W.EINVAL),                                # not a multiple of 64
+    (dict(chunk=100), W.EINVAL),                                # not a multiple of 32
+    (dict(chunk=16), W.EINVAL),
     (dict(ws=None), W.EINVAL),
     (dict(ws=FAKE + 16), W.EALIGN),
     (dict(wsb=16), W.EWORKSPACE),

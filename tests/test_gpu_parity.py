@@ -408,11 +408,14 @@ def test_draft_tiny_fp32_4k_three_steps(mode):
     say("draft tiny fp32 4k", mode)
     eo, el = draft_steps(wl, None, mode)
     assert eo <= TOL["f32"] and el <= TOL["f32"], (eo, el)
+    eo, el = draft_steps(wl, None, mode, chunk=32)                 # splits of half a 64-key tile
+    assert eo <= TOL["f32"] and el <= TOL["f32"], (eo, el)
 
 
 @pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
 @pytest.mark.parametrize("fast_pv", [False, True])
-@pytest.mark.parametrize("n0,chunk", [(1, 64), (63, 64), (64, 0), (700, 128), (5000, 256), (9001, 1024)])
+@pytest.mark.parametrize("n0,chunk", [(1, 64), (63, 64), (64, 0), (700, 128), (5000, 256), (9001, 1024),
+                                      (90, 32), (1500, 96)])
 def test_draft_bf16_16q_2kv_d256(mode, fast_pv, n0, chunk):
     wl = synth.workload("draft_131k_bf16", window=1024)
     say("draft bf16", mode, fast_pv, n0, chunk)
