@@ -376,6 +376,11 @@ int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_
     return launch_status(window ? launch_window_mfma(shape->head_dim, group, a, grid, st)
                                 : launch_verify(shape->head_dim, group, true, a, grid, st));
   }
+  // The native step in bf16 with fp32 weights: whole tiles per wave, the scores summed and
+  // exponentiated once per key and row (faster than the slice kernel at every head shape measured).
+  if (shape->dtype == WMTP_BF16 && base_mode == WMTP_FULL)
+    return launch_status(launch_draft_rows(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, a, grid,
+                                           static_cast<hipStream_t>(stream)));
   return launch_status(launch_draft(shape->dtype, shape->head_dim, shape->num_q_heads / shape->num_kv_heads,
                                     base_mode == WMTP_SINK_WINDOW, fast_pv, a, grid,
                                     static_cast<hipStream_t>(stream)));

@@ -42,6 +42,9 @@ struct AppendArgs {
 
 hipError_t launch_draft(int dtype, int head_dim, int group, bool window, bool pv_dot2, const SplitArgs& a,
                         int grid, hipStream_t st);
+// The native draft step in bf16 with fp32 softmax weights: each wave owns whole tiles of keys over
+// all of head_dim (wmtp_draft_rows.hip).
+hipError_t launch_draft_rows(int head_dim, int group, const SplitArgs& a, int grid, hipStream_t st);
 // Matrix-core split-K attention over the paged pool (bf16, head_dim 256) for
 // a.t_q query tokens, or for exactly one when single_query is set.
 hipError_t launch_verify(int head_dim, int group, bool single_query, const SplitArgs& a, int grid, hipStream_t st);

@@ -472,6 +472,19 @@ def test_draft_matrix_core_groupings(mode, hq, hk, d):
     assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
 
 
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_draft_fp32_weight_groupings(g, d):
+    """fp32 PV weights in full mode run the whole-tile vector kernel: every grouping G = 1, 2, 4, 8
+    at head_dim 64, 128 and 256 (16- or 32-key tiles; the lanes of a key hold whole scores of
+    G / parts rows after the part sums), with fused appends, ragged lengths, an empty sequence
+    and splits of 96 keys (a partial last tile)."""
+    wl = synth.workload("draft_131k_bf16", num_q_heads=2 * g, num_kv_heads=2, head_dim=d, window=300)
+    say("draft fp32-weight groupings", g, d)
+    eo, el = draft_steps(wl, (1500, 0, 77), O.FULL, chunk=96, fast_pv=False, fused=True)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
 @pytest.mark.parametrize("hq,hk,d", [(8, 8, 64), (4, 2, 128), (4, 1, 64), (16, 4, 256)])
 def test_draft_other_head_shapes(hq, hk, d):
     wl = synth.workload("draft_131k_bf16", num_q_heads=hq, num_kv_heads=hk, head_dim=d, window=300)
