@@ -304,6 +304,19 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
       l_lane[g] += p[g];
     }
 
+    // Masked entries get p = 0, but their values may be any bits (rows past a sequence's end in
+    // its last block, ring slots never written or stale), and 0 x NaN is NaN: on a tile with
+    // such entries their values are zeroed.  Entry of V load k: as in the loads above.
+    const uint64_t vis = __ballot(valid);
+    if (vis != ~0ull) {
+      const int v_tok = ln / LPR;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int tt = PV_DOT2 ? 2 * (k >> 1) * TPV + 2 * v_tok + (k & 1) : k * TPV + v_tok;
+        if (!((vis >> tt) & 1ull)) vreg[slot][k] = uint2{0u, 0u};
+      }
+    }
+
     // ---- hand p to the PV lanes through the (now free) K stage
     float* pl_lds = reinterpret_cast<float*>(my_k);
 #pragma unroll

@@ -305,13 +305,18 @@ __global__ __launch_bounds__(D / kVQ * 64, 8 / (D / kVQ)) void mfma_attn_kernel(
     // ---- mask, lazy row maximum.  Paged: only tiles that reach a causal or
     // split boundary.  Ring: keys past the split and holes, from one ballot of
     // the tile's tags (bit k: key k is visible).
+    // Keys no row may see get p = 0, but their values may be any bits (rows past a sequence's
+    // end in its last block, ring slots never written or stale), and 0 x NaN is NaN: their V
+    // elements are zeroed too.  V element (ks, jj) of this lane is the key of score x = 8 ks + jj.
     if constexpr (RING) {
       const uint32_t live = (uint32_t)__ballot(t0 + c32 < t_end && tagreg[slot] == wv.pos(t0 + c32));
       if (live != 0xffffffffu) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int key = 8 * (x >> 2) + 4 * kh + (x & 3);
-          s2[x] = (live >> key) & 1u ? s2[x] : kNegInf;
+          const bool vis = (live >> key) & 1u;
+          s2[x] = vis ? s2[x] : kNegInf;
+          vreg[slot][x >> 3][x & 7] = vis ? vreg[slot][x >> 3][x & 7] : 0u;
         }
       }
     } else if (t0 + kVTile - 1 > all_last) {
@@ -319,6 +324,7 @@ __global__ __launch_bounds__(D / kVQ * 64, 8 / (D / kVQ)) void mfma_attn_kernel(
       for (int x = 0; x < 16; ++x) {
         const int key = t0 + 8 * (x >> 2) + 4 * kh + (x & 3);
         s2[x] = key <= row_last ? s2[x] : kNegInf;
+        vreg[slot][x >> 3][x & 7] = key < t_end ? vreg[slot][x >> 3][x & 7] : 0u;
       }
     }
     float mx = s2[0];

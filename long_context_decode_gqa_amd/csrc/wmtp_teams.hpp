@@ -333,10 +333,23 @@ __global__ __launch_bounds__((D / kVQ + 4) * 64, 1) void mfma_attn_teams_kernel(
         const int P = 64 * l + lane;
         *reinterpret_cast<u32x4*>(kst + vpiece(P / kVNQ, P % kVNQ) * 16) = ld.kreg[slot][l];
       }
+      // Keys past the split's end get p = 0, but rows past the sequence's end may hold any bits
+      // (0 x NaN is NaN): on the tile that reaches past it, their values are staged as zeros.
+      // Element jj of k-step ks is key 16 ks + 8 (jj / 4) + 4 kh + jj % 4 of the tile.
+      const int t0 = t_begin + it * kVTile;
+      const bool tail = t0 + kVTile > w.t_end;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const u32x4 v4 = {ld.vreg[slot][q >> 1][4 * (q & 1)], ld.vreg[slot][q >> 1][4 * (q & 1) + 1],
-                          ld.vreg[slot][q >> 1][4 * (q & 1) + 2], ld.vreg[slot][q >> 1][4 * (q & 1) + 3]};
+        u32x4 v4 = {ld.vreg[slot][q >> 1][4 * (q & 1)], ld.vreg[slot][q >> 1][4 * (q & 1) + 1],
+                    ld.vreg[slot][q >> 1][4 * (q & 1) + 2], ld.vreg[slot][q >> 1][4 * (q & 1) + 3]};
+        if (tail) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int jj = 4 * (q & 1) + e;
+            const int key = t0 + 16 * (q >> 1) + 8 * (jj >> 2) + 4 * kh + (jj & 3);
+            v4[e] = key < w.t_end ? v4[e] : 0u;
+          }
+        }
         v_stage[it % NB][wave][q][lane] = v4;
       }
       __syncthreads();

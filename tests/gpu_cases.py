@@ -39,9 +39,11 @@ class PagedCache:
     """One layer's paged K/V for `batch` sequences (device), sized for n0 + extra tokens.
 
     interleaved: one pool [blocks][H_kv][2][16][D] with K and V of a (block, head)
-    side by side (k and v are views of it); else separate pools [blocks][H_kv][16][D]."""
+    side by side (k and v are views of it); else separate pools [blocks][H_kv][16][D].
+    fill: the value of every pool element no context token is placed in (rows past a
+    sequence's end in its last block, spare blocks): 0, or NaN for an uninitialised pool."""
 
-    def __init__(self, k_ctx, v_ctx, n0, extra, seed, permuted=True, spare=2, interleaved=False):
+    def __init__(self, k_ctx, v_ctx, n0, extra, seed, permuted=True, spare=2, interleaved=False, fill=0.0):
         B = k_ctx.shape[0]
         self.n0 = list(n0)
         self.interleaved = interleaved
@@ -50,11 +52,11 @@ class PagedCache:
         self.bt_np = bt
         shape = (total, k_ctx.shape[2], 16, k_ctx.shape[3])
         if interleaved:
-            pool = torch.zeros((total, k_ctx.shape[2], 2, 16, k_ctx.shape[3]), dtype=k_ctx.dtype)
+            pool = torch.full((total, k_ctx.shape[2], 2, 16, k_ctx.shape[3]), fill, dtype=k_ctx.dtype)
             kpool, vpool = pool[:, :, 0], pool[:, :, 1]
         else:
-            kpool = torch.zeros(shape, dtype=k_ctx.dtype)
-            vpool = torch.zeros_like(kpool)
+            kpool = torch.full(shape, fill, dtype=k_ctx.dtype)
+            vpool = torch.full_like(kpool, fill)
         for b in range(B):
             place_paged(kpool, k_ctx[b, :self.n0[b]], bt[b])
             place_paged(vpool, v_ctx[b, :self.n0[b]], bt[b])
@@ -75,10 +77,12 @@ class PagedCache:
 
 
 class RingCache:
-    def __init__(self, batch, hk, d, sink, window, dtype, headroom=0):
+    """fill: the value of the slots no append has written (0, or NaN for an uninitialised ring)."""
+
+    def __init__(self, batch, hk, d, sink, window, dtype, headroom=0, fill=0.0):
         slots = sink + window + headroom
-        self.k = torch.zeros((batch, hk, slots, d), dtype=dtype, device=DEV)
-        self.v = torch.zeros_like(self.k)
+        self.k = torch.full((batch, hk, slots, d), fill, dtype=dtype, device=DEV)
+        self.v = torch.full_like(self.k, fill)
         self.tags = torch.full((batch, slots), -1, dtype=torch.int32, device=DEV)
         self.desc = W.make_ring(self.k, self.v, self.tags, sink, window, headroom)
 

@@ -287,8 +287,9 @@ def test_per_sequence_sinks_and_windows_parity(fast_pv):
     assert worst <= TOL["bf16"], worst
 
 
+@pytest.mark.parametrize("poison", [False, True])
 @pytest.mark.parametrize("fast_pv", [False, True])
-def test_window_holes_are_masked(fast_pv):
+def test_window_holes_are_masked(fast_pv, poison):
     """A visible entry whose slot tag does not hold its position is left out.
 
     The ring is rolled back below the query's length, so the newest visible
@@ -296,6 +297,8 @@ def test_window_holes_are_masked(fast_pv):
     of the window set.  Sequence 0 has wrapped (n > S + W); sequence 1 is
     shorter than S + W, so sinks and window overlap.  Both kernels that serve
     window mode are covered (bf16 PV weights at d = 256: the matrix-core one).
+    poison: the holes' K and V are then overwritten with NaN (a slot that does not
+    hold its position may hold any bits; 0 x NaN would be NaN).
     """
     S, Wn, R, Hq, Hk, D, B = 4, 64, 2, 16, 2, 256, 2
     G = Hq // Hk
@@ -309,6 +312,11 @@ def test_window_holes_are_masked(fast_pv):
         sub = W.Ring(ring.k[b].data_ptr(), ring.v[b].data_ptr(), ring.tags[b].data_ptr(), S, Wn, R)
         W.ring_append(sh, sub, kc[b:b + 1, :n0[b]].contiguous().to(DEV), vc[b:b + 1, :n0[b]].contiguous().to(DEV), [0])
     W.ring_rollback(ring.desc, kept)
+    if poison:
+        holes = (ring.tags < 0).unsqueeze(1).unsqueeze(-1).expand_as(ring.k)
+        assert bool(holes.any())
+        ring.k.masked_fill_(holes, float("nan"))
+        ring.v.masked_fill_(holes, float("nan"))
     q = synth.normal((B, Hq, D), 41, "hole_q", 1.0, "bf16")
     qf = O.to_f64(synth.bf16_bits(q), "bf16")
     flag = W.DRAFT_FAST_PV if fast_pv else 0
@@ -333,7 +341,7 @@ def test_window_holes_are_masked(fast_pv):
 
 # ============================================================== draft attention
 def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtype=torch.float32, fused=False,
-                headroom=0, record=None, interleaved=False):
+                headroom=0, record=None, interleaved=False, fill=0.0):
     """Run gamma draft steps on the GPU and the oracle; return the worst max-abs errors (o, lse).
 
     fused: append and attend in one call (wmtp_draft_attn_append) instead of an
@@ -350,9 +358,9 @@ def draft_steps(wl, contexts, mode, chunk=0, fast_pv=False, steps=None, out_dtyp
     new_v = host_array(case.v_new, dt)
     if mode == O.FULL:
         cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=steps, seed=wl.seed, permuted=wl.permuted,
-                           interleaved=interleaved)
+                           interleaved=interleaved, fill=fill)
     else:
-        ring = RingCache(B, Hk, D, wl.sink, wl.window, TDT[dt], headroom)
+        ring = RingCache(B, Hk, D, wl.sink, wl.window, TDT[dt], headroom, fill=fill)
         for b in range(B):                   # bulk-fill each sequence's ring with its context
             if case.n0[b] == 0:
                 continue
@@ -509,8 +517,44 @@ def test_window_covering_context_equals_full_on_gpu():
         assert eo <= TOL["bf16"] and el <= TOL["bf16"]
 
 
+# ============================================================== unused cache rows may hold any bits
+# Keys past a sequence's end share their block with its last keys, and ring slots that no
+# append has written (or whose tag is stale) sit beside visible ones.  They get weight 0, but
+# 0 x NaN is NaN: every kernel must keep their values out of the PV product.  Pools and rings
+# filled with NaN before the context is placed must give the oracle's result.
+NAN = float("nan")
+
+
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+@pytest.mark.parametrize("fast_pv", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_draft_unused_rows_hold_nan(mode, fast_pv, d):
+    wl = synth.workload("draft_131k_bf16", num_q_heads=8, num_kv_heads=2, head_dim=d, window=300)
+    say("draft NaN-filled cache", mode, fast_pv, d)
+    eo, el = draft_steps(wl, (1500, 77, 5), mode, chunk=96, fast_pv=fast_pv, fused=True, headroom=3, fill=NAN)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (eo, el)
+
+
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+def test_draft_fp32_unused_rows_hold_nan(mode):
+    wl = synth.workload("tiny_fp32_4k")
+    say("draft fp32 NaN-filled cache", mode)
+    eo, el = draft_steps(wl, (300, 7), mode, chunk=64, fused=True, headroom=2, fill=NAN)
+    assert eo <= TOL["f32"] and el <= TOL["f32"], (eo, el)
+
+
+@pytest.mark.parametrize("t_q,hq,hk,d", [(4, 16, 2, 256), (6, 16, 2, 256), (9, 16, 2, 256), (4, 8, 2, 128),
+                                         (12, 8, 2, 128), (4, 4, 1, 64), (24, 4, 1, 64)])
+def test_verify_unused_rows_hold_nan(t_q, hq, hk, d):
+    wl = synth.workload("step_1m_bf16", num_q_heads=hq, num_kv_heads=hk, head_dim=d)
+    say("verify NaN-filled pool", t_q, hq, hk, d)
+    for contexts, split in (((1500, 3), 96), ((29,), 32), ((700,), 0)):
+        eo, el = verify_run(wl, contexts, t_q, split, fused=True, fill=NAN)
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"], (contexts, split, eo, el)
+
+
 # ============================================================== verify attention
-def verify_run(wl, contexts, t_q, split=0, layer=0, fused=False, record=None, interleaved=False):
+def verify_run(wl, contexts, t_q, split=0, layer=0, fused=False, record=None, interleaved=False, fill=0.0):
     """Verify on the GPU (append + verify, or the fused call) against the oracle: worst (o, lse) errors.
     record: a list that receives (out, lse, k pool, v pool)."""
     case = synth.verify_case(wl, contexts, t_q, layer=layer)
@@ -518,7 +562,7 @@ def verify_run(wl, contexts, t_q, split=0, layer=0, fused=False, record=None, in
     dt = wl.dtype
     sh = W.make_shape(Hq, Hk, D, TDT[dt], wl.scale)
     cache = PagedCache(case.k_ctx, case.v_ctx, case.n0, extra=t_q, seed=wl.seed + 100 + layer,
-                       interleaved=interleaved)
+                       interleaved=interleaved, fill=fill)
     kn, vn = case.k_new.contiguous().to(DEV), case.v_new.contiguous().to(DEV)
     lens = [n + t_q for n in case.n0]
     ws = W.workspace(W.verify_workspace_bytes(sh, t_q, lens, split), DEV)
