@@ -42,8 +42,8 @@ METRIC = "draft+verify attention µs/decode-step and HBM GB/s (% of peak) at 1M 
 # 256 MiB device copy gives in the same run (FETCH x2.0, WRITE x1.0).  Valid only
 # for the kernel code they were taken with (sha256 of the sources without
 # comments and whitespace, below); otherwise null.
-VERIFY_TRAFFIC = {"sources_sha256": "e542efdf8b92e7ab8428e1eb3f0a9892f34bc4018ae41bbf558931851ecb7d3d",
-                  "fetch_kib": 1049671.18, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
+VERIFY_TRAFFIC = {"sources_sha256": "054721d1e60e93c91416d13fd54f3e69225322b1b9e9135995521abbe247011c",
+                  "fetch_kib": 1049653.28, "write_kib": 8232.00, "fetch_factor": 2.0, "write_factor": 1.0}
 VERIFY_SOURCES = ("long_context_decode_gqa_amd/csrc/wmtp_verify.hip", "long_context_decode_gqa_amd/csrc/wmtp_row_tile.hpp",
                   "long_context_decode_gqa_amd/csrc/wmtp_teams.hpp", "long_context_decode_gqa_amd/csrc/wmtp_device.hpp")
 
