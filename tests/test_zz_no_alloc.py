@@ -79,3 +79,64 @@ def test_noalloc_draft_matches_workspace_calls(mode, fused, fast_pv):
             o_ref, l_ref = O.draft_attention(qf[b], sk, sv, lens[b], mode, S, Wn, wl.scale)
             eo, el = max_err(got_o[b], o_ref), max_err(got_l[b], l_ref)
             assert eo <= TOL["bf16"] and el <= TOL["bf16"], (call, b, eo, el)
+
+
+@pytest.mark.parametrize("fast_pv", [True, False])
+@pytest.mark.parametrize("mode", [O.FULL, O.SINK_WINDOW])
+def test_noalloc_draft_steps_in_a_graph(mode, fast_pv):
+    """Callers under graph capture: three no-allocation draft steps (the append inside) captured
+    in a HIP graph.  Every replay, with eager work and synchronisations between replays, gives the
+    eager calls' outputs bit for bit; the eager calls match the oracle."""
+    wl = synth.workload("draft_131k_bf16", window=512)
+    Hq, Hk, D, S, Wn, g = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.sink, wl.window, wl.gamma
+    sh = W.make_shape(Hq, Hk, D, torch.bfloat16, wl.scale)
+    flag = W.DRAFT_FAST_PV if fast_pv else 0
+    n0 = 3000
+    say("noalloc graph", mode, fast_pv)
+    case = synth.draft_case(wl, (n0,), seed=47)
+    if mode == O.FULL:
+        cache = PagedCache(case.k_ctx, case.v_ctx, (n0,), extra=g, seed=47, interleaved=True)
+        kw = dict(paged=cache.desc)
+    else:
+        ring = RingCache(1, Hk, D, S, Wn, torch.bfloat16, headroom=g - 1)
+        W.ring_append(sh, ring.desc, case.k_ctx[:, :n0].contiguous().to(DEV), case.v_ctx[:, :n0].contiguous().to(DEV),
+                      [0])
+        kw = dict(ring=ring.desc)
+    q = case.q.contiguous().to(DEV)
+    kn, vn = case.k_new.contiguous().to(DEV), case.v_new.contiguous().to(DEV)
+    out = torch.zeros((g, 1, Hq, D), dtype=torch.float32, device=DEV)
+    lse = torch.zeros((g, 1, Hq), dtype=torch.float32, device=DEV)
+
+    def steps():
+        for j in range(g):
+            W.draft_attn_noalloc(mode | flag, sh, q[j], [n0 + j + 1], out[j], lse[j], k_new=kn[j], v_new=vn[j], **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        steps()                      # eager (the appends rewrite the same tokens at the same positions)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    qf = O.to_f64(synth.bf16_bits(case.q[:, 0]), "bf16")
+    kb, vb = synth.bf16_bits(case.k_ctx[0]), synth.bf16_bits(case.v_ctx[0])
+    for j in range(g):
+        nkb = synth.bf16_bits(case.k_new[:j + 1, 0, 0])
+        nvb = synth.bf16_bits(case.v_new[:j + 1, 0, 0])
+        sk = O.ConcatKV(O.LogicalKV(kb, "bf16", n0), O.LogicalKV(nkb, "bf16"))
+        sv = O.ConcatKV(O.LogicalKV(vb, "bf16", n0), O.LogicalKV(nvb, "bf16"))
+        o_ref, l_ref = O.draft_attention(qf[j], sk, sv, n0 + j + 1, mode, S, Wn, wl.scale)
+        eo, el = max_err(ref_o[j, 0], o_ref), max_err(ref_l[j, 0], l_ref)
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"], (j, eo, el)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), rep
+    del graph
