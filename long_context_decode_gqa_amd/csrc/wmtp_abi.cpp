@@ -365,8 +365,8 @@ int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_
     // A draft step is attention of a single query token, i.e. the verify
     // contraction with t_q = 1; both round p to bf16 before PV, so the G packed
     // rows run on the matrix-core kernel, which spends fewer vector instructions
-    // per key than the dot-product kernel: over the paged context (native) or
-    // over the ring's visible entries (window).
+    // per key than the vector kernels: over the paged context (native) or over
+    // the ring's visible entries (window).
     a.t_q = 1;
     const int group = shape->num_q_heads / shape->num_kv_heads;
     const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -382,8 +382,7 @@ int draft_attn(int32_t mode, const wmtp_shape* shape, const void* q, const wmtp_
     return launch_status(launch_draft_rows(shape->head_dim, shape->num_q_heads / shape->num_kv_heads, a, grid,
                                            static_cast<hipStream_t>(stream)));
   return launch_status(launch_draft(shape->dtype, shape->head_dim, shape->num_q_heads / shape->num_kv_heads,
-                                    base_mode == WMTP_SINK_WINDOW, fast_pv, a, grid,
-                                    static_cast<hipStream_t>(stream)));
+                                    base_mode == WMTP_SINK_WINDOW, a, grid, static_cast<hipStream_t>(stream)));
 }
 
 int verify_attn(const wmtp_shape* shape, const void* q, int32_t t_q, const wmtp_paged* kv, const void* k_new,

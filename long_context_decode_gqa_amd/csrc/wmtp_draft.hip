@@ -1,14 +1,17 @@
-// Split-K flash-decoding for the MTP draft head on gfx950.
+// Split-K flash-decoding for the MTP draft head on gfx950, with fp32 softmax
+// weights in the PV product: the slice kernel.
 //
 // The native MTP draft attends over the whole KV cache at every draft step, so
 // its read scales with the context length; Windowed-MTP attends over sink tokens
 // plus a window of recent tokens held in a compact ring ("Windowed-MTP:
 // Removing the Full-Context Draft-KV Tax at Million-Token Context", arxivlens
-// summary, Abstract; readpriors.com post, What happened).  One kernel serves
-// both: the only difference is how a visible entry is located (block table vs
-// ring slot + tag check).  Window mode walks the visible positions (the
-// sequence's own sinks, then its window) and reads each from its ring slot, so
-// its cost follows the sequence's S_b + W_b, not the ring's size.
+// summary, Abstract; readpriors.com post, What happened).  This kernel serves
+// window mode (bf16 or fp32 data) and full mode with fp32 data; the two differ
+// only in how a visible entry is located (block table vs ring slot + tag
+// check).  Full mode in bf16 runs on the whole-tile kernel (wmtp_draft_rows.hip)
+// and bf16 PV weights on the matrix-core kernels.  Window mode walks the visible
+// positions (the sequence's own sinks, then its window) and reads each from its
+// ring slot, so its cost follows the sequence's S_b + W_b, not the ring's size.
 //
 // Work item = (sequence b, KV head h, split of `chunk` visible entries); one
 // workgroup per item whose waves each own a 64-byte slice of every K/V row (8
@@ -81,13 +84,12 @@ __device__ __forceinline__ int k_piece(int t, int c) {
   }
 }
 
-template <int D, int G, bool BF16, bool WINDOW, bool PV_DOT2>
+template <int D, int G, bool BF16, bool WINDOW>
 __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_splitk_kernel(const SplitArgs a) {
   using S = DraftShape<D, G, BF16>;
   constexpr int NCH = S::NCH, TPI = S::TPI, GP = S::GP, QB = S::QB, ROWB = S::ROWB, NW = S::NW;
   constexpr int EV = S::EV, LPR = S::LPR, TPV = S::TPV, NV = S::NV;
   constexpr float TAU = 8.0f;   // lazy-max slack, log2 units
-  static_assert(!PV_DOT2 || BF16, "dot2 PV needs bf16 values");
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[NW * S::KSTAGE];
   __shared__ __attribute__((aligned(16))) float sc_lds[2 * NW * GP * S::TILE];
@@ -186,18 +188,11 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
       const int tt = i * TPI + k_tok;
       kreg[slot][i] = load_at<u32x4>(run_base(kbase, run, i * TPI, TPI, tt), lane_off(t0, tt) + k_c * 16);
     }
-    // V: load k brings entry k*TPV + v_tok (fp32 PV) or, for the paired bf16 PV,
-    // entry 2 (k/2 * TPV + v_tok) + k%2, bytes [8 v_d, 8 v_d + 8) of the slice.
+    // V: load k brings entry k*TPV + v_tok, bytes [8 v_d, 8 v_d + 8) of the slice.
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      if constexpr (PV_DOT2) {
-        const int first = 2 * (k >> 1) * TPV;
-        const int tt = first + 2 * v_tok + (k & 1);
-        vreg[slot][k] = load_at<uint2>(run_base(vbase, run, first, 2 * TPV, tt), lane_off(t0, tt) + v_d * 8);
-      } else {
-        const int tt = k * TPV + v_tok;
-        vreg[slot][k] = load_at<uint2>(run_base(vbase, run, k * TPV, TPV, tt), lane_off(t0, tt) + v_d * 8);
-      }
+      const int tt = k * TPV + v_tok;
+      vreg[slot][k] = load_at<uint2>(run_base(vbase, run, k * TPV, TPV, tt), lane_off(t0, tt) + v_d * 8);
     }
     if constexpr (WINDOW) tag[slot] = tags[wv.slot(min(t0 + ln, t_end - 1))];
   };
@@ -300,20 +295,17 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       p[g] = valid ? exp2f(s2[g] - M[g]) : 0.f;
-      if constexpr (PV_DOT2) p[g] = round_bf16(p[g]);   // PV consumes bf16 p: keep l consistent
       l_lane[g] += p[g];
     }
 
     // Masked entries get p = 0, but their values may be any bits (rows past a sequence's end in
     // its last block, ring slots never written or stale), and 0 x NaN is NaN: on a tile with
-    // such entries their values are zeroed.  Entry of V load k: as in the loads above.
+    // such entries their values are zeroed.  V load k holds entry k * TPV + v_tok.
     const uint64_t vis = __ballot(valid);
     if (vis != ~0ull) {
-      const int v_tok = ln / LPR;
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        const int tt = PV_DOT2 ? 2 * (k >> 1) * TPV + 2 * v_tok + (k & 1) : k * TPV + v_tok;
-        if (!((vis >> tt) & 1ull)) vreg[slot][k] = uint2{0u, 0u};
+        if (!((vis >> (k * TPV + v_tok)) & 1ull)) vreg[slot][k] = uint2{0u, 0u};
       }
     }
 
@@ -327,58 +319,31 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
       *reinterpret_cast<f32x4*>(pl_lds + (pl * S::TILE + ln) * 4) = w4;
     }
 
-    // ---- PV over this wave's slice of D
-    if constexpr (PV_DOT2) {
+    // ---- PV over this wave's slice of D (fp32 weights, fp32 FMAs)
 #pragma unroll
-      for (int k = 0; k < NV / 2; ++k) {
-        const int ta = 2 * (k * TPV + v_tok);
-        float pa[GP], pb[GP];
+    for (int k = 0; k < NV; ++k) {
+      const int tt = k * TPV + v_tok;
+      float pp[GP];
 #pragma unroll
-        for (int pl = 0; pl < GP / 4; ++pl) {
-          const f32x4 xa = *reinterpret_cast<const f32x4*>(pl_lds + (pl * S::TILE + ta) * 4);
-          const f32x4 xb = *reinterpret_cast<const f32x4*>(pl_lds + (pl * S::TILE + ta + 1) * 4);
+      for (int pl = 0; pl < GP / 4; ++pl) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(pl_lds + (pl * S::TILE + tt) * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { pa[pl * 4 + e] = xa[e]; pb[pl * 4 + e] = xb[e]; }
-        }
-        const uint2 va = vreg[slot][2 * k], vb = vreg[slot][2 * k + 1];
-        uint32_t vp[4];
-        vp[0] = __builtin_amdgcn_perm(vb.x, va.x, 0x05040100u);
-        vp[1] = __builtin_amdgcn_perm(vb.x, va.x, 0x07060302u);
-        vp[2] = __builtin_amdgcn_perm(vb.y, va.y, 0x05040100u);
-        vp[3] = __builtin_amdgcn_perm(vb.y, va.y, 0x07060302u);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const uint32_t pp = pack_bf16x2(pa[g], pb[g]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[g][e] = dot2_bf16(pp, vp[e], o[g][e]);
-        }
+        for (int e = 0; e < 4; ++e) pp[pl * 4 + e] = x[e];
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const int tt = k * TPV + v_tok;
-        float pp[GP];
-#pragma unroll
-        for (int pl = 0; pl < GP / 4; ++pl) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(pl_lds + (pl * S::TILE + tt) * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pp[pl * 4 + e] = x[e];
-        }
-        float vf[EV];
-        if constexpr (BF16) {
-          vf[0] = bf16lo(vreg[slot][k].x);
-          vf[1] = bf16hi(vreg[slot][k].x);
-          vf[2] = bf16lo(vreg[slot][k].y);
-          vf[3] = bf16hi(vreg[slot][k].y);
-        } else {
-          vf[0] = __uint_as_float(vreg[slot][k].x);
-          vf[1] = __uint_as_float(vreg[slot][k].y);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < EV; ++e) o[g][e] = fmaf(pp[g], vf[e], o[g][e]);
+      float vf[EV];
+      if constexpr (BF16) {
+        vf[0] = bf16lo(vreg[slot][k].x);
+        vf[1] = bf16hi(vreg[slot][k].x);
+        vf[2] = bf16lo(vreg[slot][k].y);
+        vf[3] = bf16hi(vreg[slot][k].y);
+      } else {
+        vf[0] = __uint_as_float(vreg[slot][k].x);
+        vf[1] = __uint_as_float(vreg[slot][k].y);
       }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) o[g][e] = fmaf(pp[g], vf[e], o[g][e]);
     }
   };
 
@@ -439,50 +404,40 @@ __global__ __launch_bounds__((DraftShape<D, G, BF16>::THREADS)) void draft_split
 }
 
 // ----------------------------------------------------------------------------- dispatch
+// Window mode (bf16 or fp32 data) and full mode with fp32 data.  Full mode in bf16 runs on the
+// whole-tile kernel (wmtp_draft_rows.hip), and bf16 PV weights on the matrix-core kernels.
 template <int D, int G, bool BF16>
-static hipError_t launch_dg(bool window, bool dot2, const SplitArgs& a, int grid, hipStream_t st) {
+static hipError_t launch_dg(bool window, const SplitArgs& a, int grid, hipStream_t st) {
   constexpr int T = DraftShape<D, G, BF16>::THREADS;
   if (window) {
-    if constexpr (BF16) {
-      if (dot2) { draft_splitk_kernel<D, G, BF16, true, true><<<grid, T, 0, st>>>(a); return hipGetLastError(); }
-    }
-    draft_splitk_kernel<D, G, BF16, true, false><<<grid, T, 0, st>>>(a);
+    draft_splitk_kernel<D, G, BF16, true><<<grid, T, 0, st>>>(a);
+  } else if constexpr (!BF16) {
+    draft_splitk_kernel<D, G, BF16, false><<<grid, T, 0, st>>>(a);
   } else {
-    if constexpr (BF16) {
-      if (dot2) { draft_splitk_kernel<D, G, BF16, false, true><<<grid, T, 0, st>>>(a); return hipGetLastError(); }
-    }
-    draft_splitk_kernel<D, G, BF16, false, false><<<grid, T, 0, st>>>(a);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int D, bool BF16>
-static hipError_t launch_d(int G, bool window, bool dot2, const SplitArgs& a, int grid, hipStream_t st) {
+static hipError_t launch_d(int G, bool window, const SplitArgs& a, int grid, hipStream_t st) {
   switch (G) {
-    case 1: return launch_dg<D, 1, BF16>(window, dot2, a, grid, st);
-    case 2: return launch_dg<D, 2, BF16>(window, dot2, a, grid, st);
-    case 4: return launch_dg<D, 4, BF16>(window, dot2, a, grid, st);
-    case 8: return launch_dg<D, 8, BF16>(window, dot2, a, grid, st);
+    case 1: return launch_dg<D, 1, BF16>(window, a, grid, st);
+    case 2: return launch_dg<D, 2, BF16>(window, a, grid, st);
+    case 4: return launch_dg<D, 4, BF16>(window, a, grid, st);
+    case 8: return launch_dg<D, 8, BF16>(window, a, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_draft(int dtype, int head_dim, int group, bool window, bool pv_dot2, const SplitArgs& a,
-                        int grid, hipStream_t st) {
+hipError_t launch_draft(int dtype, int head_dim, int group, bool window, const SplitArgs& a, int grid,
+                        hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   const bool bf16 = dtype == WMTP_BF16;
-  if (bf16) {
-    switch (head_dim) {
-      case 64: return launch_d<64, true>(group, window, pv_dot2, a, grid, st);
-      case 128: return launch_d<128, true>(group, window, pv_dot2, a, grid, st);
-      case 256: return launch_d<256, true>(group, window, pv_dot2, a, grid, st);
-    }
-  } else {
-    switch (head_dim) {
-      case 64: return launch_d<64, false>(group, window, false, a, grid, st);
-      case 128: return launch_d<128, false>(group, window, false, a, grid, st);
-      case 256: return launch_d<256, false>(group, window, false, a, grid, st);
-    }
+  switch (head_dim) {
+    case 64: return bf16 ? launch_d<64, true>(group, window, a, grid, st) : launch_d<64, false>(group, window, a, grid, st);
+    case 128: return bf16 ? launch_d<128, true>(group, window, a, grid, st) : launch_d<128, false>(group, window, a, grid, st);
+    case 256: return bf16 ? launch_d<256, true>(group, window, a, grid, st) : launch_d<256, false>(group, window, a, grid, st);
   }
   return hipErrorInvalidValue;
 }

@@ -40,8 +40,9 @@ struct AppendArgs {
   int32_t pos[WMTP_MAX_BATCH];  // first new position (appends) or kept length (rollback)
 };
 
-hipError_t launch_draft(int dtype, int head_dim, int group, bool window, bool pv_dot2, const SplitArgs& a,
-                        int grid, hipStream_t st);
+// The slice kernel (wmtp_draft.hip): window mode, and full mode with fp32 data, fp32 PV weights.
+hipError_t launch_draft(int dtype, int head_dim, int group, bool window, const SplitArgs& a, int grid,
+                        hipStream_t st);
 // The native draft step in bf16 with fp32 softmax weights: each wave owns whole tiles of keys over
 // all of head_dim (wmtp_draft_rows.hip).
 hipError_t launch_draft_rows(int head_dim, int group, const SplitArgs& a, int grid, hipStream_t st);
