@@ -699,12 +699,12 @@ def draft_131k_measurements(flag, reps, dev):
 
 def native_draft_pv_measurements(step, reps):
     """The 1M native draft step (append inside the attention launch, then the combine) with fp32 softmax
-    weights in the PV product (the vector dot-product kernel) beside bf16 weight pairs (the matrix-core
+    weights in the PV product (the whole-tile vector kernel) beside bf16 weight pairs (the matrix-core
     kernel), in the main step's launch configuration.  Every launch streams the 2 GiB pool, far past
     the caches, so each repetition reads it from HBM."""
     n = step.n0 + 1
     res = {}
-    for flag, name in ((0, "fp32_weights_dot_product_kernel"), (W.DRAFT_FAST_PV, "bf16_weights_matrix_core_kernel")):
+    for flag, name in ((0, "fp32_weights_vector_kernel"), (W.DRAFT_FAST_PV, "bf16_weights_matrix_core_kernel")):
         a = W.prepare_draft_attn_append(W.FULL | flag, step.sh, step.q_draft[0], step.k_draft[0], step.v_draft[0],
                                         [n], step.ws_full, paged=step.layers[0][1], chunk_tokens=step.chunk_full)
         a()

@@ -782,7 +782,7 @@ def _check_rows(out, lse, q_rows, sk, sv, positions, h, scale, what):
 @pytest.mark.slow
 def test_draft_full_1m_paged_exact_pv():
     """Native draft step over a 1,048,576-token paged pool (random block permutation, separate K and
-    V pools), fp32 PV weights and 256-token splits (the dot-product kernel); every query head of
+    V pools), fp32 PV weights and 256-token splits (the whole-tile vector kernel); every query head of
     both KV heads checked, on needle inputs that include the pool's last block."""
     say("draft 1M exact PV")
     n0, bt, k, v, btd, desc, views = _paged_1m(2)
