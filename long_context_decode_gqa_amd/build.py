@@ -62,6 +62,42 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+UBSAN_LIB = os.path.join(ROOT, "_build", "ubsan", "libwmtp.so")
+
+
+def build_host_ubsan(verbose: bool = False) -> str:
+    """A variant of the library whose host code (the C ABI's checks and planners) carries the
+    undefined-behaviour sanitizer, minimal runtime, aborting on the first report; the device code
+    is the same.  For the CPU suite: WMTP_LIBRARY=<this path> python -m pytest tests -m "not gpu"."""
+    build(verbose=False)                  # the device objects
+    flags = ["-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fsanitize-minimal-runtime"]
+    abi = os.path.join(CSRC, "wmtp_abi.cpp")
+    obj = os.path.join(OBJ_DIR, "wmtp_abi.ubsan.o")
+    cmd = [HIPCC, "-x", "hip", *COMMON, *flags, "-Xarch_host", "-fno-sanitize-recover=all", "-c", abi, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {abi}:\n{r.stderr}")
+    objs = [os.path.join(OBJ_DIR, os.path.basename(src) + ".o") for src in sources() if src != abi] + [obj]
+    res = subprocess.run([HIPCC, "-print-resource-dir"], capture_output=True, text=True).stdout.strip()
+    found = [os.path.join(d, f) for d, _, fs in os.walk(os.path.join(res, "lib")) for f in fs
+             if f.startswith("libclang_rt.ubsan_minimal") and f.endswith(".so")]
+    if not found:
+        raise RuntimeError(f"no minimal UBSan runtime under {res}")
+    rt_dir = os.path.dirname(found[0])
+    os.makedirs(os.path.dirname(UBSAN_LIB), exist_ok=True)
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", *flags, "-shared-libsan", f"-Wl,-rpath,{rt_dir}",
+           "-o", UBSAN_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {UBSAN_LIB}")
+    return UBSAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--host-ubsan" in sys.argv[1:]:
+        build_host_ubsan(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -15,7 +15,9 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_lib", "libwmtp.so")
+# WMTP_LIBRARY names another build of the same library (for instance the host-sanitizer variant of
+# long_context_decode_gqa_amd.build --host-ubsan); unset, the in-tree build.
+LIB_PATH = os.environ.get("WMTP_LIBRARY") or os.path.join(_PKG, "_lib", "libwmtp.so")
 
 # ---------------------------------------------------------------- constants (wmtp.h)
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4, -5
